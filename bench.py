@@ -1,0 +1,192 @@
+"""Throughput of the AWQ per-layer scale search on one MI355X.
+
+One step = the whole hot path on one synthetic layer already resident in HBM:
+activation statistics, the 20-point alpha search (scale table, reference
+output, fake quantisation, candidate GEMMs with the fused squared-error
+epilogue, loss reduction and argmin) and the final quantise + pack with the
+chosen scales.  The metric is alpha-candidates scored per second.
+
+Prints one JSON line.  Besides the throughput it reports the dominant kernel
+(the candidate GEMM) against the dense fp16/bf16 MFMA peak, with its average
+launch time taken from HIP events recorded on the launch stream during the
+timed steps, and the CPU oracle timed on a bounded sample of the same layer.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+METRIC = "alpha-candidates/sec per layer; fake-quant GEMM TFLOP/s as % of MFMA peak"
+PEAK_TFLOPS = {"fp16": 2516.6, "bf16": 2516.6, "fp32": 157.3}
+TRAFFIC_FILE = ROOT / "profiles" / "traffic.json"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--config", default="llama7b-qproj")
+    p.add_argument("--flags", type=int, default=0, help="0 weight-delta form, 1 reference-output form")
+    p.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in sorted((ROOT / "post_weight_quantization_act_amd" / "csrc").glob("*")):
+        h.update(f.read_bytes())
+    return h.hexdigest()[:16]
+
+
+def cpu_baseline(spec, W, X, budget_s: float) -> dict:
+    """The oracle as it is, on the first k alphas of the same layer."""
+    import numpy as np
+
+    import oracle
+    from datagen import to_numpy
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - informational only
+        threads = len(os.sched_getaffinity(0))
+    Wn, Xn = to_numpy(W), to_numpy(X)
+    alphas = oracle.alpha_grid(spec.n_alpha)
+    t0 = time.perf_counter()
+    oracle.search(Wn, Xn, spec.bits, spec.group, alphas[:1])
+    t1 = time.perf_counter() - t0
+    k = 1
+    elapsed = t1
+    if t1 < budget_s / 2:
+        # the fixed part (statistics + reference output) is included in every run
+        k = int(min(spec.n_alpha, max(2, budget_s / max(t1, 1e-3))))
+        t0 = time.perf_counter()
+        oracle.search(Wn, Xn, spec.bits, spec.group, alphas[:k])
+        elapsed = time.perf_counter() - t0
+    return {"value": k / elapsed, "unit": "alpha-candidates/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"oracle.search (statistics, fp64 reference output, fake quantisation and "
+                      f"fp64 loss) over the first {k} of {spec.n_alpha} alphas of the full "
+                      f"{spec.name} layer, {elapsed:.1f} s on {threads} BLAS threads"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import post_weight_quantization_act_amd as awq
+    from datagen import CONFIGS, make_layer
+
+    spec = CONFIGS[args.config]
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    W, X = make_layer(spec)
+    Wd, Xd = W.to(dev), X.to(dev)
+    N, K, T = spec.N, spec.K, spec.T
+    alphas = (np.arange(spec.n_alpha, dtype=np.float64) / spec.n_alpha).astype(np.float32)
+    lay = awq.awq_search_layout(Wd.dtype, N, K, T, spec.n_alpha, args.flags, 0)
+    ws = torch.empty(lay["total_bytes"], dtype=torch.uint8, device=dev)
+    a = torch.empty(K, dtype=torch.float32, device=dev)
+    ws_stats = torch.empty(max(1, awq.awq_act_stats_workspace_size(T, K)), dtype=torch.uint8,
+                           device=dev)
+    losses = torch.empty(spec.n_alpha, dtype=torch.float64, device=dev)
+    s_best = torch.empty(K, dtype=torch.float32, device=dev)
+    best = torch.empty(1, dtype=torch.int32, device=dev)
+
+    def step():
+        awq.awq_act_stats(Xd, out=a, workspace=ws_stats)
+        awq.awq_search_scales(Wd, Xd, a, spec.bits, spec.group, alphas, flags=args.flags,
+                              workspace=ws, losses=losses, s_best=s_best, best_idx=best)
+        return awq.awq_quantize_pack(Wd, s_best, spec.bits, spec.group)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    awq.awq_profile_reset()
+    awq.awq_profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    awq.awq_profile_enable(False)
+    n_gemm, ms_gemm = awq.awq_profile_read("awq_gemm_sse")
+    n_fq, ms_fq = awq.awq_profile_read("awq_fake_quant")
+    n_st, ms_st = awq.awq_profile_read("awq_act_stats_partial")
+    n_pk, ms_pk = awq.awq_profile_read("awq_quantize_pack")
+    n_ref, ms_ref = awq.awq_profile_read("awq_gemm_ref_output")
+    awq.awq_profile_reset()
+
+    ms_per_step = 1e3 * elapsed / args.steps
+    value = spec.n_alpha * args.steps / elapsed
+    batch = lay["alpha_batch"]
+    flop_per_launch = 2.0 * T * N * K * batch
+    avg_ms = ms_gemm / max(n_gemm, 1)
+    achieved = flop_per_launch / (avg_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[spec.dtype]
+    traffic = None
+    src_hash = kernel_source_hash()
+    if TRAFFIC_FILE.exists():
+        tr = json.loads(TRAFFIC_FILE.read_text())
+        ent = tr.get(f"{args.config}:{args.flags}")
+        if ent and ent.get("source_hash") == src_hash:
+            traffic = ent["bytes_per_launch"]
+    esize = 4 if spec.dtype == "fp32" else 2
+    detail = {
+        "gemm_sse": {"launches": n_gemm, "avg_ms": avg_ms, "tflops": achieved},
+        "fake_quant": {"launches": n_fq, "avg_ms": ms_fq / max(n_fq, 1),
+                       "gbps": (N * K * esize * (1 + batch)) / (ms_fq / max(n_fq, 1) * 1e-3) / 1e9},
+        "act_stats": {"avg_ms": ms_st / max(n_st, 1),
+                      "gbps": (T * K * esize) / (ms_st / max(n_st, 1) * 1e-3) / 1e9},
+        "quantize_pack": {"avg_ms": ms_pk / max(n_pk, 1),
+                          "gbps": (N * K * esize + N * K * spec.bits / 8 + 5 * N * K / spec.group)
+                          / (ms_pk / max(n_pk, 1) * 1e-3) / 1e9},
+        "ref_output_gemm_ms": ms_ref / max(n_ref, 1) if n_ref else None,
+    }
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "alpha-candidates/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec.dtype,
+        "data": "synthetic",
+        "config": {"workload": spec.name, "N_out": N, "K_in": K, "T_tokens": T,
+                   "bits": spec.bits, "group": spec.group, "n_alpha": spec.n_alpha,
+                   "loss_form": "reference_output" if args.flags else "weight_delta",
+                   "alpha_batch": batch},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": traffic,
+                     "kernel": "gemm_mfma_kernel (candidate GEMM + squared-error epilogue)",
+                     "flop_per_launch": flop_per_launch},
+        "kernels": detail,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(spec, W, X, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,226 @@
+/*
+ * awq.h -- C ABI of the MI355X (gfx950) AWQ per-layer scale-search library.
+ *
+ * The library computes the activation-aware weight quantisation scale search
+ * for one linear layer y = W x, W [N out, K in], on calibration activations
+ * X [T tokens, K]:
+ *
+ *   1. a_j = mean_t |X[t, j]|                              (awq_act_stats)
+ *   2. for every alpha on a grid: s_j = max(a_j, 1e-8)^alpha
+ *   3. group-wise asymmetric round-to-nearest quantisation of W diag(s),
+ *      dequantisation, division by s                     (awq_fake_quant)
+ *   4. mean squared error of the layer output X W_hat^T against X W^T
+ *   5. argmin over alpha                                  (awq_search_scales)
+ *   and the final integer codes with per-group step and zero-point
+ *                                                         (awq_quantize_pack)
+ *
+ * Sources (web pages on the method):
+ *   [P1] "Как работает quantization-aware scaling в AWQ для защиты важных
+ *        весов?" (aivaro.ru Q&A), sections 5, 6 and 9
+ *   [P2] "AWQ: Activation-Aware Weight Quantization For On-Device LLM
+ *        Compression AND Acceleration" (reading notes), section "Measures"
+ *   [P3] "52 · AWQ, GPTQ và SmoothQuant", sections 2 and 3
+ *   [P4] "GPTQ与AWQ" (study notes), section "AWQ实现要点"
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor is a dense row-major buffer in device memory, allocated and
+ *     owned by the caller; the library allocates no device memory.  Host
+ *     buffers are named as such below.
+ *   - Work is enqueued asynchronously on `stream` (NULL = the null stream);
+ *     outputs are valid once the stream has been synchronised.  Calls that
+ *     share a workspace must be ordered on one stream.
+ *   - Arguments are validated before anything is enqueued.  A non-OK status
+ *     enqueues nothing (AWQ_ERR_HIP: a launch failed; the stream may then hold
+ *     part of the work).  awq_last_error() gives a message for the calling
+ *     thread's last non-OK status.  No C++ exception crosses this ABI.
+ *   - Element arithmetic of the quantiser is IEEE fp32 with round-to-nearest-
+ *     even, correctly rounded division and no contraction, in the fixed order
+ *     given at awq_fake_quant; codes, steps and zero-points are therefore
+ *     bit-identical to any other IEEE implementation of that order.
+ *   - W and X share one dtype.  fp16/bf16 layers use the MFMA path (fp32
+ *     accumulation); fp32 layers use an fp32 vector-ALU path.
+ *   - Sizes: every operand buffer must be below 4 GiB (byte offsets are
+ *     32-bit inside the kernels); bits in [2, 8]; group a power of two in
+ *     [32, 512] dividing K.
+ */
+#ifndef AWQ_MI355X_AWQ_H
+#define AWQ_MI355X_AWQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { AWQ_F32 = 0, AWQ_F16 = 1, AWQ_BF16 = 2 } awq_dtype_t;
+
+typedef enum {
+  AWQ_OK = 0,
+  AWQ_ERR_INVALID_ARG = -1,   /* null pointer, non-positive size, K % group != 0 ... */
+  AWQ_ERR_UNSUPPORTED = -2,   /* valid but not handled: bits, group, dtype, size limit */
+  AWQ_ERR_WORKSPACE = -3,     /* workspace missing or too small */
+  AWQ_ERR_HIP = -4            /* a HIP runtime call or launch failed */
+} awq_status_t;
+
+/* Search flags: how a candidate's output error is formed.  Both give
+ * sum_{t,i} (Y[t,i] - Yhat[t,i])^2 with Y = X W^T, Yhat = X W_hat^T. */
+/* Default: the fake-quant pass writes D = W - W_hat (fp32 difference rounded
+ * to the layer dtype) and the GEMM accumulates X D^T and squares it in the
+ * epilogue; no reference output is formed or read.  Rounding hits D, whose
+ * relative error stays at the dtype's half-ulp however small D is. */
+#define AWQ_SEARCH_WEIGHT_DELTA 0u
+/* The layer output W X is computed once into the workspace (fp32) and every
+ * candidate GEMM on W_hat subtracts its output from it in the epilogue.
+ * fp16 and fp32 layers only: rounding W_hat itself to bf16 perturbs the
+ * up-scaled salient channels by more than the 1e-3 loss tolerance, so bf16
+ * returns AWQ_ERR_UNSUPPORTED. */
+#define AWQ_SEARCH_REFERENCE_OUTPUT 1u
+
+/* awq_fake_quant output selection. */
+#define AWQ_FQ_WEIGHT_HAT 0u     /* out = W_hat */
+#define AWQ_FQ_WEIGHT_DELTA 1u   /* out = W - W_hat */
+
+/* Library version string, e.g. "awq-mi355x 0.1". */
+const char* awq_version(void);
+
+/* Message for the calling thread's last non-OK status ("" if none). */
+const char* awq_last_error(void);
+
+/* ------------------------------------------------------------------------ *
+ * Step 1: per-input-channel activation magnitude ([P2] "Measures";
+ * [P4] "AWQ实现要点" item 2).
+ *
+ *   a_out[j] = fp32( (sum_{t<T} |X[t, j]|) / T ),  the sum in fp64.
+ *
+ * X: [T, K] of x_dtype.  a_out: [K] fp32.  workspace: device scratch of at
+ * least awq_act_stats_workspace_size(T, K) bytes (fp64 partial sums), may be
+ * NULL when that size is 0.  The summation order is fixed, so the result is
+ * reproducible run to run.
+ * ------------------------------------------------------------------------ */
+size_t awq_act_stats_workspace_size(int64_t T, int64_t K);
+awq_status_t awq_act_stats(const void* X, awq_dtype_t x_dtype, int64_t T, int64_t K,
+                           float* a_out, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+/* ------------------------------------------------------------------------ *
+ * Step 2: the scale table ([P2] "Measures": s = a^alpha per input channel).
+ *
+ *   s_out[k, j] = fp32( pow( fp64(max(a[j], 1e-8f)), fp64(alphas[k]) ) )
+ *
+ * a: [K] fp32 device.  alphas: [n_alpha] fp32 HOST array.  s_out:
+ * [n_alpha, K] fp32 device.  (awq_search_scales builds the same table
+ * internally; this entry point exposes it on its own.)
+ * ------------------------------------------------------------------------ */
+awq_status_t awq_scale_table(const float* a, int64_t K, const float* alphas, int n_alpha,
+                             float* s_out, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ *
+ * Step 3: group-wise asymmetric fake quantisation of W diag(s)
+ * ([P1] sections 5 and 9: round-to-nearest over groups, zero_point,
+ * q_group_size, w_bit; [P2] "Measures": scale, then quantise group-wise).
+ *
+ * For one scale vector s_k (row k of s, n_s rows) and every output row i and
+ * group g of `group` consecutive input channels, in fp32 and in this order:
+ *   w'    = W[i, j] * s[j]
+ *   mx,mn = max, min of w' over the group
+ *   delta = max((mx - mn) / (2^bits - 1), 1e-10f)
+ *   z     = clamp(rint(-mn / delta), 0, 2^bits - 1)
+ *   c     = clamp(rint(w' / delta) + z, 0, 2^bits - 1)     (rint: ties to even)
+ *   W_hat = ((c - z) * delta) / s[j]
+ * Output out[k, i, j] = W_hat rounded (nearest-even) to out_dtype, or, with
+ * flags = AWQ_FQ_WEIGHT_DELTA, fp32(W[i, j] - W_hat) rounded to out_dtype.
+ * W: [N, K] of w_dtype; s: [n_s, K] fp32 device; out: [n_s, N, K] of out_dtype (AWQ_F16/AWQ_BF16 only for fp16/bf16 W, AWQ_F32
+ * only for fp32 W).
+ * ------------------------------------------------------------------------ */
+awq_status_t awq_fake_quant(const void* W, awq_dtype_t w_dtype, int64_t N, int64_t K,
+                            const float* s, int n_s, int bits, int group, uint32_t flags,
+                            void* out, awq_dtype_t out_dtype, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ *
+ * Steps 2-5: the whole search ([P2] "Measures": statistics, then for each
+ * alpha scale, group-quantise and measure the error, keep the best;
+ * [P1] section 6: the criterion is the output mean squared error).
+ *
+ * Inputs: W [N, K] and X [T, K] of `dtype`; a [K] fp32 device (from
+ * awq_act_stats); alphas [n_alpha] fp32 HOST array; bits; group; flags
+ * (AWQ_SEARCH_WEIGHT_DELTA, the default, or AWQ_SEARCH_REFERENCE_OUTPUT).
+ * Outputs (device): losses_out [n_alpha] fp64,
+ *   losses_out[k] = sum_{t,i} (Y[t,i] - Yhat_k[t,i])^2 / (T N),
+ *   Y = X W^T, Yhat_k = X W_hat_k^T with W_hat_k from awq_fake_quant; the
+ *   GEMM takes X and D = W - W_hat_k (or W_hat_k) in the layer dtype and
+ *   accumulates in fp32;
+ * best_idx_out [1] int32 = lowest k with the smallest loss;
+ * s_best_out [K] fp32 = row best_idx of the scale table (the factors the
+ * caller folds into the operator that produces X, dividing it).
+ *
+ * workspace: device scratch laid out as awq_search_layout() reports for the
+ * same arguments and workspace_bytes.  With the full size (layout with
+ * workspace_bytes = 0) every alpha is fake-quantised and scored in one batch;
+ * a smaller workspace (at least one alpha's W_hat) makes the library process
+ * the grid in batches of layout.alpha_batch.  After the call the workspace
+ * holds the scale table, the reference output (REFERENCE_OUTPUT form), the
+ * last batch's D (or W_hat) and the per-tile partial sums, at the reported
+ * offsets.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  size_t total_bytes;       /* bytes the call uses */
+  size_t s_table_offset;    /* fp32 [n_alpha][K] */
+  size_t y_ref_offset;      /* fp32 [T][N]; SIZE_MAX in the WEIGHT_DELTA form */
+  size_t w_hat_offset;      /* dtype [alpha_batch][N][K]: D = W - W_hat, or W_hat */
+  size_t partials_offset;   /* fp64 [n_alpha][tiles_m][tiles_n]: sum of squared
+                               errors of output tile (m, n) = rows
+                               [m*tile_m, +tile_m) x cols [n*tile_n, +tile_n) */
+  int32_t alpha_batch;      /* alphas fake-quantised and scored per pass */
+  int32_t tile_m, tile_n;   /* output tile of the GEMM (tokens x out channels) */
+  int32_t tiles_m, tiles_n; /* ceil(T / tile_m), ceil(N / tile_n) */
+} awq_search_layout_t;
+
+/* Host-only query (no device work).  workspace_bytes = 0 asks for the layout
+ * that scores every alpha in one batch; otherwise the largest batch that fits
+ * in workspace_bytes.  AWQ_ERR_WORKSPACE if not even one alpha fits. */
+awq_status_t awq_search_layout(awq_dtype_t dtype, int64_t N, int64_t K, int64_t T,
+                               int n_alpha, uint32_t flags, size_t workspace_bytes,
+                               awq_search_layout_t* layout_out);
+
+awq_status_t awq_search_scales(const void* W, const void* X, awq_dtype_t dtype,
+                               int64_t N, int64_t K, int64_t T,
+                               const float* a, int bits, int group,
+                               const float* alphas, int n_alpha, uint32_t flags,
+                               double* losses_out, float* s_best_out,
+                               int32_t* best_idx_out,
+                               void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/* ------------------------------------------------------------------------ *
+ * Step 5b: final quantisation and packing ([P2] "Measures", last step: save
+ * the low-bit weights with their quantisation metadata; [P1] section 9).
+ *
+ * Same arithmetic as awq_fake_quant for one scale vector s [K] (device).
+ * codes_out: uint32 [N, bits*K/32]; the code of column j sits at bits
+ * [bits*j, bits*j + bits) of its row's little-endian bitstream (bit p of a
+ * row in word p/32, bit p%32).  scales_out: fp32 [N, K/group] = delta.
+ * zeros_out: uint8 [N, K/group] = z.  With s = 1 this is plain
+ * round-to-nearest quantisation.
+ * ------------------------------------------------------------------------ */
+awq_status_t awq_quantize_pack(const void* W, awq_dtype_t w_dtype, int64_t N, int64_t K,
+                               const float* s, int bits, int group,
+                               uint32_t* codes_out, float* scales_out, uint8_t* zeros_out,
+                               hipStream_t stream);
+
+/* ------------------------------------------------------------------------ *
+ * Kernel timing.  While enabled, every kernel the library launches is
+ * bracketed by a pair of HIP events on its stream; awq_profile_read()
+ * synchronises on them and returns, for kernels whose name starts with
+ * `prefix` (NULL or "" = all), the launch count and the summed elapsed
+ * milliseconds.  awq_profile_reset() drops the records.  Thread-safe.
+ * ------------------------------------------------------------------------ */
+awq_status_t awq_profile_enable(int enable);
+awq_status_t awq_profile_read(const char* prefix, int64_t* launches, double* total_ms);
+awq_status_t awq_profile_reset(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* AWQ_MI355X_AWQ_H */

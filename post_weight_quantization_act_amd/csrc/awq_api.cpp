@@ -1,0 +1,364 @@
+// C ABI of the AWQ scale-search library: argument validation, workspace
+// layout, the order of launches on the caller's stream, error reporting and
+// optional per-launch timing.  All arithmetic runs in the HIP kernels of
+// act_stats.hip, quant.hip and gemm_sse.hip.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "common.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+awq_status_t fail(awq_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+awq_status_t hip_fail(hipError_t e, const char* what) {
+  return fail(AWQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr uint64_t kMaxBufferBytes = 0xFFFFFF00ull;  // byte offsets inside kernels are 32-bit
+constexpr int kMaxAlpha = 4096;
+
+int esize(awq_dtype_t dt) { return dt == AWQ_F32 ? 4 : 2; }
+
+bool valid_dtype(int dt) { return dt == AWQ_F32 || dt == AWQ_F16 || dt == AWQ_BF16; }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Checks shared by the quantiser entry points.
+awq_status_t check_quant_args(awq_dtype_t dt, int64_t N, int64_t K, int bits, int group) {
+  if (!valid_dtype(dt)) return fail(AWQ_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
+  if (N < 1 || K < 1) return fail(AWQ_ERR_INVALID_ARG, "N and K must be >= 1 (N=%lld K=%lld)",
+                                  (long long)N, (long long)K);
+  if (bits < 2 || bits > 8) return fail(AWQ_ERR_UNSUPPORTED, "bits=%d outside [2, 8]", bits);
+  if (group < 32 || group > 512 || (group & (group - 1)) != 0)
+    return fail(AWQ_ERR_UNSUPPORTED, "group=%d must be a power of two in [32, 512]", group);
+  if (K % group != 0)
+    return fail(AWQ_ERR_INVALID_ARG, "K=%lld is not a multiple of group=%d", (long long)K, group);
+  if ((uint64_t)N * (uint64_t)K * (uint64_t)esize(dt) > kMaxBufferBytes || N > INT32_MAX)
+    return fail(AWQ_ERR_UNSUPPORTED, "W [%lld, %lld] exceeds the 4 GiB operand limit",
+                (long long)N, (long long)K);
+  return AWQ_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Workspace layout of the search.
+// ---------------------------------------------------------------------------
+awq_status_t compute_layout(awq_dtype_t dt, int64_t N, int64_t K, int64_t T, int n_alpha,
+                            uint32_t flags, size_t ws_bytes, awq_search_layout_t* L) {
+  const awq::GemmTiles gt = awq::gemm_tiles(dt);
+  const bool delta = (flags & AWQ_SEARCH_REFERENCE_OUTPUT) == 0;
+  std::memset(L, 0, sizeof(*L));
+  L->tile_m = gt.tile_m;
+  L->tile_n = gt.tile_n;
+  L->tiles_m = (int32_t)((T + gt.tile_m - 1) / gt.tile_m);
+  L->tiles_n = (int32_t)((N + gt.tile_n - 1) / gt.tile_n);
+  size_t off = 0;
+  L->s_table_offset = off;
+  off = align_up(off + (size_t)n_alpha * (size_t)K * 4);
+  L->partials_offset = off;
+  off = align_up(off + (size_t)n_alpha * (size_t)L->tiles_m * (size_t)L->tiles_n * 8);
+  if (delta) {
+    L->y_ref_offset = SIZE_MAX;
+  } else {
+    L->y_ref_offset = off;
+    off = align_up(off + (size_t)T * (size_t)N * 4);
+  }
+  L->w_hat_offset = off;
+  const size_t per_alpha = align_up((size_t)N * (size_t)K * (size_t)esize(dt));
+  int batch = n_alpha;
+  if (ws_bytes != 0) {
+    if (ws_bytes < off + per_alpha)
+      return fail(AWQ_ERR_WORKSPACE, "workspace of %zu bytes is below the minimum %zu", ws_bytes,
+                  off + per_alpha);
+    const size_t fit = (ws_bytes - off) / per_alpha;
+    if (fit < (size_t)batch) batch = (int)fit;
+  }
+  // keep the flattened GEMM grid within int range
+  const int64_t tiles = (int64_t)L->tiles_m * L->tiles_n;
+  const int64_t max_batch = (int64_t)(INT32_MAX / 2) / (tiles > 0 ? tiles : 1);
+  if (batch > max_batch) batch = (int)(max_batch > 0 ? max_batch : 1);
+  L->alpha_batch = batch;
+  L->total_bytes = off + (size_t)batch * per_alpha;
+  return AWQ_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Per-launch event timing.
+// ---------------------------------------------------------------------------
+struct ProfRec {
+  std::string name;
+  hipEvent_t start, stop;
+};
+std::mutex g_prof_mu;
+std::vector<ProfRec> g_prof;
+std::atomic<bool> g_prof_on{false};
+
+}  // namespace
+
+namespace awq {
+
+int prof_begin(const char* kernel, hipStream_t stream) {
+  if (!g_prof_on.load(std::memory_order_relaxed)) return -1;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  ProfRec r;
+  r.name = kernel;
+  if (hipEventCreate(&r.start) != hipSuccess) return -1;
+  if (hipEventCreate(&r.stop) != hipSuccess) {
+    (void)hipEventDestroy(r.start);
+    return -1;
+  }
+  (void)hipEventRecord(r.start, stream);
+  g_prof.push_back(r);
+  return (int)g_prof.size() - 1;
+}
+
+void prof_end(int token, hipStream_t stream) {
+  if (token < 0) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if ((size_t)token < g_prof.size()) (void)hipEventRecord(g_prof[token].stop, stream);
+}
+
+}  // namespace awq
+
+#define AWQ_GUARD_BEGIN try {
+#define AWQ_GUARD_END                                                  \
+  }                                                                    \
+  catch (...) {                                                        \
+    return fail(AWQ_ERR_HIP, "unexpected C++ exception in the library"); \
+  }
+
+extern "C" {
+
+const char* awq_version(void) { return "awq-mi355x 0.1"; }
+
+const char* awq_last_error(void) { return g_last_error.c_str(); }
+
+size_t awq_act_stats_workspace_size(int64_t T, int64_t K) {
+  if (T < 1 || K < 1) return 0;
+  return align_up(awq::act_stats_ws_bytes(T, K));
+}
+
+awq_status_t awq_act_stats(const void* X, awq_dtype_t x_dtype, int64_t T, int64_t K, float* a_out,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  AWQ_GUARD_BEGIN
+  if (!valid_dtype(x_dtype)) return fail(AWQ_ERR_INVALID_ARG, "unknown dtype %d", (int)x_dtype);
+  if (T < 1 || K < 1) return fail(AWQ_ERR_INVALID_ARG, "T and K must be >= 1");
+  if (!X || !a_out) return fail(AWQ_ERR_INVALID_ARG, "null X or a_out");
+  const size_t need = awq_act_stats_workspace_size(T, K);
+  if (!workspace || workspace_bytes < need)
+    return fail(AWQ_ERR_WORKSPACE, "act_stats needs %zu workspace bytes, got %zu", need,
+                workspace_bytes);
+  if (!aligned(workspace, 8)) return fail(AWQ_ERR_WORKSPACE, "workspace must be 8-byte aligned");
+  hipError_t e = awq::launch_act_stats(X, x_dtype, T, K, a_out, workspace, stream);
+  if (e != hipSuccess) return hip_fail(e, "act_stats launch");
+  return AWQ_OK;
+  AWQ_GUARD_END
+}
+
+awq_status_t awq_scale_table(const float* a, int64_t K, const float* alphas, int n_alpha,
+                             float* s_out, hipStream_t stream) {
+  AWQ_GUARD_BEGIN
+  if (!a || !alphas || !s_out) return fail(AWQ_ERR_INVALID_ARG, "null pointer");
+  if (K < 1 || n_alpha < 1 || n_alpha > kMaxAlpha)
+    return fail(AWQ_ERR_INVALID_ARG, "K=%lld n_alpha=%d", (long long)K, n_alpha);
+  for (int k = 0; k < n_alpha; ++k)
+    if (!std::isfinite(alphas[k])) return fail(AWQ_ERR_INVALID_ARG, "alpha[%d] is not finite", k);
+  for (int c0 = 0; c0 < n_alpha; c0 += 64) {
+    awq::AlphaChunk ch;
+    ch.n = std::min(64, n_alpha - c0);
+    for (int i = 0; i < ch.n; ++i) ch.v[i] = alphas[c0 + i];
+    hipError_t e = awq::launch_scale_table(a, K, ch, s_out + (size_t)c0 * K, stream);
+    if (e != hipSuccess) return hip_fail(e, "scale_table launch");
+  }
+  return AWQ_OK;
+  AWQ_GUARD_END
+}
+
+awq_status_t awq_fake_quant(const void* W, awq_dtype_t w_dtype, int64_t N, int64_t K,
+                            const float* s, int n_s, int bits, int group, uint32_t flags,
+                            void* out, awq_dtype_t out_dtype, hipStream_t stream) {
+  AWQ_GUARD_BEGIN
+  awq_status_t st = check_quant_args(w_dtype, N, K, bits, group);
+  if (st != AWQ_OK) return st;
+  if (!W || !s || !out) return fail(AWQ_ERR_INVALID_ARG, "null pointer");
+  if (n_s < 1) return fail(AWQ_ERR_INVALID_ARG, "n_s must be >= 1");
+  if (flags & ~AWQ_FQ_WEIGHT_DELTA) return fail(AWQ_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  if (out_dtype != w_dtype)
+    return fail(AWQ_ERR_UNSUPPORTED, "out_dtype must equal w_dtype");
+  if (!aligned(W, 16) || !aligned(s, 16) || !aligned(out, 16))
+    return fail(AWQ_ERR_UNSUPPORTED, "W, s and out must be 16-byte aligned");
+  hipError_t e = awq::launch_fake_quant(W, w_dtype, N, K, s, n_s, bits, group,
+                                        (flags & AWQ_FQ_WEIGHT_DELTA) != 0, out, stream);
+  if (e != hipSuccess) return hip_fail(e, "fake_quant launch");
+  return AWQ_OK;
+  AWQ_GUARD_END
+}
+
+awq_status_t awq_search_layout(awq_dtype_t dtype, int64_t N, int64_t K, int64_t T, int n_alpha,
+                               uint32_t flags, size_t workspace_bytes,
+                               awq_search_layout_t* layout_out) {
+  AWQ_GUARD_BEGIN
+  if (!layout_out) return fail(AWQ_ERR_INVALID_ARG, "null layout_out");
+  if (!valid_dtype(dtype)) return fail(AWQ_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (N < 1 || K < 1 || T < 1 || n_alpha < 1 || n_alpha > kMaxAlpha)
+    return fail(AWQ_ERR_INVALID_ARG, "sizes must be >= 1 and n_alpha <= %d", kMaxAlpha);
+  if (flags & ~AWQ_SEARCH_REFERENCE_OUTPUT)
+    return fail(AWQ_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  return compute_layout(dtype, N, K, T, n_alpha, flags, workspace_bytes, layout_out);
+  AWQ_GUARD_END
+}
+
+awq_status_t awq_search_scales(const void* W, const void* X, awq_dtype_t dtype, int64_t N,
+                               int64_t K, int64_t T, const float* a, int bits, int group,
+                               const float* alphas, int n_alpha, uint32_t flags,
+                               double* losses_out, float* s_best_out, int32_t* best_idx_out,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  AWQ_GUARD_BEGIN
+  awq_status_t st = check_quant_args(dtype, N, K, bits, group);
+  if (st != AWQ_OK) return st;
+  if (!W || !X || !a || !alphas || !losses_out || !s_best_out || !best_idx_out)
+    return fail(AWQ_ERR_INVALID_ARG, "null pointer");
+  if (T < 1) return fail(AWQ_ERR_INVALID_ARG, "T must be >= 1");
+  if (n_alpha < 1 || n_alpha > kMaxAlpha)
+    return fail(AWQ_ERR_INVALID_ARG, "n_alpha=%d outside [1, %d]", n_alpha, kMaxAlpha);
+  if (flags & ~AWQ_SEARCH_REFERENCE_OUTPUT)
+    return fail(AWQ_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  if ((flags & AWQ_SEARCH_REFERENCE_OUTPUT) && dtype == AWQ_BF16)
+    return fail(AWQ_ERR_UNSUPPORTED,
+                "the reference-output form is not offered for bf16 (W_hat rounding exceeds the "
+                "loss tolerance); use AWQ_SEARCH_WEIGHT_DELTA");
+  for (int k = 0; k < n_alpha; ++k)
+    if (!std::isfinite(alphas[k])) return fail(AWQ_ERR_INVALID_ARG, "alpha[%d] is not finite", k);
+  if ((uint64_t)T * (uint64_t)K * (uint64_t)esize(dtype) > kMaxBufferBytes || T > INT32_MAX)
+    return fail(AWQ_ERR_UNSUPPORTED, "X [%lld, %lld] exceeds the 4 GiB operand limit",
+                (long long)T, (long long)K);
+  if (!aligned(W, 16) || !aligned(X, 16) || !aligned(a, 4) || !aligned(s_best_out, 4))
+    return fail(AWQ_ERR_UNSUPPORTED, "W and X must be 16-byte aligned");
+  if (!workspace) return fail(AWQ_ERR_WORKSPACE, "null workspace");
+  if (!aligned(workspace, 256)) return fail(AWQ_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  awq_search_layout_t L;
+  st = compute_layout(dtype, N, K, T, n_alpha, flags, workspace_bytes, &L);
+  if (st != AWQ_OK) return st;
+  if (workspace_bytes < L.total_bytes)
+    return fail(AWQ_ERR_WORKSPACE, "workspace of %zu bytes is below %zu", workspace_bytes,
+                L.total_bytes);
+
+  char* ws = static_cast<char*>(workspace);
+  float* s_table = reinterpret_cast<float*>(ws + L.s_table_offset);
+  double* partials = reinterpret_cast<double*>(ws + L.partials_offset);
+  const bool delta = (flags & AWQ_SEARCH_REFERENCE_OUTPUT) == 0;
+  float* y_ref = delta ? nullptr : reinterpret_cast<float*>(ws + L.y_ref_offset);
+  void* w_hat = ws + L.w_hat_offset;
+
+  hipError_t e;
+  // step 2: scale table
+  for (int c0 = 0; c0 < n_alpha; c0 += 64) {
+    awq::AlphaChunk ch;
+    ch.n = std::min(64, n_alpha - c0);
+    for (int i = 0; i < ch.n; ++i) ch.v[i] = alphas[c0 + i];
+    e = awq::launch_scale_table(a, K, ch, s_table + (size_t)c0 * K, stream);
+    if (e != hipSuccess) return hip_fail(e, "scale_table launch");
+  }
+  // reference output W X, once per layer
+  if (!delta) {
+    e = awq::launch_gemm(awq::Epi::kStore, dtype, X, W, 1, T, N, K, y_ref, nullptr, 0, stream);
+    if (e != hipSuccess) return hip_fail(e, "reference GEMM launch");
+  }
+  // steps 3-4 over the grid, alpha_batch candidates per pass
+  for (int a0 = 0; a0 < n_alpha; a0 += L.alpha_batch) {
+    const int nb = std::min(L.alpha_batch, n_alpha - a0);
+    e = awq::launch_fake_quant(W, dtype, N, K, s_table + (size_t)a0 * K, nb, bits, group, delta,
+                               w_hat, stream);
+    if (e != hipSuccess) return hip_fail(e, "fake_quant launch");
+    e = awq::launch_gemm(delta ? awq::Epi::kSseDelta : awq::Epi::kSseRef, dtype, X, w_hat, nb, T,
+                         N, K, y_ref, partials, a0, stream);
+    if (e != hipSuccess) return hip_fail(e, "candidate GEMM launch");
+  }
+  // step 5: losses, argmin, best scales
+  const int64_t tiles = (int64_t)L.tiles_m * L.tiles_n;
+  e = awq::launch_loss_argmin(partials, n_alpha, tiles, 1.0 / ((double)T * (double)N), s_table, K,
+                              losses_out, best_idx_out, s_best_out, stream);
+  if (e != hipSuccess) return hip_fail(e, "loss/argmin launch");
+  return AWQ_OK;
+  AWQ_GUARD_END
+}
+
+awq_status_t awq_quantize_pack(const void* W, awq_dtype_t w_dtype, int64_t N, int64_t K,
+                               const float* s, int bits, int group, uint32_t* codes_out,
+                               float* scales_out, uint8_t* zeros_out, hipStream_t stream) {
+  AWQ_GUARD_BEGIN
+  awq_status_t st = check_quant_args(w_dtype, N, K, bits, group);
+  if (st != AWQ_OK) return st;
+  if (!W || !s || !codes_out || !scales_out || !zeros_out)
+    return fail(AWQ_ERR_INVALID_ARG, "null pointer");
+  if (!aligned(W, 16) || !aligned(s, 16) || !aligned(codes_out, 4) || !aligned(scales_out, 4))
+    return fail(AWQ_ERR_UNSUPPORTED, "W and s must be 16-byte aligned, codes and scales 4-byte");
+  hipError_t e = awq::launch_quantize_pack(W, w_dtype, N, K, s, bits, group, codes_out, scales_out,
+                                           zeros_out, stream);
+  if (e != hipSuccess) return hip_fail(e, "quantize_pack launch");
+  return AWQ_OK;
+  AWQ_GUARD_END
+}
+
+awq_status_t awq_profile_enable(int enable) {
+  g_prof_on.store(enable != 0);
+  return AWQ_OK;
+}
+
+awq_status_t awq_profile_read(const char* prefix, int64_t* launches, double* total_ms) {
+  AWQ_GUARD_BEGIN
+  if (!launches || !total_ms) return fail(AWQ_ERR_INVALID_ARG, "null output");
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  const size_t plen = prefix ? std::strlen(prefix) : 0;
+  int64_t n = 0;
+  double ms = 0.0;
+  for (const ProfRec& r : g_prof) {
+    if (plen && r.name.compare(0, plen, prefix) != 0) continue;
+    hipError_t e = hipEventSynchronize(r.stop);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    float t = 0.f;
+    e = hipEventElapsedTime(&t, r.start, r.stop);
+    if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+    ms += t;
+    ++n;
+  }
+  *launches = n;
+  *total_ms = ms;
+  return AWQ_OK;
+  AWQ_GUARD_END
+}
+
+awq_status_t awq_profile_reset(void) {
+  AWQ_GUARD_BEGIN
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  for (ProfRec& r : g_prof) {
+    (void)hipEventDestroy(r.start);
+    (void)hipEventDestroy(r.stop);
+  }
+  g_prof.clear();
+  return AWQ_OK;
+  AWQ_GUARD_END
+}
+
+}  // extern "C"

@@ -1,0 +1,85 @@
+// Internal declarations shared by the HIP translation units of the AWQ
+// scale-search library (gfx950 only).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "../../include/awq.h"
+
+namespace awq {
+
+// ---- vector types -----------------------------------------------------------
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+
+// Element tags: storage type of W / X / W_hat.
+struct F32T { typedef float storage; static constexpr int size = 4; };
+struct F16T { typedef _Float16 storage; static constexpr int size = 2; };
+struct BF16T { typedef __bf16 storage; static constexpr int size = 2; };
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(_Float16 x) { return (float)x; }
+__device__ __forceinline__ float to_f32(__bf16 x) { return (float)x; }
+
+// Round-to-nearest-even conversions out of fp32.
+template <typename S> __device__ __forceinline__ S from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ _Float16 from_f32<_Float16>(float x) { return (_Float16)x; }
+template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return (__bf16)x; }
+
+// ---- launch plumbing ----------------------------------------------------------
+// Optional per-launch event timing (see awq_profile_* in the public header).
+// prof_begin returns a token (or -1 when profiling is off) to hand to prof_end.
+int prof_begin(const char* kernel, hipStream_t stream);
+void prof_end(int token, hipStream_t stream);
+
+struct ProfScope {
+  int tok;
+  hipStream_t st;
+  ProfScope(const char* name, hipStream_t s) : tok(prof_begin(name, s)), st(s) {}
+  ~ProfScope() { prof_end(tok, st); }
+};
+
+// ---- launchers (each returns hipSuccess or the launch error) ---------------------
+// act_stats.hip
+size_t act_stats_ws_bytes(int64_t T, int64_t K);
+hipError_t launch_act_stats(const void* X, awq_dtype_t dt, int64_t T, int64_t K, float* a,
+                            void* ws, hipStream_t st);
+
+// quant.hip
+struct AlphaChunk {
+  int n;
+  float v[64];
+};
+hipError_t launch_scale_table(const float* a, int64_t K, const AlphaChunk& al, float* s_out,
+                              hipStream_t st);
+hipError_t launch_fake_quant(const void* W, awq_dtype_t dt, int64_t N, int64_t K,
+                             const float* s, int n_s, int bits, int group, bool delta_form,
+                             void* out, hipStream_t st);
+hipError_t launch_quantize_pack(const void* W, awq_dtype_t dt, int64_t N, int64_t K,
+                                const float* s, int bits, int group, uint32_t* codes,
+                                float* scales, uint8_t* zeros, hipStream_t st);
+
+// gemm_sse.hip
+enum class Epi { kStore = 0, kSseRef = 1, kSseDelta = 2 };
+struct GemmTiles {
+  int tile_m, tile_n;
+};
+GemmTiles gemm_tiles(awq_dtype_t dt);
+// C[t, n] = sum_k X[t, k] * B[n, k] over nb weight matrices B_b = B + b*N*K.
+//   kStore:    Y[t, n] = C (nb must be 1)
+//   kSseRef:   partials[(a0 + b)][tm][tn] = sum over the tile of (Y - C)^2
+//   kSseDelta: partials[(a0 + b)][tm][tn] = sum over the tile of C^2
+hipError_t launch_gemm(Epi epi, awq_dtype_t dt, const void* X, const void* B, int nb,
+                       int64_t T, int64_t N, int64_t K, float* Y, double* partials,
+                       int a0, hipStream_t st);
+hipError_t launch_loss_argmin(const double* partials, int n_alpha, int64_t tiles_per_alpha,
+                              double inv_count, const float* s_table, int64_t K,
+                              double* losses, int32_t* best, float* s_best, hipStream_t st);
+
+}  // namespace awq

@@ -1,0 +1,339 @@
+// Scale table, group-wise fake quantisation and final packing.
+//
+// AWQ Q&A page (aivaro.ru), sections 5 and 9: the scaled weights are
+// quantised round-to-nearest per group, asymmetric (zero_point), group size
+// q_group_size, w_bit bits.  AWQ reading notes, section "Measures": for each
+// candidate exponent alpha the scales are s = a^alpha, the weights are scaled
+// per input channel, quantised group-wise and dequantised, and the chosen
+// scales' codes are saved with their per-group metadata.
+//
+// This file is compiled with -ffp-contract=off.  Every quantiser operation is
+// a single IEEE fp32 operation with round-to-nearest-even (division is the
+// correctly rounded sequence, rint is v_rndne_f32, denormals are kept), in
+// the order: w' = w*s; mx, mn over the group; delta = (mx - mn)/qmax floored
+// at 1e-10; z = clamp(rint(-mn/delta)); c = clamp(rint(w'/delta) + z);
+// W_hat = ((c - z)*delta)/s.  So codes, steps and zero-points match any other
+// IEEE evaluation of that order bit for bit.
+#include "common.h"
+
+namespace awq {
+namespace {
+
+constexpr float kAMin = 1e-8f;
+constexpr float kDeltaMin = 1e-10f;
+
+// ---------------------------------------------------------------------------
+// min / max across the `lanes` consecutive lanes that hold one group (a power
+// of two; groups start at multiples of it; the branches are wave-uniform).
+// The steps inside a 16-lane DPP row use quad permutes and the half-row / row
+// mirrors; wider groups finish with cross-row swizzles.  Every lane ends with the group's
+// min and max.
+// ---------------------------------------------------------------------------
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xf, 0xf, false));
+}
+
+__device__ __forceinline__ void group_minmax(float& mn, float& mx, int lanes) {
+  if (lanes >= 2) {
+    mn = fminf(mn, dpp<0xB1>(mn));   // quad_perm [1,0,3,2]
+    mx = fmaxf(mx, dpp<0xB1>(mx));
+  }
+  if (lanes >= 4) {
+    mn = fminf(mn, dpp<0x4E>(mn));   // quad_perm [2,3,0,1]
+    mx = fmaxf(mx, dpp<0x4E>(mx));
+  }
+  if (lanes >= 8) {
+    mn = fminf(mn, dpp<0x141>(mn));  // row_half_mirror
+    mx = fmaxf(mx, dpp<0x141>(mx));
+  }
+  if (lanes >= 16) {
+    mn = fminf(mn, dpp<0x140>(mn));  // row_mirror
+    mx = fmaxf(mx, dpp<0x140>(mx));
+  }
+  if (lanes >= 32) {
+    mn = fminf(mn, __shfl_xor(mn, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+  }
+  if (lanes >= 64) {
+    mn = fminf(mn, __shfl_xor(mn, 32));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+  }
+}
+
+struct GroupQ {
+  float delta, z;
+};
+
+__device__ __forceinline__ GroupQ group_params(float mn, float mx, float qmax) {
+  GroupQ g;
+  g.delta = fmaxf((mx - mn) / qmax, kDeltaMin);
+  g.z = fminf(fmaxf(__builtin_rintf(-mn / g.delta), 0.0f), qmax);
+  return g;
+}
+
+__device__ __forceinline__ float code_of(float wp, const GroupQ& g, float qmax) {
+  return fminf(fmaxf(__builtin_rintf(wp / g.delta) + g.z, 0.0f), qmax);
+}
+
+template <typename S>
+__device__ __forceinline__ void load8(const S* p, float (&v)[8]);
+template <>
+__device__ __forceinline__ void load8<float>(const float* p, float (&v)[8]) {
+  f32x4 a = *reinterpret_cast<const f32x4*>(p);
+  f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+template <typename S>
+__device__ __forceinline__ void load8(const S* p, float (&v)[8]) {
+  i32x4 raw = *reinterpret_cast<const i32x4*>(p);
+  const S* e = reinterpret_cast<const S*>(&raw);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = to_f32(e[i]);
+}
+
+template <typename S>
+__device__ __forceinline__ void store8(S* p, const float (&v)[8]);
+template <>
+__device__ __forceinline__ void store8<float>(float* p, const float (&v)[8]) {
+  *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
+  *reinterpret_cast<f32x4*>(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
+}
+template <typename S>
+__device__ __forceinline__ void store8(S* p, const float (&v)[8]) {
+  i32x4 raw;
+  S* e = reinterpret_cast<S*>(&raw);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) e[i] = from_f32<S>(v[i]);
+  *reinterpret_cast<i32x4*>(p) = raw;
+}
+
+// ---------------------------------------------------------------------------
+// s[k][j] = fp32(pow(fp64(max(a_j, 1e-8)), fp64(alpha_k)))
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void scale_table_kernel(const float* __restrict__ a, int64_t K,
+                                                          AlphaChunk al, float* __restrict__ s) {
+  const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= K) return;
+  const double x = (double)fmaxf(a[j], kAMin);
+  for (int k = 0; k < al.n; ++k) s[(int64_t)k * K + j] = (float)pow(x, (double)al.v[k]);
+}
+
+// ---------------------------------------------------------------------------
+// Fake quantisation of W diag(s_k) for n_s scale vectors in one pass over W.
+//
+// A workgroup owns a tile of 16 rows x 512 columns.  Each wave covers one
+// 512-column row segment per step (8 consecutive columns per lane, 16-byte
+// loads), so the tile is read from HBM once into registers (4 rows x 8
+// values per lane) and reused for every scale vector; only the 8 scales of
+// the lane's columns are fetched per vector.  A group of G channels lives in
+// G/8 consecutive lanes and is reduced with DPP.  Output k is written to
+// out + k*N*K.
+// ---------------------------------------------------------------------------
+constexpr int kFqThreads = 256;
+constexpr int kFqCols = 512;                  // columns per workgroup (one wave-row)
+constexpr int kFqRowSteps = 4;                // rows per wave
+constexpr int kFqRows = kFqRowSteps * (kFqThreads / 64);
+
+template <typename S, typename O, bool kDelta>
+__global__ __launch_bounds__(kFqThreads) void fake_quant_kernel(
+    const S* __restrict__ W, int64_t N, int64_t K, const float* __restrict__ s, int n_s,
+    float qmax, int lanes, O* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t col = (int64_t)blockIdx.x * kFqCols + lane * 8;
+  const int64_t row0 = (int64_t)blockIdx.y * kFqRows + wave;
+  const bool col_ok = col < K;
+
+  float w[kFqRowSteps][8];
+  bool row_ok[kFqRowSteps];
+#pragma unroll
+  for (int p = 0; p < kFqRowSteps; ++p) {
+    const int64_t r = row0 + (int64_t)p * (kFqThreads / 64);
+    row_ok[p] = r < N;
+    if (col_ok && row_ok[p]) {
+      load8(W + r * K + col, w[p]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w[p][i] = 0.0f;
+    }
+  }
+
+  for (int k = 0; k < n_s; ++k) {
+    float sv[8];
+    if (col_ok) {
+      load8(s + (int64_t)k * K + col, sv);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sv[i] = 1.0f;
+    }
+    O* outk = out + (int64_t)k * N * K;
+#pragma unroll
+    for (int p = 0; p < kFqRowSteps; ++p) {
+      float wp[8];
+      float mn, mx;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) wp[i] = w[p][i] * sv[i];
+      mn = wp[0];
+      mx = wp[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) {
+        mn = fminf(mn, wp[i]);
+        mx = fmaxf(mx, wp[i]);
+      }
+      group_minmax(mn, mx, lanes);
+      const GroupQ g = group_params(mn, mx, qmax);
+      float o[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float c = code_of(wp[i], g, qmax);
+        const float deq = (c - g.z) * g.delta;
+        const float what = deq / sv[i];
+        o[i] = kDelta ? (w[p][i] - what) : what;
+      }
+      const int64_t r = row0 + (int64_t)p * (kFqThreads / 64);
+      if (col_ok && row_ok[p]) store8(outk + r * K + col, o);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Final quantisation + packing for one scale vector.
+//
+// One lane owns 32 consecutive columns of a row: it loads them, reduces its
+// share of the group (G/32 lanes per group, DPP), computes the 32 codes and
+// writes them as `bits` uint32 words -- exactly its slice of the row's
+// little-endian bitstream (32 codes x bits bits).  The first lane of each
+// group writes the group's step and zero-point.
+// ---------------------------------------------------------------------------
+template <typename S, int BITS>
+__global__ __launch_bounds__(256) void quantize_pack_kernel(
+    const S* __restrict__ W, int64_t N, int64_t K, const float* __restrict__ s, int group,
+    int lanes, uint32_t* __restrict__ codes, float* __restrict__ scales,
+    uint8_t* __restrict__ zeros) {
+  const int64_t chunks_per_row = K / 32;
+  const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const bool ok = q < N * chunks_per_row;
+  const int64_t row = ok ? q / chunks_per_row : 0;
+  const int64_t cc = ok ? q % chunks_per_row : 0;
+  const int64_t col0 = cc * 32;
+  const float qmax = (float)((1 << BITS) - 1);
+
+  float wp[32];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    float v[8], sv[8];
+    if (ok) {
+      load8(W + row * K + col0 + h * 8, v);
+      load8(s + col0 + h * 8, sv);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) { v[i] = 0.0f; sv[i] = 1.0f; }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) wp[h * 8 + i] = v[i] * sv[i];
+  }
+  float mn = wp[0], mx = wp[0];
+#pragma unroll
+  for (int i = 1; i < 32; ++i) {
+    mn = fminf(mn, wp[i]);
+    mx = fmaxf(mx, wp[i]);
+  }
+  group_minmax(mn, mx, lanes);
+  const GroupQ g = group_params(mn, mx, qmax);
+
+  // 32 codes of `bits` bits -> `bits` words; bit p of the slice is bit
+  // p%32 of word p/32.
+  uint32_t words[BITS];
+#pragma unroll
+  for (int i = 0; i < BITS; ++i) words[i] = 0u;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    const uint32_t c = (uint32_t)code_of(wp[j], g, qmax);
+    const int p = BITS * j;               // compile-time after unrolling
+    const int wi = p >> 5, sh = p & 31;
+    words[wi] |= c << sh;
+    if (sh + BITS > 32) words[wi + 1] |= c >> (32 - sh);   // BITS <= 8: two words at most
+  }
+  if (!ok) return;
+  uint32_t* dst = codes + row * (chunks_per_row * BITS) + cc * BITS;
+#pragma unroll
+  for (int t = 0; t < BITS; ++t) dst[t] = words[t];
+  if ((cc % lanes) == 0) {
+    const int64_t gi = row * (K / group) + col0 / group;
+    scales[gi] = g.delta;
+    zeros[gi] = (uint8_t)g.z;
+  }
+}
+
+template <typename S, typename O, bool kDelta>
+hipError_t fq_dispatch(const void* W, int64_t N, int64_t K, const float* s, int n_s, int bits,
+                       int group, void* out, hipStream_t st) {
+  dim3 grid((unsigned)((K + kFqCols - 1) / kFqCols), (unsigned)((N + kFqRows - 1) / kFqRows));
+  const float qmax = (float)((1 << bits) - 1);
+  const S* w = static_cast<const S*>(W);
+  O* o = static_cast<O*>(out);
+  ProfScope p("awq_fake_quant", st);
+  fake_quant_kernel<S, O, kDelta><<<grid, kFqThreads, 0, st>>>(w, N, K, s, n_s, qmax, group / 8, o);
+  return hipGetLastError();
+}
+
+template <typename S>
+hipError_t pack_dispatch(const void* W, int64_t N, int64_t K, const float* s, int bits, int group,
+                         uint32_t* codes, float* scales, uint8_t* zeros, hipStream_t st) {
+  const int64_t threads = N * (K / 32);
+  const unsigned blocks = (unsigned)((threads + 255) / 256);
+  const S* w = static_cast<const S*>(W);
+  ProfScope p("awq_quantize_pack", st);
+  const int lanes = group / 32;
+  switch (bits) {
+    case 2: quantize_pack_kernel<S, 2><<<blocks, 256, 0, st>>>(w, N, K, s, group, lanes, codes, scales, zeros); break;
+    case 3: quantize_pack_kernel<S, 3><<<blocks, 256, 0, st>>>(w, N, K, s, group, lanes, codes, scales, zeros); break;
+    case 4: quantize_pack_kernel<S, 4><<<blocks, 256, 0, st>>>(w, N, K, s, group, lanes, codes, scales, zeros); break;
+    case 5: quantize_pack_kernel<S, 5><<<blocks, 256, 0, st>>>(w, N, K, s, group, lanes, codes, scales, zeros); break;
+    case 6: quantize_pack_kernel<S, 6><<<blocks, 256, 0, st>>>(w, N, K, s, group, lanes, codes, scales, zeros); break;
+    case 7: quantize_pack_kernel<S, 7><<<blocks, 256, 0, st>>>(w, N, K, s, group, lanes, codes, scales, zeros); break;
+    default: quantize_pack_kernel<S, 8><<<blocks, 256, 0, st>>>(w, N, K, s, group, lanes, codes, scales, zeros); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_scale_table(const float* a, int64_t K, const AlphaChunk& al, float* s_out,
+                              hipStream_t st) {
+  ProfScope p("awq_scale_table", st);
+  scale_table_kernel<<<(unsigned)((K + 255) / 256), 256, 0, st>>>(a, K, al, s_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_fake_quant(const void* W, awq_dtype_t dt, int64_t N, int64_t K, const float* s,
+                             int n_s, int bits, int group, bool delta_form, void* out,
+                             hipStream_t st) {
+  switch (dt) {
+    case AWQ_F32:
+      return delta_form ? fq_dispatch<float, float, true>(W, N, K, s, n_s, bits, group, out, st)
+                        : fq_dispatch<float, float, false>(W, N, K, s, n_s, bits, group, out, st);
+    case AWQ_F16:
+      return delta_form
+                 ? fq_dispatch<_Float16, _Float16, true>(W, N, K, s, n_s, bits, group, out, st)
+                 : fq_dispatch<_Float16, _Float16, false>(W, N, K, s, n_s, bits, group, out, st);
+    default:
+      return delta_form
+                 ? fq_dispatch<__bf16, __bf16, true>(W, N, K, s, n_s, bits, group, out, st)
+                 : fq_dispatch<__bf16, __bf16, false>(W, N, K, s, n_s, bits, group, out, st);
+  }
+}
+
+hipError_t launch_quantize_pack(const void* W, awq_dtype_t dt, int64_t N, int64_t K,
+                                const float* s, int bits, int group, uint32_t* codes,
+                                float* scales, uint8_t* zeros, hipStream_t st) {
+  switch (dt) {
+    case AWQ_F32: return pack_dispatch<float>(W, N, K, s, bits, group, codes, scales, zeros, st);
+    case AWQ_F16: return pack_dispatch<_Float16>(W, N, K, s, bits, group, codes, scales, zeros, st);
+    default: return pack_dispatch<__bf16>(W, N, K, s, bits, group, codes, scales, zeros, st);
+  }
+}
+
+}  // namespace awq

@@ -1,0 +1,152 @@
+"""The C-ABI library loads, exports every declared entry point, and rejects
+invalid arguments on the host before touching a device (no GPU needed)."""
+
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+import torch
+
+import post_weight_quantization_act_amd as awq
+
+HEADER = Path(__file__).resolve().parents[1] / "include" / "awq.h"
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(awq_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("awq_act_stats", "awq_search_scales", "awq_quantize_pack", "awq_fake_quant",
+              "awq_scale_table", "awq_search_layout", "awq_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = awq.library()
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+    assert awq.awq_version().startswith("awq-mi355x")
+
+
+def test_binding_covers_every_entry_point():
+    for n in declared_functions():
+        if n in ("awq_last_error",):
+            continue
+        assert hasattr(awq, n), n
+
+
+def _call(name, *args):
+    return getattr(awq.library(), name)(*args)
+
+
+NULL = None
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every case fails validation first
+
+
+@pytest.mark.parametrize("args,status", [
+    ((NULL, 1, 4, 4, FAKE, FAKE, 1 << 20, NULL), -1),           # null X
+    ((FAKE, 7, 4, 4, FAKE, FAKE, 1 << 20, NULL), -1),           # bad dtype
+    ((FAKE, 1, 0, 4, FAKE, FAKE, 1 << 20, NULL), -1),           # T = 0
+    ((FAKE, 1, 4, 4, FAKE, NULL, 0, NULL), -3),                 # no workspace
+])
+def test_act_stats_validation(args, status):
+    assert _call("awq_act_stats", *args) == status
+    assert awq.library().awq_last_error().decode() != ""
+
+
+def _pack_args(**over):
+    a = dict(W=FAKE, dt=1, N=8, K=256, s=FAKE, bits=4, group=128, codes=FAKE, scales=FAKE,
+             zeros=FAKE, stream=NULL)
+    a.update(over)
+    return tuple(a.values())
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(W=NULL), -1),
+    (dict(K=200), -1),                    # K % group != 0
+    (dict(group=96, K=288), -2),          # not a power of two
+    (dict(group=16, K=256), -2),          # below 32
+    (dict(bits=1), -2),
+    (dict(bits=9), -2),
+    (dict(N=0), -1),
+    (dict(dt=3), -1),
+    (dict(N=70000, K=32768, group=128), -2),   # W above 4 GiB
+    (dict(W=ctypes.c_void_p(0x1002)), -2),     # misaligned W
+])
+def test_quantize_pack_validation(over, status):
+    assert _call("awq_quantize_pack", *_pack_args(**over)) == status
+
+
+def _search_args(**over):
+    alphas = (ctypes.c_float * 3)(0.0, 0.5, 0.9)
+    a = dict(W=FAKE, X=FAKE, dt=1, N=8, K=256, T=16, a=FAKE, bits=4, group=128,
+             alphas=ctypes.cast(alphas, ctypes.c_void_p), n_alpha=3, flags=0, losses=FAKE,
+             s_best=FAKE, best=FAKE, ws=ctypes.c_void_p(0x10000), ws_bytes=1 << 30, stream=NULL)
+    a.update(over)
+    return tuple(a.values()), alphas
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(X=NULL), -1),
+    (dict(n_alpha=0), -1),
+    (dict(flags=4), -1),
+    (dict(flags=1, dt=2), -2),                # reference-output form with bf16
+    (dict(T=0), -1),
+    (dict(ws=NULL), -3),
+    (dict(ws_bytes=1024), -3),
+    (dict(ws=ctypes.c_void_p(0x10010)), -3),  # workspace not 256-byte aligned
+    (dict(bits=3, group=100), -2),
+    (dict(T=1 << 20, K=4096), -2),            # X above 4 GiB
+])
+def test_search_validation(over, status):
+    args, keep = _search_args(**over)
+    assert _call("awq_search_scales", *args) == status
+
+
+def test_search_rejects_nan_alpha():
+    args, alphas = _search_args()
+    alphas[1] = float("nan")
+    assert _call("awq_search_scales", *args) == -1
+
+
+def test_search_layout_full_and_batched():
+    N, K, T, n = 4096, 4096, 4096, 20
+    full = awq.awq_search_layout(torch.float16, N, K, T, n, awq.AWQ_SEARCH_REFERENCE_OUTPUT, 0)
+    assert full["alpha_batch"] == n
+    assert (full["tile_m"], full["tile_n"]) == (256, 256)
+    assert (full["tiles_m"], full["tiles_n"]) == (16, 16)
+    assert full["s_table_offset"] == 0
+    assert full["y_ref_offset"] != 2 ** 64 - 1
+    per_alpha = N * K * 2
+    assert full["total_bytes"] == full["w_hat_offset"] + n * per_alpha
+    for off in ("partials_offset", "y_ref_offset", "w_hat_offset"):
+        assert full[off] % 256 == 0
+    assert full["y_ref_offset"] - full["partials_offset"] >= n * 16 * 16 * 8
+    assert full["w_hat_offset"] - full["y_ref_offset"] >= T * N * 4
+    part = awq.awq_search_layout(torch.float16, N, K, T, n, awq.AWQ_SEARCH_REFERENCE_OUTPUT,
+                                 full["w_hat_offset"] + 3 * per_alpha + 5)
+    assert part["alpha_batch"] == 3
+    delta = awq.awq_search_layout(torch.float16, N, K, T, n, awq.AWQ_SEARCH_WEIGHT_DELTA, 0)
+    assert delta["y_ref_offset"] == 2 ** 64 - 1
+    assert delta["total_bytes"] < full["total_bytes"]
+    with pytest.raises(awq.AwqError):
+        awq.awq_search_layout(torch.float16, N, K, T, n, awq.AWQ_SEARCH_REFERENCE_OUTPUT,
+                              full["w_hat_offset"] + 10)
+    f32 = awq.awq_search_layout(torch.float32, 100, 256, 70, 2, 0, 0)
+    assert (f32["tile_m"], f32["tiles_m"], f32["tiles_n"]) == (64, 2, 2)
+
+
+def test_act_stats_workspace_size_is_positive():
+    assert awq.awq_act_stats_workspace_size(65536, 11008) >= 11008 * 8
+    assert awq.awq_act_stats_workspace_size(0, 5) == 0
+
+
+def test_binding_refuses_cpu_tensors():
+    W = torch.zeros(8, 128, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        awq.awq_quantize_pack(W, torch.ones(128), 4, 128)

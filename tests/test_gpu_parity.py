@@ -1,0 +1,306 @@
+"""HIP library vs the CPU oracle on the same seeded inputs (needs a gfx950 GPU).
+
+Bars: integer codes, steps and zero-points bit-exact for a given s; the fake-
+quantised weights equal the oracle's fp32 values rounded to the layer dtype;
+activation statistics within 1e-6 relative; per-alpha losses within 1e-3
+relative; the chosen alpha identical unless the oracle's two best losses are
+within 1e-3 of each other.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import post_weight_quantization_act_amd as awq
+from datagen import random_layer, to_numpy
+
+pytestmark = pytest.mark.gpu
+
+F32 = np.float32
+DT = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    awq.library()
+    yield
+    torch.cuda.synchronize()
+
+
+def cast_like(x32: np.ndarray, dtype: torch.dtype) -> np.ndarray:
+    """Round fp32 values to `dtype` (nearest-even) and widen back to fp32."""
+    return torch.from_numpy(np.ascontiguousarray(x32, dtype=F32)).to(dtype).to(torch.float32).numpy()
+
+
+def dev_f32(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to(torch.float32).cpu().numpy()
+
+
+def log_case(**kw):
+    print("case", kw, flush=True)
+
+
+def rand_scales(K, seed, spread=2.0, outliers=()):
+    rng = np.random.default_rng(seed)
+    s = np.exp(rng.uniform(-spread, spread, K)).astype(F32)
+    for j, f in outliers:
+        s[j] = F32(f)
+    return s
+
+
+# ---------------------------------------------------------------------------
+# step 1: statistics
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
+@pytest.mark.parametrize("T,K", [(1, 32), (37, 1000), (300, 4096), (4097, 520), (64, 7),
+                                 (20000, 136)])
+def test_act_stats(dtype, T, K):
+    log_case(test="act_stats", dtype=dtype, T=T, K=K)
+    _, X = random_layer(7 + T + K, 1, K, T, dtype=dtype, outlier_factor=50.0)
+    a = awq.awq_act_stats(X.cuda())
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(a.cpu().numpy(), oracle.act_stats(to_numpy(X)), rtol=1e-6, atol=0)
+
+
+def test_act_stats_unaligned_rows():
+    log_case(test="act_stats_unaligned")
+    _, X = random_layer(5, 1, 136, 333, dtype="fp16")
+    flat = torch.empty(X.numel() + 1, dtype=X.dtype, device="cuda")
+    Xd = flat[1:].view(333, 136)
+    Xd.copy_(X.cuda())
+    a = awq.awq_act_stats(Xd)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(a.cpu().numpy(), oracle.act_stats(to_numpy(X)), rtol=1e-6, atol=0)
+
+
+# ---------------------------------------------------------------------------
+# step 2: scale table
+# ---------------------------------------------------------------------------
+def test_scale_table():
+    log_case(test="scale_table")
+    rng = np.random.default_rng(1)
+    a = np.concatenate([np.exp(rng.uniform(-6, 5, 3000)), [0.0, 1e-12, 1.0, 2.0]]).astype(F32)
+    alphas = oracle.alpha_grid(20)
+    s = awq.awq_scale_table(torch.from_numpy(a).cuda(), alphas).cpu().numpy()
+    ref = oracle.scale_table(a, alphas)
+    ulp = np.abs(s.view(np.int32).astype(np.int64) - ref.view(np.int32).astype(np.int64))
+    assert ulp.max() <= 1                      # pow is not correctly rounded in either libm
+    assert (ulp == 0).mean() > 0.999
+    np.testing.assert_array_equal(s[0], np.ones_like(a))
+
+
+# ---------------------------------------------------------------------------
+# step 3: fake quantisation
+# ---------------------------------------------------------------------------
+FQ_CASES = [
+    ("fp16", 4, 128, 37, 640), ("fp16", 3, 128, 16, 512), ("bf16", 3, 128, 50, 1024),
+    ("bf16", 4, 64, 9, 192), ("fp32", 4, 128, 21, 384), ("fp16", 2, 32, 5, 96),
+    ("fp16", 8, 256, 7, 768), ("bf16", 5, 512, 3, 1536), ("fp32", 3, 32, 1, 32),
+]
+
+
+@pytest.mark.parametrize("dtype,bits,group,N,K", FQ_CASES)
+@pytest.mark.parametrize("delta", [False, True])
+def test_fake_quant_exact(dtype, bits, group, N, K, delta):
+    log_case(test="fake_quant", dtype=dtype, bits=bits, group=group, N=N, K=K, delta=delta)
+    W, _ = random_layer(N * 31 + K, N, K, 1, dtype=dtype)
+    Wn = to_numpy(W).astype(F32)
+    if N > 2:
+        Wn[1, :group] = np.abs(Wn[1, :group]) + F32(0.001)   # one-signed group
+        Wn[2, :group] = F32(0.25)                             # constant group
+        W = torch.from_numpy(Wn).to(DT[dtype])
+        Wn = to_numpy(W).astype(F32)
+    s = np.stack([rand_scales(K, 3, outliers=((0, 40.0),)), np.ones(K, dtype=F32),
+                  rand_scales(K, 4, spread=4.0)])
+    out = awq.awq_fake_quant(W.cuda(), torch.from_numpy(s).cuda(), bits, group,
+                             awq.AWQ_FQ_WEIGHT_DELTA if delta else awq.AWQ_FQ_WEIGHT_HAT)
+    got = dev_f32(out)
+    for k in range(s.shape[0]):
+        what = oracle.fake_quant(Wn, s[k], bits, group)
+        ref = (Wn - what).astype(F32) if delta else what
+        exp = cast_like(ref, DT[dtype])
+        bad = got[k] != exp
+        assert not bad.any(), (k, np.argwhere(bad)[:5], got[k][bad][:5], exp[bad][:5])
+
+
+def test_fake_quant_alpha_zero_is_rtn():
+    log_case(test="fake_quant_rtn")
+    W, _ = random_layer(77, 64, 1024, 1, dtype="fp16")
+    ones = torch.ones(1024, device="cuda")
+    got = dev_f32(awq.awq_fake_quant(W.cuda(), ones, 4, 128))[0]
+    exp = cast_like(oracle.fake_quant(to_numpy(W), np.ones(1024, F32), 4, 128), torch.float16)
+    np.testing.assert_array_equal(got, exp)
+
+
+# ---------------------------------------------------------------------------
+# step 5b: quantise + pack
+# ---------------------------------------------------------------------------
+PACK_CASES = [
+    ("fp16", 4, 128, 33, 512), ("fp16", 3, 128, 40, 4096), ("bf16", 3, 128, 17, 8192),
+    ("bf16", 4, 64, 8, 320), ("fp32", 4, 128, 12, 256), ("fp16", 2, 32, 3, 64),
+    ("fp16", 5, 256, 6, 512), ("fp16", 6, 32, 2, 96), ("bf16", 7, 512, 4, 1024),
+    ("fp32", 8, 64, 5, 128),
+]
+
+
+@pytest.mark.parametrize("dtype,bits,group,N,K", PACK_CASES)
+def test_quantize_pack_exact(dtype, bits, group, N, K):
+    log_case(test="quantize_pack", dtype=dtype, bits=bits, group=group, N=N, K=K)
+    W, _ = random_layer(N * 7 + K + bits, N, K, 1, dtype=dtype)
+    Wn = to_numpy(W).astype(F32)
+    s = rand_scales(K, bits, outliers=((K // 2, 100.0),))
+    codes, scales, zeros = awq.awq_quantize_pack(W.cuda(), torch.from_numpy(s).cuda(), bits, group)
+    torch.cuda.synchronize()
+    c_ref, d_ref, z_ref = oracle.quantize_pack(Wn, s, bits, group)
+    np.testing.assert_array_equal(codes.cpu().numpy().view(np.uint32), c_ref)
+    np.testing.assert_array_equal(scales.cpu().numpy(), d_ref)
+    np.testing.assert_array_equal(zeros.cpu().numpy(), z_ref)
+
+
+def test_quantize_pack_unit_scale_is_rtn_and_unpacks():
+    log_case(test="quantize_pack_rtn")
+    W, _ = random_layer(99, 16, 256, 1, dtype="fp16")
+    Wn = to_numpy(W).astype(F32)
+    codes, scales, zeros = awq.awq_quantize_pack(W.cuda(), torch.ones(256, device="cuda"), 3, 128)
+    c = oracle.unpack_codes(codes.cpu().numpy().view(np.uint32), 3, 256)
+    c_ref, _, _ = oracle.quantize_codes(Wn, np.ones(256, F32), 3, 128)
+    np.testing.assert_array_equal(c, c_ref)
+    assert c.max() <= 7
+
+
+# ---------------------------------------------------------------------------
+# steps 2-5: the whole search
+# ---------------------------------------------------------------------------
+def check_losses(got, ref, best_got, best_ref, tol=None):
+    """Losses within 1e-3 relative (or the per-alpha bound `tol`); the argmin
+    may only differ where the oracle's two best losses are that close."""
+    if tol is None:
+        np.testing.assert_allclose(got, ref, rtol=1e-3, atol=0)
+        rel = 1e-3
+    else:
+        assert np.all(np.abs(got - ref) <= tol), (got, ref, tol)
+        rel = float(np.max(tol / ref))
+    if best_got != best_ref:
+        top = np.sort(ref)[:2]
+        assert (top[1] - top[0]) / top[0] < 2 * rel, (best_got, best_ref, ref)
+
+
+UNIT_ROUNDOFF = {"fp16": 2.0 ** -11, "bf16": 2.0 ** -8, "fp32": 2.0 ** -24}
+
+
+def rounding_bound(Xn, Wn, W_hat, dtype):
+    """Worst-case loss error of the GPU arithmetic for one candidate.
+
+    Each output error e = sum_k x_k d_k is formed from d = W - W_hat rounded
+    to the layer dtype (relative error <= u) and accumulated in fp32
+    (<= K 2^-24 of sum |x d|): |e_gpu - e| <= B = (u + K 2^-24) sum_k |x_k d_k|,
+    so |loss_gpu - loss| <= mean(2 |e| B + B^2), plus fp32 rounding of e^2."""
+    X64 = Xn.astype(np.float64)
+    D = Wn.astype(np.float64) - W_hat.astype(np.float64)
+    e = X64 @ D.T
+    B = (UNIT_ROUNDOFF[dtype] * (1 + 2.0 ** -20) + Xn.shape[1] * 2.0 ** -24) * (np.abs(X64) @ np.abs(D).T)
+    return float(np.mean(2 * np.abs(e) * B + B * B) + 1e-6 * np.mean(e * e))
+
+
+SEARCH_CASES = [
+    ("fp16", 4, 128, 300, 384, 520), ("bf16", 3, 128, 129, 256, 77), ("fp32", 4, 128, 64, 512, 256),
+    ("fp16", 3, 64, 256, 256, 256), ("fp16", 4, 128, 513, 640, 300),
+    # degenerate layers: one output channel and/or one calibration token
+    ("bf16", 4, 32, 1, 96, 1), ("fp16", 3, 128, 700, 256, 1), ("bf16", 4, 128, 1, 384, 900),
+]
+
+
+@pytest.mark.parametrize("dtype,bits,group,N,K,T", SEARCH_CASES)
+@pytest.mark.parametrize("flags", [awq.AWQ_SEARCH_WEIGHT_DELTA, awq.AWQ_SEARCH_REFERENCE_OUTPUT])
+def test_search_matches_oracle(dtype, bits, group, N, K, T, flags):
+    if dtype == "bf16" and flags == awq.AWQ_SEARCH_REFERENCE_OUTPUT:
+        pytest.skip("reference-output form is not offered for bf16")
+    log_case(test="search", dtype=dtype, bits=bits, group=group, N=N, K=K, T=T, flags=flags)
+    W, X = random_layer(N + K + T, N, K, T, dtype=dtype, outlier_factor=30.0)
+    Wn, Xn = to_numpy(W), to_numpy(X)
+    alphas = oracle.alpha_grid(20)
+    ref = oracle.search(Wn, Xn, bits, group, alphas)
+    Wd, Xd = W.cuda(), X.cuda()
+    a = awq.awq_act_stats(Xd)
+    res = awq.awq_search_scales(Wd, Xd, a, bits, group, alphas, flags=flags)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(a.cpu().numpy(), ref["a"], rtol=1e-6, atol=0)
+    losses = res["losses"].cpu().numpy()
+    best = int(res["best_idx"].cpu()[0])
+    tol = None
+    if T * N < 1024:
+        # degenerate layer: too few outputs for operand rounding to average
+        # out, so the bar is the arithmetic's own worst-case bound
+        tol = np.array([max(1e-3 * ref["losses"][k], rounding_bound(
+            Xn, Wn, oracle.fake_quant(Wn, ref["s_table"][k], bits, group), dtype))
+            for k in range(len(alphas))])
+    check_losses(losses, ref["losses"], best, ref["best"], tol)
+    assert best == oracle.argmin_lowest(losses)
+    lay = res["layout"]
+    ws = res["workspace"]
+    s_tab = ws[lay["s_table_offset"]:lay["s_table_offset"] + 20 * K * 4].view(torch.float32)
+    np.testing.assert_array_equal(res["s_best"].cpu().numpy(), s_tab.view(20, K)[best].cpu().numpy())
+    # partials: their fixed-order sum is the loss
+    tiles = lay["tiles_m"] * lay["tiles_n"]
+    p0 = lay["partials_offset"]
+    parts = ws[p0:p0 + 20 * tiles * 8].view(torch.float64).view(20, tiles).cpu().numpy()
+    np.testing.assert_allclose(parts.sum(1) / (T * N), losses, rtol=1e-12)
+    if flags == awq.AWQ_SEARCH_REFERENCE_OUTPUT:
+        y0 = lay["y_ref_offset"]
+        Y = ws[y0:y0 + T * N * 4].view(torch.float32).view(T, N).cpu().numpy()
+        Yr = oracle.reference_output(Wn, Xn)
+        np.testing.assert_allclose(Y, Yr, rtol=0, atol=2e-6 * np.abs(Yr).max() + 1e-30)
+
+
+def test_search_batched_workspace_is_identical():
+    log_case(test="search_batched")
+    W, X = random_layer(5, 200, 512, 300, dtype="fp16", outlier_factor=20.0)
+    Wd, Xd = W.cuda(), X.cuda()
+    alphas = oracle.alpha_grid(20)
+    a = awq.awq_act_stats(Xd)
+    full = awq.awq_search_scales(Wd, Xd, a, 4, 128, alphas, flags=awq.AWQ_SEARCH_REFERENCE_OUTPUT)
+    lay = full["layout"]
+    small = torch.empty(lay["w_hat_offset"] + 3 * 200 * 512 * 2 + 100, dtype=torch.uint8,
+                        device="cuda")
+    part = awq.awq_search_scales(Wd, Xd, a, 4, 128, alphas, workspace=small,
+                                 flags=awq.AWQ_SEARCH_REFERENCE_OUTPUT)
+    assert part["layout"]["alpha_batch"] == 3
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(full["losses"].cpu().numpy(), part["losses"].cpu().numpy())
+    assert int(full["best_idx"].cpu()[0]) == int(part["best_idx"].cpu()[0])
+    d_full = awq.awq_search_scales(Wd, Xd, a, 4, 128, alphas)
+    lay = d_full["layout"]
+    small = torch.empty(lay["w_hat_offset"] + 7 * 200 * 512 * 2, dtype=torch.uint8, device="cuda")
+    d_part = awq.awq_search_scales(Wd, Xd, a, 4, 128, alphas, workspace=small)
+    assert d_part["layout"]["alpha_batch"] == 7
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(d_full["losses"].cpu().numpy(), d_part["losses"].cpu().numpy())
+
+
+def test_search_reference_form_rejects_bf16():
+    log_case(test="search_reference_bf16")
+    W, X = random_layer(3, 8, 128, 8, dtype="bf16")
+    Wd, Xd = W.cuda(), X.cuda()
+    a = awq.awq_act_stats(Xd)
+    with pytest.raises(awq.AwqError) as ei:
+        awq.awq_search_scales(Wd, Xd, a, 4, 128, [0.0, 0.5], flags=awq.AWQ_SEARCH_REFERENCE_OUTPUT)
+    assert ei.value.status == -2
+
+
+def test_search_custom_grid_and_ties():
+    log_case(test="search_ties")
+    W, X = random_layer(8, 64, 256, 64, dtype="fp16")
+    Wd, Xd = W.cuda(), X.cuda()
+    a = awq.awq_act_stats(Xd)
+    # duplicated alphas give exactly equal losses: the lowest index must win
+    alphas = np.array([0.3, 0.3, 0.0, 0.0], dtype=F32)
+    res = awq.awq_search_scales(Wd, Xd, a, 4, 128, alphas)
+    torch.cuda.synchronize()
+    losses = res["losses"].cpu().numpy()
+    assert losses[0] == losses[1] and losses[2] == losses[3]
+    assert int(res["best_idx"].cpu()[0]) == (0 if losses[0] <= losses[2] else 2)
+    ref = oracle.search(to_numpy(W), to_numpy(X), 4, 128, alphas)
+    np.testing.assert_allclose(losses, ref["losses"], rtol=1e-3)
