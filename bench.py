@@ -39,7 +39,25 @@ def parse():
     p.add_argument("--flags", type=int, default=0, help="0 weight-delta form, 1 reference-output form")
     p.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="only run a plain 1 GiB fp32 device copy (torch.neg into a second "
+                        "buffer) three times: the known-size reference for HBM byte counters")
     return p.parse_args()
+
+
+def calibrate_copy() -> None:
+    import torch
+
+    dev = torch.device("cuda", 0)
+    n = 1 << 28                                   # 2^28 fp32 = 1 GiB
+    x = torch.ones(n, dtype=torch.float32, device=dev)
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.neg(x, out=y)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "torch.neg fp32", "bytes_read": 4 * n,
+                      "bytes_written": 4 * n, "launches": 3}), flush=True)
 
 
 def kernel_source_hash() -> str:
@@ -87,6 +105,9 @@ def main():
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
               "(this build has no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     import numpy as np
     import torch
 

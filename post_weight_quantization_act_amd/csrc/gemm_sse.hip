@@ -21,26 +21,37 @@ namespace {
 
 // ============================================================================
 // MFMA path (fp16 / bf16)
+//
+// Workgroup tile 256 x 256, 4 waves in a 2 x 2 arrangement, each wave owns a
+// 128 x 128 block = 8 x 8 MFMA 16x16x32 accumulators (256 fp32 registers).
+// K advances 32 per stage through a ring of 4 LDS stages (32 KB each: A and B
+// tiles of 256 rows x 64 bytes).  Operand tiles go global -> LDS directly
+// (buffer_load_dwordx4 ... lds), three stages ahead of the MFMAs, so the
+// ~1000-cycle MFMA time of a stage hides three stages of load latency and no
+// VGPRs are spent on staging.  One barrier per stage.
 // ============================================================================
 constexpr int BM = 256;          // tokens per workgroup tile
 constexpr int BN = 256;          // output channels per workgroup tile
-constexpr int BK = 64;           // k per LDS stage (128 bytes per row)
+constexpr int BK = 32;           // k per LDS stage: 64 bytes per row
+constexpr int kStages = 4;
 constexpr int kThreads = 256;    // 4 waves, 2 x 2
 constexpr int WTM = BM / 2;      // wave tile 128 x 128
 constexpr int WTN = BN / 2;
 constexpr int MI = WTM / 16;     // 16x16 MFMA blocks per wave along M
 constexpr int NI = WTN / 16;
-constexpr int kChunksPerRow = BK / 8;                       // 16-byte chunks per LDS row
-constexpr int kLoadsPerThread = BM * kChunksPerRow / kThreads;  // per operand
+constexpr int kRowBytes = BK * 2;                       // 64
+constexpr int kTileBytes = BM * kRowBytes;              // 16 KB per operand per stage
+constexpr int kStageBytes = 2 * kTileBytes;             // A then B
+constexpr int kSlabRows = 64 * 16 / kRowBytes;          // rows one wave-wide DMA fills: 16
+constexpr int kDmaPerWave = BM / kSlabRows / 4;         // per operand per stage: 4
 constexpr int kGroupM = 8;       // row tiles per raster group
 
 static_assert(BM == BN, "A and B tiles share the load mapping");
+static_assert(kRowBytes == 64, "swizzle below assumes 4 chunks of 16 bytes per row");
 
-// 16-byte chunk c of LDS row r is stored at chunk c ^ (r & 7): the 16 lanes
-// that read one fragment column hit 8 distinct chunks of 8 consecutive rows.
-__device__ __forceinline__ int lds_chunk_offset(int row, int chunk) {
-  return row * kChunksPerRow + (chunk ^ (row & 7));
-}
+// 16-byte chunk c of LDS row r sits at chunk c ^ ((r >> 1) & 3): the 8 lanes
+// of a ds_read_b128 phase (8 consecutive rows, one chunk) cover all 32 banks.
+__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 3); }
 
 template <typename S>
 __device__ __forceinline__ f32x4 mfma16(i32x4 a, i32x4 b, f32x4 c);
@@ -53,6 +64,29 @@ template <>
 __device__ __forceinline__ f32x4 mfma16<__bf16>(i32x4 a, i32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Buffer resource of a raw byte range: loads at offsets >= num_bytes return 0.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t num_bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  return i32x4{(int)(uint32_t)b, (int)(uint32_t)(b >> 32), (int)num_bytes, 0x00020000};
+}
+
+// 16 bytes per lane from rsrc + voff into LDS at m0 + 16 * lane.  Issued as
+// inline asm so the compiler does not serialise the ring with a full
+// vmcnt(0) before every LDS read; the kernel waits with explicit counts.
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds_addr, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(rsrc)
+               : "memory");
+}
+
+// Wait until at most n DMA instructions of this lane are outstanding.
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 // Workgroup id -> (batch, tile_m, tile_n).  The dispatcher hands consecutive
@@ -85,8 +119,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 void gemm_mfma_kernel(const S* __restrict__ X, const S* __restrict__ B, int nb, int T, int N,
                       int K, float* __restrict__ Y, double* __restrict__ partials, int a0,
                       int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(16))) i32x4 lds_a[2][BM * kChunksPerRow];
-  __shared__ __attribute__((aligned(16))) i32x4 lds_b[2][BN * kChunksPerRow];
+  __shared__ __attribute__((aligned(1024))) char smem[kStages * kStageBytes];
   __shared__ double red[kThreads / 64];
 
   const int tid = threadIdx.x;
@@ -98,50 +131,42 @@ void gemm_mfma_kernel(const S* __restrict__ X, const S* __restrict__ B, int nb, 
   const int m0 = tile.tm * BM;
   const int n0 = tile.tn * BN;
 
-  // Buffer resources: out-of-range offsets read as zero, which pads the
-  // ragged edges of T, N and K.
   const uint32_t a_bytes = (uint32_t)((uint64_t)T * K * sizeof(S));
   const uint32_t b_bytes = (uint32_t)((uint64_t)N * K * sizeof(S));
-  const S* Bb = B + (int64_t)tile.b * N * K;
-  const __amdgpu_buffer_rsrc_t ra =
-      __builtin_amdgcn_make_buffer_rsrc((void*)X, (short)0, (int)a_bytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rb =
-      __builtin_amdgcn_make_buffer_rsrc((void*)Bb, (short)0, (int)b_bytes, 0x00020000);
+  const i32x4 ra = make_rsrc(X, a_bytes);
+  const i32x4 rb = make_rsrc(B + (int64_t)tile.b * N * K, b_bytes);
 
-  // Load mapping: chunk id = tid + kThreads*i -> (row = id / 8, chunk = id % 8).
-  uint32_t a_off[kLoadsPerThread], b_off[kLoadsPerThread];
-  int st_off[kLoadsPerThread];
+  // DMA mapping: wave w, instruction i fills slab w*4 + i (16 rows); lane l
+  // lands on row l/4, physical chunk l%4 and so fetches logical chunk
+  // swz(row, l%4) of that row.  Rows past T or N read as zero.
+  uint32_t a_off[kDmaPerWave], b_off[kDmaPerWave];
 #pragma unroll
-  for (int i = 0; i < kLoadsPerThread; ++i) {
-    const int id = tid + kThreads * i;
-    const int r = id / kChunksPerRow, c = id % kChunksPerRow;
-    st_off[i] = lds_chunk_offset(r, c);
-    const int gr = m0 + r, gn = n0 + r;
-    a_off[i] = gr < T ? (uint32_t)(((int64_t)gr * K + c * 8) * sizeof(S)) : a_bytes;
-    b_off[i] = gn < N ? (uint32_t)(((int64_t)gn * K + c * 8) * sizeof(S)) : b_bytes;
+  for (int i = 0; i < kDmaPerWave; ++i) {
+    const int row = (wave * kDmaPerWave + i) * kSlabRows + (lane >> 2);
+    const int c = swz(row, lane & 3);
+    a_off[i] = (m0 + row < T) ? (uint32_t)(((int64_t)(m0 + row) * K + c * 8) * sizeof(S)) : a_bytes;
+    b_off[i] = (n0 + row < N) ? (uint32_t)(((int64_t)(n0 + row) * K + c * 8) * sizeof(S)) : b_bytes;
   }
-  const int my_chunk = tid % kChunksPerRow;
+  const uint32_t smem_base = (uint32_t)(uintptr_t)smem;
+  auto issue = [&](int kt) {
+    const uint32_t st = smem_base + (uint32_t)((kt % kStages) * kStageBytes);
+    const uint32_t kb = (uint32_t)(kt * BK * sizeof(S));
+#pragma unroll
+    for (int i = 0; i < kDmaPerWave; ++i) {
+      const uint32_t slab = (uint32_t)((wave * kDmaPerWave + i) * 1024);
+      dma16(ra, __builtin_amdgcn_readfirstlane(st + slab),
+            a_off[i] == a_bytes ? a_bytes : a_off[i] + kb);
+      dma16(rb, __builtin_amdgcn_readfirstlane(st + kTileBytes + slab),
+            b_off[i] == b_bytes ? b_bytes : b_off[i] + kb);
+    }
+  };
 
-  i32x4 stage_a[kLoadsPerThread], stage_b[kLoadsPerThread];
-  auto gload = [&](int kt) {
-    const int k0 = kt * BK;
-    const bool k_ok = k0 + my_chunk * 8 < K;
-    const uint32_t kb = (uint32_t)(k0 * sizeof(S));
-#pragma unroll
-    for (int i = 0; i < kLoadsPerThread; ++i) {
-      const uint32_t oa = (k_ok && a_off[i] != a_bytes) ? a_off[i] + kb : a_bytes;
-      const uint32_t ob = (k_ok && b_off[i] != b_bytes) ? b_off[i] + kb : b_bytes;
-      stage_a[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, oa, 0, 0);
-      stage_b[i] = __builtin_amdgcn_raw_buffer_load_b128(rb, ob, 0, 0);
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < kLoadsPerThread; ++i) {
-      lds_a[buf][st_off[i]] = stage_a[i];
-      lds_b[buf][st_off[i]] = stage_b[i];
-    }
-  };
+  // Fragment reads: row = wave block + i*16 + lane%16, chunk lane/16; the
+  // swizzle term depends on lane%16 only, so the in-block offset is per-lane.
+  const int frow = lane & 15;
+  const uint32_t frag_off = (uint32_t)(frow * kRowBytes + 16 * swz(frow, lane >> 4));
+  const uint32_t a_frag = (uint32_t)(wm * WTM * kRowBytes) + frag_off;
+  const uint32_t b_frag = (uint32_t)(kTileBytes + wn * WTN * kRowBytes) + frag_off;
 
   f32x4 acc[MI][NI];
 #pragma unroll
@@ -149,33 +174,54 @@ void gemm_mfma_kernel(const S* __restrict__ X, const S* __restrict__ B, int nb, 
 #pragma unroll
     for (int j = 0; j < NI; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = (K + BK - 1) / BK;
-  const int frow = lane & 15;   // fragment row within a 16-row block
-  const int fk = lane >> 4;     // which 8-wide k slice of the 32-wide step
+  auto read_frags = [&](int kt, i32x4 (&fa)[MI], i32x4 (&fb)[NI]) {
+    const char* st = smem + (kt % kStages) * kStageBytes;
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+      fa[i] = *reinterpret_cast<const i32x4*>(st + a_frag + i * 16 * kRowBytes);
+#pragma unroll
+    for (int j = 0; j < NI; ++j)
+      fb[j] = *reinterpret_cast<const i32x4*>(st + b_frag + j * 16 * kRowBytes);
+  };
 
-  gload(0);
-  lstore(0);
+  // Pipeline: stage s is DMA'd into buffer s % 4 four stages before its
+  // MFMAs; its fragments are read into registers during the previous stage's
+  // MFMAs.  At the top of iteration kt every wave has finished reading buffer
+  // kt % 4 (it read stage kt's fragments in iteration kt - 1), so after the
+  // barrier that buffer can take stage kt + 4.
+  const int nk = K / BK;                      // K is a multiple of 32
+#pragma unroll
+  for (int s = 0; s < kStages; ++s)
+    if (s < nk) issue(s);
+  if (nk > 3) wait_vm<3 * 2 * kDmaPerWave>();
+  else if (nk > 2) wait_vm<2 * 2 * kDmaPerWave>();
+  else if (nk > 1) wait_vm<2 * kDmaPerWave>();
+  else wait_vm<0>();
   __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-#pragma unroll
-    for (int kk = 0; kk < BK / 32; ++kk) {
-      i32x4 fa[MI], fb[NI];
-#pragma unroll
-      for (int i = 0; i < MI; ++i)
-        fa[i] = lds_a[cur][lds_chunk_offset(wm * WTM + i * 16 + frow, kk * 4 + fk)];
-#pragma unroll
-      for (int j = 0; j < NI; ++j)
-        fb[j] = lds_b[cur][lds_chunk_offset(wn * WTN + j * 16 + frow, kk * 4 + fk)];
-#pragma unroll
-      for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int j = 0; j < NI; ++j) acc[i][j] = mfma16<S>(fa[i], fb[j], acc[i][j]);
-    }
-    if (kt + 1 < nk) lstore(cur ^ 1);
+  i32x4 fa[MI], fb[NI], ga[MI], gb[NI];
+  read_frags(0, fa, fb);
+
+  // One stage: wait for stage kt + 1, let the ring advance, read stage
+  // kt + 1's fragments into (na, nb) while the MFMAs consume (ca, cb).
+  auto step = [&](int kt, i32x4(&ca)[MI], i32x4(&cb)[NI], i32x4(&na)[MI], i32x4(&nb)[NI]) {
+    // stage kt + 1 has landed once only stages kt + 2 and kt + 3 may pend
+    if (kt + 3 < nk) wait_vm<2 * 2 * kDmaPerWave>();
+    else if (kt + 2 < nk) wait_vm<2 * kDmaPerWave>();
+    else wait_vm<0>();
     __syncthreads();
+    if (kt + kStages < nk) issue(kt + kStages);
+    if (kt + 1 < nk) read_frags(kt + 1, na, nb);
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NI; ++j) acc[i][j] = mfma16<S>(ca[i], cb[j], acc[i][j]);
+  };
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    step(kt, fa, fb, ga, gb);
+    step(kt + 1, ga, gb, fa, fb);
   }
+  if (kt < nk) step(kt, fa, fb, ga, gb);
 
   // Epilogue.  Lane l of a 16x16 block holds rows 4*(l/16) + r, column l%16.
   const int ecol = lane & 15;
@@ -196,11 +242,11 @@ void gemm_mfma_kernel(const S* __restrict__ X, const S* __restrict__ B, int nb, 
   }
   double sse = 0.0;
 #pragma unroll
-  for (int i = 0; i < MI; ++i)
+  for (int i = 0; i < MI; ++i) {
+    float part = 0.0f;
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
       const int n = n0 + wn * WTN + j * 16 + ecol;
-      float part = 0.0f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = m0 + wm * WTM + i * 16 + erow + r;
@@ -212,8 +258,9 @@ void gemm_mfma_kernel(const S* __restrict__ X, const S* __restrict__ B, int nb, 
         }
         part += e * e;
       }
-      sse += (double)part;
     }
+    sse += (double)part;
+  }
   // wave reduction in fp64, then the 4 waves in order
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) sse += __shfl_xor(sse, off);
