@@ -1,0 +1,139 @@
+"""The five synthetic layers at their full sizes, in the launch configuration
+the benchmark uses (one search call over the whole 20-point grid), checked
+against the CPU oracle where it can compute outputs one by one:
+
+* activation statistics over the whole X (1e-6 relative);
+* the fake-quantised weight differences of sampled output rows, every alpha,
+  bit-exact against the oracle fed the library's own scale table;
+* the squared-error partial sums of sampled output tiles (first, last
+  (ragged) and an interior tile) for alpha = 0, the chosen alpha and the
+  last alpha, recomputed in fp64 (1e-3 relative);
+* packed codes, steps and zero-points of sampled rows, bit-exact;
+* and the properties that hold at any size: losses are the fixed-order sums
+  of the partials, the chosen index is the lowest minimum, s_best is its row
+  of the scale table.
+The small layer (512 x 512, 256 tokens) is compared in full.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import post_weight_quantization_act_amd as awq
+from datagen import CONFIGS, make_layer, to_numpy
+
+pytestmark = pytest.mark.gpu
+
+F32 = np.float32
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    awq.library()
+    yield
+    torch.cuda.synchronize()
+
+
+def ws_view(ws, off, count, dtype):
+    nbytes = count * torch.empty((), dtype=dtype).element_size()
+    return ws[off:off + nbytes].view(dtype)
+
+
+def test_tiny_layer_full_search_matches_oracle():
+    spec = CONFIGS["tiny-512"]
+    print("case", spec.name, flush=True)
+    W, X = make_layer(spec)
+    Wn, Xn = to_numpy(W), to_numpy(X)
+    alphas = oracle.alpha_grid(spec.n_alpha)
+    ref = oracle.search(Wn, Xn, spec.bits, spec.group, alphas)
+    Wd, Xd = W.cuda(), X.cuda()
+    a = awq.awq_act_stats(Xd)
+    res = awq.awq_search_scales(Wd, Xd, a, spec.bits, spec.group, alphas)
+    codes, scales, zeros = awq.awq_quantize_pack(Wd, res["s_best"], spec.bits, spec.group)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(a.cpu().numpy(), ref["a"], rtol=1e-6)
+    losses = res["losses"].cpu().numpy()
+    np.testing.assert_allclose(losses, ref["losses"], rtol=1e-3)
+    best = int(res["best_idx"].cpu()[0])
+    if best != ref["best"]:
+        top = np.sort(ref["losses"])[:2]
+        assert (top[1] - top[0]) / top[0] < 1e-3
+    c_ref, d_ref, z_ref = oracle.quantize_pack(Wn, res["s_best"].cpu().numpy(), spec.bits,
+                                               spec.group)
+    np.testing.assert_array_equal(codes.cpu().numpy().view(np.uint32), c_ref)
+    np.testing.assert_array_equal(scales.cpu().numpy(), d_ref)
+    np.testing.assert_array_equal(zeros.cpu().numpy(), z_ref)
+
+
+@pytest.mark.parametrize("name", ["llama7b-qproj", "llama7b-upgate", "llama7b-down", "70b-mlp"])
+def test_full_size_layer(name):
+    spec = CONFIGS[name]
+    print("case", spec.name, flush=True)
+    N, K, T, bits, G = spec.N, spec.K, spec.T, spec.bits, spec.group
+    W, X = make_layer(spec)
+    Wn, Xn = to_numpy(W), to_numpy(X)
+    dt = W.dtype
+    alphas = oracle.alpha_grid(spec.n_alpha)
+    Wd, Xd = W.cuda(), X.cuda()
+    a = awq.awq_act_stats(Xd)
+    res = awq.awq_search_scales(Wd, Xd, a, bits, G, alphas)
+    codes, scales, zeros = awq.awq_quantize_pack(Wd, res["s_best"], bits, G)
+    torch.cuda.synchronize()
+    print("  gpu done", flush=True)
+
+    # statistics over the whole of X
+    a_ref = oracle.act_stats(Xn)
+    np.testing.assert_allclose(a.cpu().numpy(), a_ref, rtol=1e-6)
+
+    lay = res["layout"]
+    ws = res["workspace"]
+    n_a = spec.n_alpha
+    assert lay["alpha_batch"] == n_a
+    s_tab = ws_view(ws, lay["s_table_offset"], n_a * K, torch.float32).view(n_a, K).cpu().numpy()
+    np.testing.assert_allclose(s_tab, oracle.scale_table(a_ref, alphas), rtol=2 ** -22)
+    tm_n, tn_n = lay["tiles_m"], lay["tiles_n"]
+    parts = ws_view(ws, lay["partials_offset"], n_a * tm_n * tn_n, torch.float64)
+    parts = parts.view(n_a, tm_n, tn_n).cpu().numpy()
+    losses = res["losses"].cpu().numpy()
+    best = int(res["best_idx"].cpu()[0])
+
+    # any-size properties
+    np.testing.assert_allclose(parts.reshape(n_a, -1).sum(1) / (T * N), losses, rtol=1e-12)
+    assert best == oracle.argmin_lowest(losses)
+    np.testing.assert_array_equal(res["s_best"].cpu().numpy(), s_tab[best])
+    assert np.all(losses > 0)
+
+    # fake-quantised differences D = W - W_hat of sampled rows, every alpha
+    D = ws_view(ws, lay["w_hat_offset"], n_a * N * K, dt).view(n_a, N, K)
+    rows = np.array([0, 1, N // 2, N - 1])
+    Dg = D[:, torch.from_numpy(rows).cuda(), :].to(torch.float32).cpu().numpy()
+    Wr = Wn[rows].astype(F32)
+    for k in range(n_a):
+        ref = (Wr - oracle.fake_quant(Wr, s_tab[k], bits, G)).astype(F32)
+        exp = torch.from_numpy(ref).to(dt).to(torch.float32).numpy()
+        assert np.array_equal(Dg[k], exp), (k, np.argwhere(Dg[k] != exp)[:4])
+
+    # per-tile squared errors, recomputed in fp64
+    tiles = [(0, 0), (tm_n - 1, tn_n - 1), (tm_n // 2, tn_n // 3)]
+    tile_m, tile_n = lay["tile_m"], lay["tile_n"]
+    for k in sorted({0, best, n_a - 1}):
+        for tm, tn in tiles:
+            r0, r1 = tm * tile_m, min(T, (tm + 1) * tile_m)
+            c0, c1 = tn * tile_n, min(N, (tn + 1) * tile_n)
+            Wc = Wn[c0:c1].astype(F32)
+            Dk = Wc.astype(np.float64) - oracle.fake_quant(Wc, s_tab[k], bits, G).astype(np.float64)
+            E = Xn[r0:r1].astype(np.float64) @ Dk.T
+            sse = float(np.sum(E * E))
+            assert abs(parts[k, tm, tn] - sse) <= 1e-3 * sse, (k, tm, tn, parts[k, tm, tn], sse)
+
+    # packed codes of sampled rows
+    pr = np.concatenate([np.arange(0, 32), np.arange(N - 32, N)])
+    c_ref, d_ref, z_ref = oracle.quantize_pack(Wn[pr].astype(F32), s_tab[best], bits, G)
+    np.testing.assert_array_equal(codes.cpu().numpy()[pr].view(np.uint32), c_ref)
+    np.testing.assert_array_equal(scales.cpu().numpy()[pr], d_ref)
+    np.testing.assert_array_equal(zeros.cpu().numpy()[pr], z_ref)
+    print(f"  best alpha {alphas[best]:.2f} loss {losses[best]:.4e} (RTN {losses[0]:.4e})",
+          flush=True)
