@@ -27,7 +27,7 @@ sys.path.insert(0, str(ROOT))
 
 METRIC = "alpha-candidates/sec per layer; fake-quant GEMM TFLOP/s as % of MFMA peak"
 PEAK_TFLOPS = {"fp16": 2516.6, "bf16": 2516.6, "fp32": 157.3}
-TRAFFIC_FILE = ROOT / "profiles" / "traffic.json"
+PROFILES = ROOT / "profiles"
 
 
 def parse():
@@ -65,6 +65,20 @@ def kernel_source_hash() -> str:
     for f in sorted((ROOT / "post_weight_quantization_act_amd" / "csrc").glob("*")):
         h.update(f.read_bytes())
     return h.hexdigest()[:16]
+
+
+def measured_traffic(key: str):
+    """HBM bytes per candidate-GEMM launch from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy's readings), or
+    None when no summary covers this workload or the kernels changed since."""
+    src_hash = kernel_source_hash()
+    for f in sorted(PROFILES.glob("hbm_traffic_*.md")):
+        for line in f.read_text().splitlines():
+            if line.startswith("bench-traffic: "):
+                ent = json.loads(line[len("bench-traffic: "):])
+                if ent.get("key") == key and ent.get("source_hash") == src_hash:
+                    return ent["bytes_per_launch"]
+    return None
 
 
 def cpu_baseline(spec, W, X, budget_s: float) -> dict:
@@ -162,13 +176,7 @@ def main():
     avg_ms = ms_gemm / max(n_gemm, 1)
     achieved = flop_per_launch / (avg_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[spec.dtype]
-    traffic = None
-    src_hash = kernel_source_hash()
-    if TRAFFIC_FILE.exists():
-        tr = json.loads(TRAFFIC_FILE.read_text())
-        ent = tr.get(f"{args.config}:{args.flags}")
-        if ent and ent.get("source_hash") == src_hash:
-            traffic = ent["bytes_per_launch"]
+    traffic = measured_traffic(f"{args.config}:{args.flags}")
     esize = 4 if spec.dtype == "fp32" else 2
     detail = {
         "gemm_sse": {"launches": n_gemm, "avg_ms": avg_ms, "tflops": achieved},
