@@ -161,14 +161,25 @@ awq_status_t awq_fake_quant(const void* W, awq_dtype_t w_dtype, int64_t N, int64
  * a smaller workspace (at least one alpha's W_hat) makes the library process
  * the grid in batches of layout.alpha_batch.  After the call the workspace
  * holds the scale table, the reference output (REFERENCE_OUTPUT form), the
- * last batch's D (or W_hat) and the per-tile partial sums, at the reported
- * offsets.
+ * tiled copy of X, the last batch's D (or W_hat) and the per-tile partial
+ * sums, at the reported offsets.
+ *
+ * Tiled layout (fp16/bf16 GEMM operands): rows padded with zeros to a multiple
+ * of 256, K split in stages of 32.  Element (row, k) of a [rows, K] matrix
+ * sits at element index ((t * K/32 + s) * 256 + r) * 32 + 8 * (c ^ ((r >> 1) & 3))
+ * + k % 8 with t = row / 256, r = row % 256, s = k / 32, c = (k % 32) / 8:
+ * each 256 x 32 block is one contiguous 16 KB unit, pre-swizzled for the
+ * GEMM's LDS fragment reads.
  * ------------------------------------------------------------------------ */
 typedef struct {
   size_t total_bytes;       /* bytes the call uses */
   size_t s_table_offset;    /* fp32 [n_alpha][K] */
   size_t y_ref_offset;      /* fp32 [T][N]; SIZE_MAX in the WEIGHT_DELTA form */
-  size_t w_hat_offset;      /* dtype [alpha_batch][N][K]: D = W - W_hat, or W_hat */
+  size_t x_tiled_offset;    /* fp16/bf16: X in the tiled layout below, Tp = T rounded
+                               up to a multiple of 256 rows; SIZE_MAX for fp32 */
+  size_t w_hat_offset;      /* alpha_batch consecutive matrices D = W - W_hat (or
+                               W_hat): fp16/bf16 tiled [Np = N rounded up to 256][K],
+                               fp32 row-major [N][K] */
   size_t partials_offset;   /* fp64 [n_alpha][tiles_m][tiles_n]: sum of squared
                                errors of output tile (m, n) = rows
                                [m*tile_m, +tile_m) x cols [n*tile_n, +tile_n) */

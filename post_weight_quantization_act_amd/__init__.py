@@ -46,6 +46,7 @@ class SearchLayout(ctypes.Structure):
         ("total_bytes", ctypes.c_size_t),
         ("s_table_offset", ctypes.c_size_t),
         ("y_ref_offset", ctypes.c_size_t),
+        ("x_tiled_offset", ctypes.c_size_t),
         ("w_hat_offset", ctypes.c_size_t),
         ("partials_offset", ctypes.c_size_t),
         ("alpha_batch", ctypes.c_int32),

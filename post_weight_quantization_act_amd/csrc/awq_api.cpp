@@ -55,7 +55,8 @@ awq_status_t check_quant_args(awq_dtype_t dt, int64_t N, int64_t K, int bits, in
     return fail(AWQ_ERR_UNSUPPORTED, "group=%d must be a power of two in [32, 512]", group);
   if (K % group != 0)
     return fail(AWQ_ERR_INVALID_ARG, "K=%lld is not a multiple of group=%d", (long long)K, group);
-  if ((uint64_t)N * (uint64_t)K * (uint64_t)esize(dt) > kMaxBufferBytes || N > INT32_MAX)
+  if ((uint64_t)awq::padded_rows(N) * (uint64_t)K * (uint64_t)esize(dt) > kMaxBufferBytes ||
+      N > INT32_MAX)
     return fail(AWQ_ERR_UNSUPPORTED, "W [%lld, %lld] exceeds the 4 GiB operand limit",
                 (long long)N, (long long)K);
   return AWQ_OK;
@@ -84,8 +85,16 @@ awq_status_t compute_layout(awq_dtype_t dt, int64_t N, int64_t K, int64_t T, int
     L->y_ref_offset = off;
     off = align_up(off + (size_t)T * (size_t)N * 4);
   }
+  const bool tiled = dt != AWQ_F32;   // the MFMA path reads tiled operands
+  if (tiled) {
+    L->x_tiled_offset = off;
+    off = align_up(off + (size_t)awq::padded_rows(T) * (size_t)K * 2);
+  } else {
+    L->x_tiled_offset = SIZE_MAX;
+  }
   L->w_hat_offset = off;
-  const size_t per_alpha = align_up((size_t)N * (size_t)K * (size_t)esize(dt));
+  const size_t rows = tiled ? (size_t)awq::padded_rows(N) : (size_t)N;
+  const size_t per_alpha = align_up(rows * (size_t)K * (size_t)esize(dt));
   int batch = n_alpha;
   if (ws_bytes != 0) {
     if (ws_bytes < off + per_alpha)
@@ -209,7 +218,7 @@ awq_status_t awq_fake_quant(const void* W, awq_dtype_t w_dtype, int64_t N, int64
   if (!aligned(W, 16) || !aligned(s, 16) || !aligned(out, 16))
     return fail(AWQ_ERR_UNSUPPORTED, "W, s and out must be 16-byte aligned");
   hipError_t e = awq::launch_fake_quant(W, w_dtype, N, K, s, n_s, bits, group,
-                                        (flags & AWQ_FQ_WEIGHT_DELTA) != 0, out, stream);
+                                        (flags & AWQ_FQ_WEIGHT_DELTA) != 0, false, out, stream);
   if (e != hipSuccess) return hip_fail(e, "fake_quant launch");
   return AWQ_OK;
   AWQ_GUARD_END
@@ -250,7 +259,8 @@ awq_status_t awq_search_scales(const void* W, const void* X, awq_dtype_t dtype, 
                 "loss tolerance); use AWQ_SEARCH_WEIGHT_DELTA");
   for (int k = 0; k < n_alpha; ++k)
     if (!std::isfinite(alphas[k])) return fail(AWQ_ERR_INVALID_ARG, "alpha[%d] is not finite", k);
-  if ((uint64_t)T * (uint64_t)K * (uint64_t)esize(dtype) > kMaxBufferBytes || T > INT32_MAX)
+  if ((uint64_t)awq::padded_rows(T) * (uint64_t)K * (uint64_t)esize(dtype) > kMaxBufferBytes ||
+      T > INT32_MAX)
     return fail(AWQ_ERR_UNSUPPORTED, "X [%lld, %lld] exceeds the 4 GiB operand limit",
                 (long long)T, (long long)K);
   if (!aligned(W, 16) || !aligned(X, 16) || !aligned(a, 4) || !aligned(s_best_out, 4))
@@ -280,19 +290,29 @@ awq_status_t awq_search_scales(const void* W, const void* X, awq_dtype_t dtype, 
     e = awq::launch_scale_table(a, K, ch, s_table + (size_t)c0 * K, stream);
     if (e != hipSuccess) return hip_fail(e, "scale_table launch");
   }
-  // reference output W X, once per layer
+  // fp16/bf16: X in the GEMM's tiled layout, once per call
+  const bool tiled = dtype != AWQ_F32;
+  const void* gemm_x = X;
+  if (tiled) {
+    void* xt = ws + L.x_tiled_offset;
+    e = awq::launch_tile_rows(X, T, K, xt, stream);
+    if (e != hipSuccess) return hip_fail(e, "tile_rows launch");
+    gemm_x = xt;
+  }
+  // reference output W X, once per layer (B = the caller's row-major W)
   if (!delta) {
-    e = awq::launch_gemm(awq::Epi::kStore, dtype, X, W, 1, T, N, K, y_ref, nullptr, 0, stream);
+    e = awq::launch_gemm(awq::Epi::kStore, dtype, gemm_x, W, false, 1, T, N, K, y_ref, nullptr, 0,
+                         stream);
     if (e != hipSuccess) return hip_fail(e, "reference GEMM launch");
   }
   // steps 3-4 over the grid, alpha_batch candidates per pass
   for (int a0 = 0; a0 < n_alpha; a0 += L.alpha_batch) {
     const int nb = std::min(L.alpha_batch, n_alpha - a0);
     e = awq::launch_fake_quant(W, dtype, N, K, s_table + (size_t)a0 * K, nb, bits, group, delta,
-                               w_hat, stream);
+                               tiled, w_hat, stream);
     if (e != hipSuccess) return hip_fail(e, "fake_quant launch");
-    e = awq::launch_gemm(delta ? awq::Epi::kSseDelta : awq::Epi::kSseRef, dtype, X, w_hat, nb, T,
-                         N, K, y_ref, partials, a0, stream);
+    e = awq::launch_gemm(delta ? awq::Epi::kSseDelta : awq::Epi::kSseRef, dtype, gemm_x, w_hat,
+                         tiled, nb, T, N, K, y_ref, partials, a0, stream);
     if (e != hipSuccess) return hip_fail(e, "candidate GEMM launch");
   }
   // step 5: losses, argmin, best scales

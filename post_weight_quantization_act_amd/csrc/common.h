@@ -32,6 +32,29 @@ template <> __device__ __forceinline__ float from_f32<float>(float x) { return x
 template <> __device__ __forceinline__ _Float16 from_f32<_Float16>(float x) { return (_Float16)x; }
 template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return (__bf16)x; }
 
+// ---- tiled operand layout of the MFMA GEMM --------------------------------------
+// fp16/bf16 GEMM operands are stored tile by tile so that every global -> LDS
+// transfer of the GEMM is a contiguous 1 KB block holding whole 128-byte lines:
+// rows are padded to a multiple of 256 (padding rows are zero) and K is split in
+// stages of 32 elements.  Block (tile t, stage s) is 256 rows x 64 bytes at byte
+// ((t * (K / 32)) + s) * 16384; row r of the block occupies bytes [64 r, 64 r + 64)
+// and its 16-byte chunk c (k = 32 s + 8 c .. 32 s + 8 c + 7) sits at chunk
+// c ^ ((r >> 1) & 3), the LDS swizzle the GEMM's fragment reads expect.
+constexpr int kTileRows = 256;
+constexpr int kStageK = 32;
+constexpr int kBlockBytes = kTileRows * kStageK * 2;
+
+__host__ __device__ constexpr int64_t padded_rows(int64_t rows) {
+  return (rows + kTileRows - 1) / kTileRows * kTileRows;
+}
+__host__ __device__ __forceinline__ int swizzle_chunk(int r, int c) { return c ^ ((r >> 1) & 3); }
+// Element offset of (row, k) in the tiled layout of a [rows, K] matrix (2-byte elements).
+__host__ __device__ __forceinline__ int64_t tiled_index(int64_t row, int64_t k, int64_t K) {
+  const int64_t t = row / kTileRows, r = row % kTileRows, s = k / kStageK;
+  const int c = (int)((k % kStageK) / 8);
+  return ((t * (K / kStageK) + s) * kTileRows + r) * kStageK + 8 * swizzle_chunk((int)r, c) + k % 8;
+}
+
 // ---- launch plumbing ----------------------------------------------------------
 // Optional per-launch event timing (see awq_profile_* in the public header).
 // prof_begin returns a token (or -1 when profiling is off) to hand to prof_end.
@@ -58,9 +81,13 @@ struct AlphaChunk {
 };
 hipError_t launch_scale_table(const float* a, int64_t K, const AlphaChunk& al, float* s_out,
                               hipStream_t st);
+// out: n_s consecutive [N, K] row-major matrices, or (tiled = true, fp16/bf16
+// only) n_s consecutive tiled [padded_rows(N), K] matrices with zero padding rows.
 hipError_t launch_fake_quant(const void* W, awq_dtype_t dt, int64_t N, int64_t K,
                              const float* s, int n_s, int bits, int group, bool delta_form,
-                             void* out, hipStream_t st);
+                             bool tiled, void* out, hipStream_t st);
+// Copy a row-major [R, K] fp16/bf16 matrix into the tiled layout (zero padding rows).
+hipError_t launch_tile_rows(const void* src, int64_t R, int64_t K, void* dst, hipStream_t st);
 hipError_t launch_quantize_pack(const void* W, awq_dtype_t dt, int64_t N, int64_t K,
                                 const float* s, int bits, int group, uint32_t* codes,
                                 float* scales, uint8_t* zeros, hipStream_t st);
@@ -71,12 +98,15 @@ struct GemmTiles {
   int tile_m, tile_n;
 };
 GemmTiles gemm_tiles(awq_dtype_t dt);
-// C[t, n] = sum_k X[t, k] * B[n, k] over nb weight matrices B_b = B + b*N*K.
+// C[t, n] = sum_k X[t, k] * B_b[n, k] over nb weight matrices.
+//   fp16/bf16: X is tiled (padded_rows(T) rows); B is tiled with nb matrices of
+//   padded_rows(N) rows each (b_tiled = true) or row-major [N, K] (b_tiled =
+//   false, nb = 1).  fp32: both row-major, B_b = B + b*N*K.
 //   kStore:    Y[t, n] = C (nb must be 1)
 //   kSseRef:   partials[(a0 + b)][tm][tn] = sum over the tile of (Y - C)^2
 //   kSseDelta: partials[(a0 + b)][tm][tn] = sum over the tile of C^2
-hipError_t launch_gemm(Epi epi, awq_dtype_t dt, const void* X, const void* B, int nb,
-                       int64_t T, int64_t N, int64_t K, float* Y, double* partials,
+hipError_t launch_gemm(Epi epi, awq_dtype_t dt, const void* X, const void* B, bool b_tiled,
+                       int nb, int64_t T, int64_t N, int64_t K, float* Y, double* partials,
                        int a0, hipStream_t st);
 hipError_t launch_loss_argmin(const double* partials, int n_alpha, int64_t tiles_per_alpha,
                               double inv_count, const float* s_table, int64_t K,

@@ -22,36 +22,41 @@ namespace {
 // ============================================================================
 // MFMA path (fp16 / bf16)
 //
-// Workgroup tile 256 x 256, 4 waves in a 2 x 2 arrangement, each wave owns a
-// 128 x 128 block = 8 x 8 MFMA 16x16x32 accumulators (256 fp32 registers).
-// K advances 32 per stage through a ring of 4 LDS stages (32 KB each: A and B
-// tiles of 256 rows x 64 bytes).  Operand tiles go global -> LDS directly
-// (buffer_load_dwordx4 ... lds), three stages ahead of the MFMAs, so the
-// ~1000-cycle MFMA time of a stage hides three stages of load latency and no
-// VGPRs are spent on staging.  One barrier per stage.
+// Workgroup tile 256 tokens x 256 output channels, 8 waves in a 2 x 4
+// arrangement (two waves per SIMD), each wave owning a 128 x 64 block = 8 x 4
+// MFMA 16x16x32 accumulators (128 fp32 registers).  K advances 32 per stage
+// through a ring of 4 LDS stages (32 KB each: the A and B tiles, 256 rows x 64
+// bytes).  Operands are read in the tiled layout (see common.h), so each
+// stage of each operand is one contiguous 16 KB block: 16 wave-wide
+// global -> LDS transfers (buffer_load_dwordx4 ... lds) of 1 KB, i.e. whole
+// 128-byte lines, issued four stages ahead of the MFMAs.  The block is copied
+// verbatim, already swizzled for the fragment reads.  One barrier per stage;
+// the second wave on each SIMD keeps the matrix pipe busy while the first
+// waits at it.  The reference-output GEMM reads the caller's row-major W as
+// its B operand instead (B_TILED = false): each lane then fetches its swizzled
+// chunk of a row directly, and rows past N read as zero.
 // ============================================================================
-constexpr int BM = 256;          // tokens per workgroup tile
-constexpr int BN = 256;          // output channels per workgroup tile
-constexpr int BK = 32;           // k per LDS stage: 64 bytes per row
+constexpr int BM = kTileRows;    // tokens per workgroup tile
+constexpr int BN = kTileRows;    // output channels per workgroup tile
+constexpr int BK = kStageK;      // k per LDS stage: 64 bytes per row
 constexpr int kStages = 4;
-constexpr int kThreads = 256;    // 4 waves, 2 x 2
-constexpr int WTM = BM / 2;      // wave tile 128 x 128
-constexpr int WTN = BN / 2;
+constexpr int kWaves = 8;
+constexpr int kWavesN = 4;       // 2 x 4 waves
+constexpr int kThreads = 64 * kWaves;
+constexpr int WTM = BM / (kWaves / kWavesN);   // wave tile 128 x 64
+constexpr int WTN = BN / kWavesN;
 constexpr int MI = WTM / 16;     // 16x16 MFMA blocks per wave along M
 constexpr int NI = WTN / 16;
 constexpr int kRowBytes = BK * 2;                       // 64
 constexpr int kTileBytes = BM * kRowBytes;              // 16 KB per operand per stage
 constexpr int kStageBytes = 2 * kTileBytes;             // A then B
-constexpr int kSlabRows = 64 * 16 / kRowBytes;          // rows one wave-wide DMA fills: 16
-constexpr int kDmaPerWave = BM / kSlabRows / 4;         // per operand per stage: 4
+constexpr int kSlabRows = 64 * 16 / kRowBytes;          // rows one wave-wide transfer fills: 16
+constexpr int kDmaPerWave = BM / kSlabRows / kWaves;    // per operand per stage: 2
 constexpr int kGroupM = 8;       // row tiles per raster group
 
 static_assert(BM == BN, "A and B tiles share the load mapping");
-static_assert(kRowBytes == 64, "swizzle below assumes 4 chunks of 16 bytes per row");
-
-// 16-byte chunk c of LDS row r sits at chunk c ^ ((r >> 1) & 3): the 8 lanes
-// of a ds_read_b128 phase (8 consecutive rows, one chunk) cover all 32 banks.
-__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 3); }
+static_assert(kTileBytes == kBlockBytes, "an LDS stage tile is one block of the tiled layout");
+static_assert(kRowBytes == 64, "swizzle assumes 4 chunks of 16 bytes per row");
 
 template <typename S>
 __device__ __forceinline__ f32x4 mfma16(i32x4 a, i32x4 b, f32x4 c);
@@ -82,7 +87,7 @@ __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds_addr, uint32_t vo
                : "memory");
 }
 
-// Wait until at most n DMA instructions of this lane are outstanding.
+// Wait until at most n transfers of this lane are outstanding.
 template <int n>
 __device__ __forceinline__ void wait_vm() {
   static_assert(n >= 0 && n < 64, "vmcnt is 6 bits");
@@ -114,57 +119,68 @@ __device__ __forceinline__ TileId map_tile(int g, int total, int tiles_m, int ti
   return t;
 }
 
-template <typename S, Epi kEpi>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void gemm_mfma_kernel(const S* __restrict__ X, const S* __restrict__ B, int nb, int T, int N,
+template <typename S, Epi kEpi, bool B_TILED>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_mfma_kernel(const S* __restrict__ Xt, const S* __restrict__ B, int nb, int T, int N,
                       int K, float* __restrict__ Y, double* __restrict__ partials, int a0,
                       int tiles_m, int tiles_n) {
   __shared__ __attribute__((aligned(1024))) char smem[kStages * kStageBytes];
-  __shared__ double red[kThreads / 64];
+  __shared__ double red[kWaves];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / kWavesN, wn = wave % kWavesN;
 
   const TileId tile = map_tile(blockIdx.x, gridDim.x, tiles_m, tiles_n);
   const int m0 = tile.tm * BM;
   const int n0 = tile.tn * BN;
+  const int nk = K / BK;                      // K is a multiple of 32
 
-  const uint32_t a_bytes = (uint32_t)((uint64_t)T * K * sizeof(S));
-  const uint32_t b_bytes = (uint32_t)((uint64_t)N * K * sizeof(S));
-  const i32x4 ra = make_rsrc(X, a_bytes);
-  const i32x4 rb = make_rsrc(B + (int64_t)tile.b * N * K, b_bytes);
-
-  // DMA mapping: wave w, instruction i fills slab w*4 + i (16 rows); lane l
-  // lands on row l/4, physical chunk l%4 and so fetches logical chunk
-  // swz(row, l%4) of that row.  Rows past T or N read as zero.
-  uint32_t a_off[kDmaPerWave], b_off[kDmaPerWave];
+  // A: tiled X, block (tm, kt) at (tm * nk + kt) * 16 KB.
+  const i32x4 ra = make_rsrc(Xt, (uint32_t)((uint64_t)tiles_m * nk * kBlockBytes));
+  const uint32_t a_tile = (uint32_t)(tile.tm * nk) * kBlockBytes;
+  // B: tiled candidate matrices (block (tn, kt) of matrix b), or row-major W.
+  i32x4 rb;
+  uint32_t b_tile = 0, b_bytes = 0;
+  uint32_t b_off[kDmaPerWave];
+  if (B_TILED) {
+    rb = make_rsrc(B + (int64_t)tile.b * tiles_n * BN * K, (uint32_t)((uint64_t)tiles_n * nk * kBlockBytes));
+    b_tile = (uint32_t)(tile.tn * nk) * kBlockBytes;
+  } else {
+    b_bytes = (uint32_t)((uint64_t)N * K * sizeof(S));
+    rb = make_rsrc(B, b_bytes);
 #pragma unroll
-  for (int i = 0; i < kDmaPerWave; ++i) {
-    const int row = (wave * kDmaPerWave + i) * kSlabRows + (lane >> 2);
-    const int c = swz(row, lane & 3);
-    a_off[i] = (m0 + row < T) ? (uint32_t)(((int64_t)(m0 + row) * K + c * 8) * sizeof(S)) : a_bytes;
-    b_off[i] = (n0 + row < N) ? (uint32_t)(((int64_t)(n0 + row) * K + c * 8) * sizeof(S)) : b_bytes;
+    for (int i = 0; i < kDmaPerWave; ++i) {
+      const int row = (wave * kDmaPerWave + i) * kSlabRows + (lane >> 2);
+      const int c = swizzle_chunk(row, lane & 3);
+      b_off[i] = (n0 + row < N) ? (uint32_t)(((int64_t)(n0 + row) * K + c * 8) * sizeof(S)) : b_bytes;
+    }
   }
   const uint32_t smem_base = (uint32_t)(uintptr_t)smem;
+  // wave w, transfer i fills 1 KB slab w*2 + i of a 16 KB stage tile
   auto issue = [&](int kt) {
     const uint32_t st = smem_base + (uint32_t)((kt % kStages) * kStageBytes);
-    const uint32_t kb = (uint32_t)(kt * BK * sizeof(S));
 #pragma unroll
     for (int i = 0; i < kDmaPerWave; ++i) {
       const uint32_t slab = (uint32_t)((wave * kDmaPerWave + i) * 1024);
       dma16(ra, __builtin_amdgcn_readfirstlane(st + slab),
-            a_off[i] == a_bytes ? a_bytes : a_off[i] + kb);
-      dma16(rb, __builtin_amdgcn_readfirstlane(st + kTileBytes + slab),
-            b_off[i] == b_bytes ? b_bytes : b_off[i] + kb);
+            a_tile + (uint32_t)kt * kBlockBytes + slab + lane * 16);
+      if (B_TILED) {
+        dma16(rb, __builtin_amdgcn_readfirstlane(st + kTileBytes + slab),
+              b_tile + (uint32_t)kt * kBlockBytes + slab + lane * 16);
+      } else {
+        const uint32_t kb = (uint32_t)(kt * BK * sizeof(S));
+        dma16(rb, __builtin_amdgcn_readfirstlane(st + kTileBytes + slab),
+              b_off[i] == b_bytes ? b_bytes : b_off[i] + kb);
+      }
     }
   };
 
   // Fragment reads: row = wave block + i*16 + lane%16, chunk lane/16; the
   // swizzle term depends on lane%16 only, so the in-block offset is per-lane.
   const int frow = lane & 15;
-  const uint32_t frag_off = (uint32_t)(frow * kRowBytes + 16 * swz(frow, lane >> 4));
+  const uint32_t frag_off = (uint32_t)(frow * kRowBytes + 16 * swizzle_chunk(frow, lane >> 4));
   const uint32_t a_frag = (uint32_t)(wm * WTM * kRowBytes) + frag_off;
   const uint32_t b_frag = (uint32_t)(kTileBytes + wn * WTN * kRowBytes) + frag_off;
 
@@ -184,18 +200,18 @@ void gemm_mfma_kernel(const S* __restrict__ X, const S* __restrict__ B, int nb, 
       fb[j] = *reinterpret_cast<const i32x4*>(st + b_frag + j * 16 * kRowBytes);
   };
 
-  // Pipeline: stage s is DMA'd into buffer s % 4 four stages before its
+  // Pipeline: stage s is transferred into buffer s % 4 four stages before its
   // MFMAs; its fragments are read into registers during the previous stage's
   // MFMAs.  At the top of iteration kt every wave has finished reading buffer
   // kt % 4 (it read stage kt's fragments in iteration kt - 1), so after the
   // barrier that buffer can take stage kt + 4.
-  const int nk = K / BK;                      // K is a multiple of 32
+  constexpr int kPerStage = 2 * kDmaPerWave;  // transfers per lane per stage
 #pragma unroll
   for (int s = 0; s < kStages; ++s)
     if (s < nk) issue(s);
-  if (nk > 3) wait_vm<3 * 2 * kDmaPerWave>();
-  else if (nk > 2) wait_vm<2 * 2 * kDmaPerWave>();
-  else if (nk > 1) wait_vm<2 * kDmaPerWave>();
+  if (nk > 3) wait_vm<3 * kPerStage>();
+  else if (nk > 2) wait_vm<2 * kPerStage>();
+  else if (nk > 1) wait_vm<kPerStage>();
   else wait_vm<0>();
   __syncthreads();
   i32x4 fa[MI], fb[NI], ga[MI], gb[NI];
@@ -203,14 +219,14 @@ void gemm_mfma_kernel(const S* __restrict__ X, const S* __restrict__ B, int nb, 
 
   // One stage: wait for stage kt + 1, let the ring advance, read stage
   // kt + 1's fragments into (na, nb) while the MFMAs consume (ca, cb).
-  auto step = [&](int kt, i32x4(&ca)[MI], i32x4(&cb)[NI], i32x4(&na)[MI], i32x4(&nb)[NI]) {
+  auto step = [&](int kt, i32x4(&ca)[MI], i32x4(&cb)[NI], i32x4(&na)[MI], i32x4(&nbf)[NI]) {
     // stage kt + 1 has landed once only stages kt + 2 and kt + 3 may pend
-    if (kt + 3 < nk) wait_vm<2 * 2 * kDmaPerWave>();
-    else if (kt + 2 < nk) wait_vm<2 * kDmaPerWave>();
+    if (kt + 3 < nk) wait_vm<2 * kPerStage>();
+    else if (kt + 2 < nk) wait_vm<kPerStage>();
     else wait_vm<0>();
     __syncthreads();
     if (kt + kStages < nk) issue(kt + kStages);
-    if (kt + 1 < nk) read_frags(kt + 1, na, nb);
+    if (kt + 1 < nk) read_frags(kt + 1, na, nbf);
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -240,6 +256,8 @@ void gemm_mfma_kernel(const S* __restrict__ X, const S* __restrict__ B, int nb, 
       }
     return;
   }
+  // Padding rows of the tiled operands are zero, so in the weight-delta form
+  // every accumulator outside [T, N] is zero already.
   double sse = 0.0;
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
@@ -261,15 +279,37 @@ void gemm_mfma_kernel(const S* __restrict__ X, const S* __restrict__ B, int nb, 
     }
     sse += (double)part;
   }
-  // wave reduction in fp64, then the 4 waves in order
+  // wave reduction in fp64, then the 8 waves in order
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) sse += __shfl_xor(sse, off);
   if (lane == 0) red[wave] = sse;
   __syncthreads();
   if (tid == 0) {
-    const double s = (red[0] + red[1]) + (red[2] + red[3]);
+    double s = 0.0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) s += red[w];
     partials[((int64_t)(a0 + tile.b) * tiles_m + tile.tm) * tiles_n + tile.tn] = s;
   }
+}
+
+// Row-major [R, K] -> tiled layout, one lane per 16-byte chunk of the output
+// (coalesced writes; each group of 4 lanes reads one row's 64-byte stage slice).
+template <typename S>
+__global__ __launch_bounds__(256) void tile_rows_kernel(const S* __restrict__ src, int64_t R,
+                                                        int64_t K, int64_t chunks,
+                                                        S* __restrict__ dst) {
+  const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (q >= chunks) return;
+  const int64_t nk = K / BK;
+  const int64_t block = q / (kBlockBytes / 16);
+  const int within = (int)(q % (kBlockBytes / 16));
+  const int r = within / 4, p = within % 4;
+  const int64_t t = block / nk, s = block % nk;
+  const int64_t row = t * BM + r;
+  const int c = swizzle_chunk(r, p);   // the swizzle is an involution
+  i32x4 v = i32x4{0, 0, 0, 0};
+  if (row < R) v = *reinterpret_cast<const i32x4*>(src + row * K + s * BK + c * 8);
+  reinterpret_cast<i32x4*>(dst)[q] = v;
 }
 
 // ============================================================================
@@ -380,26 +420,38 @@ __global__ __launch_bounds__(256) void loss_argmin_kernel(const double* __restri
   for (int64_t j = threadIdx.x; j < K; j += 256) s_best[j] = src[j];
 }
 
-template <typename S, Epi kEpi>
+template <typename S, Epi kEpi, bool B_TILED>
 hipError_t launch_mfma(const void* X, const void* B, int nb, int64_t T, int64_t N, int64_t K,
                        float* Y, double* partials, int a0, hipStream_t st) {
   const int tiles_m = (int)((T + BM - 1) / BM);
   const int tiles_n = (int)((N + BN - 1) / BN);
   const int total = tiles_m * tiles_n * nb;
-  gemm_mfma_kernel<S, kEpi><<<total, kThreads, 0, st>>>(
+  gemm_mfma_kernel<S, kEpi, B_TILED><<<total, kThreads, 0, st>>>(
       static_cast<const S*>(X), static_cast<const S*>(B), nb, (int)T, (int)N, (int)K, Y, partials,
       a0, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
 template <typename S>
-hipError_t dispatch_epi(Epi epi, const void* X, const void* B, int nb, int64_t T, int64_t N,
-                        int64_t K, float* Y, double* partials, int a0, hipStream_t st) {
-  switch (epi) {
-    case Epi::kStore: return launch_mfma<S, Epi::kStore>(X, B, nb, T, N, K, Y, partials, a0, st);
-    case Epi::kSseRef: return launch_mfma<S, Epi::kSseRef>(X, B, nb, T, N, K, Y, partials, a0, st);
-    default: return launch_mfma<S, Epi::kSseDelta>(X, B, nb, T, N, K, Y, partials, a0, st);
+hipError_t dispatch_epi(Epi epi, const void* X, const void* B, bool b_tiled, int nb, int64_t T,
+                        int64_t N, int64_t K, float* Y, double* partials, int a0, hipStream_t st) {
+  if (!b_tiled) {
+    if (epi != Epi::kStore) return hipErrorInvalidValue;
+    return launch_mfma<S, Epi::kStore, false>(X, B, nb, T, N, K, Y, partials, a0, st);
   }
+  switch (epi) {
+    case Epi::kSseRef: return launch_mfma<S, Epi::kSseRef, true>(X, B, nb, T, N, K, Y, partials, a0, st);
+    case Epi::kSseDelta: return launch_mfma<S, Epi::kSseDelta, true>(X, B, nb, T, N, K, Y, partials, a0, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename S>
+hipError_t tile_rows(const void* src, int64_t R, int64_t K, void* dst, hipStream_t st) {
+  const int64_t chunks = padded_rows(R) * K * (int64_t)sizeof(S) / 16;
+  tile_rows_kernel<S><<<(unsigned)((chunks + 255) / 256), 256, 0, st>>>(
+      static_cast<const S*>(src), R, K, chunks, static_cast<S*>(dst));
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -409,8 +461,9 @@ GemmTiles gemm_tiles(awq_dtype_t dt) {
   return GemmTiles{BM, BN};
 }
 
-hipError_t launch_gemm(Epi epi, awq_dtype_t dt, const void* X, const void* B, int nb, int64_t T,
-                       int64_t N, int64_t K, float* Y, double* partials, int a0, hipStream_t st) {
+hipError_t launch_gemm(Epi epi, awq_dtype_t dt, const void* X, const void* B, bool b_tiled,
+                       int nb, int64_t T, int64_t N, int64_t K, float* Y, double* partials,
+                       int a0, hipStream_t st) {
   ProfScope p(epi == Epi::kStore ? "awq_gemm_ref_output" : "awq_gemm_sse", st);
   if (dt == AWQ_F32) {
     const int tiles_m = (int)((T + FT - 1) / FT);
@@ -420,8 +473,14 @@ hipError_t launch_gemm(Epi epi, awq_dtype_t dt, const void* X, const void* B, in
         partials, a0, tiles_m, tiles_n);
     return hipGetLastError();
   }
-  if (dt == AWQ_F16) return dispatch_epi<_Float16>(epi, X, B, nb, T, N, K, Y, partials, a0, st);
-  return dispatch_epi<__bf16>(epi, X, B, nb, T, N, K, Y, partials, a0, st);
+  if (dt == AWQ_F16)
+    return dispatch_epi<_Float16>(epi, X, B, b_tiled, nb, T, N, K, Y, partials, a0, st);
+  return dispatch_epi<__bf16>(epi, X, B, b_tiled, nb, T, N, K, Y, partials, a0, st);
+}
+
+hipError_t launch_tile_rows(const void* src, int64_t R, int64_t K, void* dst, hipStream_t st) {
+  ProfScope p("awq_tile_rows", st);
+  return tile_rows<_Float16>(src, R, K, dst, st);   // 2-byte elements: dtype-agnostic copy
 }
 
 hipError_t launch_loss_argmin(const double* partials, int n_alpha, int64_t tiles_per_alpha,

@@ -129,17 +129,18 @@ __global__ __launch_bounds__(256) void scale_table_kernel(const float* __restric
 // values per lane) and reused for every scale vector; only the 8 scales of
 // the lane's columns are fetched per vector.  A group of G channels lives in
 // G/8 consecutive lanes and is reduced with DPP.  Output k is written to
-// out + k*N*K.
+// out + k*out_rows*K, row-major or in the GEMM's tiled layout (16-byte chunks
+// land on their swizzled slot; padding rows up to a multiple of 256 get zeros).
 // ---------------------------------------------------------------------------
 constexpr int kFqThreads = 256;
 constexpr int kFqCols = 512;                  // columns per workgroup (one wave-row)
 constexpr int kFqRowSteps = 4;                // rows per wave
 constexpr int kFqRows = kFqRowSteps * (kFqThreads / 64);
 
-template <typename S, typename O, bool kDelta>
+template <typename S, typename O, bool kDelta, bool kTiled>
 __global__ __launch_bounds__(kFqThreads) void fake_quant_kernel(
     const S* __restrict__ W, int64_t N, int64_t K, const float* __restrict__ s, int n_s,
-    float qmax, int lanes, O* __restrict__ out) {
+    float qmax, int lanes, int64_t out_rows, O* __restrict__ out) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t col = (int64_t)blockIdx.x * kFqCols + lane * 8;
@@ -168,7 +169,7 @@ __global__ __launch_bounds__(kFqThreads) void fake_quant_kernel(
 #pragma unroll
       for (int i = 0; i < 8; ++i) sv[i] = 1.0f;
     }
-    O* outk = out + (int64_t)k * N * K;
+    O* outk = out + (int64_t)k * out_rows * K;
 #pragma unroll
     for (int p = 0; p < kFqRowSteps; ++p) {
       float wp[8];
@@ -193,7 +194,18 @@ __global__ __launch_bounds__(kFqThreads) void fake_quant_kernel(
         o[i] = kDelta ? (w[p][i] - what) : what;
       }
       const int64_t r = row0 + (int64_t)p * (kFqThreads / 64);
-      if (col_ok && row_ok[p]) store8(outk + r * K + col, o);
+      if (kTiled) {
+        // padding rows of the tiled layout are written as zeros
+        if (col_ok && r < out_rows) {
+          if (!row_ok[p]) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) o[i] = 0.0f;
+          }
+          store8(outk + tiled_index(r, col, K), o);
+        }
+      } else if (col_ok && row_ok[p]) {
+        store8(outk + r * K + col, o);
+      }
     }
   }
 }
@@ -269,13 +281,19 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(
 
 template <typename S, typename O, bool kDelta>
 hipError_t fq_dispatch(const void* W, int64_t N, int64_t K, const float* s, int n_s, int bits,
-                       int group, void* out, hipStream_t st) {
-  dim3 grid((unsigned)((K + kFqCols - 1) / kFqCols), (unsigned)((N + kFqRows - 1) / kFqRows));
+                       int group, bool tiled, void* out, hipStream_t st) {
+  const int64_t out_rows = tiled ? padded_rows(N) : N;
+  dim3 grid((unsigned)((K + kFqCols - 1) / kFqCols), (unsigned)((out_rows + kFqRows - 1) / kFqRows));
   const float qmax = (float)((1 << bits) - 1);
   const S* w = static_cast<const S*>(W);
   O* o = static_cast<O*>(out);
   ProfScope p("awq_fake_quant", st);
-  fake_quant_kernel<S, O, kDelta><<<grid, kFqThreads, 0, st>>>(w, N, K, s, n_s, qmax, group / 8, o);
+  if (tiled)
+    fake_quant_kernel<S, O, kDelta, true><<<grid, kFqThreads, 0, st>>>(w, N, K, s, n_s, qmax,
+                                                                       group / 8, out_rows, o);
+  else
+    fake_quant_kernel<S, O, kDelta, false><<<grid, kFqThreads, 0, st>>>(w, N, K, s, n_s, qmax,
+                                                                        group / 8, out_rows, o);
   return hipGetLastError();
 }
 
@@ -309,20 +327,22 @@ hipError_t launch_scale_table(const float* a, int64_t K, const AlphaChunk& al, f
 }
 
 hipError_t launch_fake_quant(const void* W, awq_dtype_t dt, int64_t N, int64_t K, const float* s,
-                             int n_s, int bits, int group, bool delta_form, void* out,
+                             int n_s, int bits, int group, bool delta_form, bool tiled, void* out,
                              hipStream_t st) {
   switch (dt) {
     case AWQ_F32:
-      return delta_form ? fq_dispatch<float, float, true>(W, N, K, s, n_s, bits, group, out, st)
-                        : fq_dispatch<float, float, false>(W, N, K, s, n_s, bits, group, out, st);
+      if (tiled) return hipErrorInvalidValue;
+      return delta_form
+                 ? fq_dispatch<float, float, true>(W, N, K, s, n_s, bits, group, false, out, st)
+                 : fq_dispatch<float, float, false>(W, N, K, s, n_s, bits, group, false, out, st);
     case AWQ_F16:
       return delta_form
-                 ? fq_dispatch<_Float16, _Float16, true>(W, N, K, s, n_s, bits, group, out, st)
-                 : fq_dispatch<_Float16, _Float16, false>(W, N, K, s, n_s, bits, group, out, st);
+                 ? fq_dispatch<_Float16, _Float16, true>(W, N, K, s, n_s, bits, group, tiled, out, st)
+                 : fq_dispatch<_Float16, _Float16, false>(W, N, K, s, n_s, bits, group, tiled, out, st);
     default:
       return delta_form
-                 ? fq_dispatch<__bf16, __bf16, true>(W, N, K, s, n_s, bits, group, out, st)
-                 : fq_dispatch<__bf16, __bf16, false>(W, N, K, s, n_s, bits, group, out, st);
+                 ? fq_dispatch<__bf16, __bf16, true>(W, N, K, s, n_s, bits, group, tiled, out, st)
+                 : fq_dispatch<__bf16, __bf16, false>(W, N, K, s, n_s, bits, group, tiled, out, st);
   }
 }
 

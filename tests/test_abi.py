@@ -124,10 +124,15 @@ def test_search_layout_full_and_batched():
     assert full["y_ref_offset"] != 2 ** 64 - 1
     per_alpha = N * K * 2
     assert full["total_bytes"] == full["w_hat_offset"] + n * per_alpha
-    for off in ("partials_offset", "y_ref_offset", "w_hat_offset"):
+    for off in ("partials_offset", "y_ref_offset", "x_tiled_offset", "w_hat_offset"):
         assert full[off] % 256 == 0
     assert full["y_ref_offset"] - full["partials_offset"] >= n * 16 * 16 * 8
-    assert full["w_hat_offset"] - full["y_ref_offset"] >= T * N * 4
+    assert full["x_tiled_offset"] - full["y_ref_offset"] >= T * N * 4
+    assert full["w_hat_offset"] - full["x_tiled_offset"] >= T * K * 2
+    # ragged sizes: the tiled operands are padded to 256 rows
+    rag = awq.awq_search_layout(torch.bfloat16, 300, 256, 77, 3, 0, 0)
+    assert rag["w_hat_offset"] - rag["x_tiled_offset"] >= 256 * 256 * 2
+    assert rag["total_bytes"] - rag["w_hat_offset"] == 3 * 512 * 256 * 2
     part = awq.awq_search_layout(torch.float16, N, K, T, n, awq.AWQ_SEARCH_REFERENCE_OUTPUT,
                                  full["w_hat_offset"] + 3 * per_alpha + 5)
     assert part["alpha_batch"] == 3
@@ -139,6 +144,8 @@ def test_search_layout_full_and_batched():
                               full["w_hat_offset"] + 10)
     f32 = awq.awq_search_layout(torch.float32, 100, 256, 70, 2, 0, 0)
     assert (f32["tile_m"], f32["tiles_m"], f32["tiles_n"]) == (64, 2, 2)
+    assert f32["x_tiled_offset"] == 2 ** 64 - 1
+    assert f32["total_bytes"] - f32["w_hat_offset"] == 2 * 100 * 256 * 4
 
 
 def test_act_stats_workspace_size_is_positive():

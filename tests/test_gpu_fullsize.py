@@ -42,6 +42,18 @@ def ws_view(ws, off, count, dtype):
     return ws[off:off + nbytes].view(dtype)
 
 
+def tiled_rows(flat, rows, K):
+    """Gather rows of a matrix stored in the GEMM's tiled layout (the layout
+    awq.h documents: 256-row tiles, 32-deep stages, 16-byte chunk c of row r at
+    slot c ^ ((r >> 1) & 3))."""
+    rows = torch.as_tensor(rows, dtype=torch.int64, device=flat.device)[:, None]
+    k = torch.arange(K, dtype=torch.int64, device=flat.device)[None, :]
+    t, r, s = rows // 256, rows % 256, k // 32
+    c = (k % 32) // 8
+    idx = ((t * (K // 32) + s) * 256 + r) * 32 + 8 * (c ^ ((r >> 1) & 3)) + k % 8
+    return flat[idx]
+
+
 def test_tiny_layer_full_search_matches_oracle():
     spec = CONFIGS["tiny-512"]
     print("case", spec.name, flush=True)
@@ -107,9 +119,13 @@ def test_full_size_layer(name):
     assert np.all(losses > 0)
 
     # fake-quantised differences D = W - W_hat of sampled rows, every alpha
-    D = ws_view(ws, lay["w_hat_offset"], n_a * N * K, dt).view(n_a, N, K)
+    Np = (N + 255) // 256 * 256
+    D = ws_view(ws, lay["w_hat_offset"], n_a * Np * K, dt).view(n_a, Np * K)
     rows = np.array([0, 1, N // 2, N - 1])
-    Dg = D[:, torch.from_numpy(rows).cuda(), :].to(torch.float32).cpu().numpy()
+    Dg = torch.stack([tiled_rows(D[k], rows, K) for k in range(n_a)]).to(torch.float32).cpu().numpy()
+    if Np > N:   # padding rows are zero
+        pad = torch.stack([tiled_rows(D[k], np.arange(N, Np), K) for k in (0, n_a - 1)])
+        assert int(torch.count_nonzero(pad)) == 0
     Wr = Wn[rows].astype(F32)
     for k in range(n_a):
         ref = (Wr - oracle.fake_quant(Wr, s_tab[k], bits, G)).astype(F32)

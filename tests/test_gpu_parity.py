@@ -263,7 +263,8 @@ def test_search_batched_workspace_is_identical():
     a = awq.awq_act_stats(Xd)
     full = awq.awq_search_scales(Wd, Xd, a, 4, 128, alphas, flags=awq.AWQ_SEARCH_REFERENCE_OUTPUT)
     lay = full["layout"]
-    small = torch.empty(lay["w_hat_offset"] + 3 * 200 * 512 * 2 + 100, dtype=torch.uint8,
+    per_alpha = (lay["total_bytes"] - lay["w_hat_offset"]) // 20
+    small = torch.empty(lay["w_hat_offset"] + 3 * per_alpha + 100, dtype=torch.uint8,
                         device="cuda")
     part = awq.awq_search_scales(Wd, Xd, a, 4, 128, alphas, workspace=small,
                                  flags=awq.AWQ_SEARCH_REFERENCE_OUTPUT)
@@ -273,7 +274,8 @@ def test_search_batched_workspace_is_identical():
     assert int(full["best_idx"].cpu()[0]) == int(part["best_idx"].cpu()[0])
     d_full = awq.awq_search_scales(Wd, Xd, a, 4, 128, alphas)
     lay = d_full["layout"]
-    small = torch.empty(lay["w_hat_offset"] + 7 * 200 * 512 * 2, dtype=torch.uint8, device="cuda")
+    per_alpha = (lay["total_bytes"] - lay["w_hat_offset"]) // 20
+    small = torch.empty(lay["w_hat_offset"] + 7 * per_alpha, dtype=torch.uint8, device="cuda")
     d_part = awq.awq_search_scales(Wd, Xd, a, 4, 128, alphas, workspace=small)
     assert d_part["layout"]["alpha_batch"] == 7
     torch.cuda.synchronize()
