@@ -23,18 +23,26 @@ namespace {
 // MFMA path (fp16 / bf16)
 //
 // Workgroup tile 256 tokens x 256 output channels, 8 waves in a 2 x 4
-// arrangement (two waves per SIMD), each wave owning a 128 x 64 block = 8 x 4
-// MFMA 16x16x32 accumulators (128 fp32 registers).  K advances 32 per stage
-// through a ring of 4 LDS stages (32 KB each: the A and B tiles, 256 rows x 64
-// bytes).  Operands are read in the tiled layout (see common.h), so each
-// stage of each operand is one contiguous 16 KB block: 16 wave-wide
-// global -> LDS transfers (buffer_load_dwordx4 ... lds) of 1 KB, i.e. whole
-// 128-byte lines, issued four stages ahead of the MFMAs.  The block is copied
-// verbatim, already swizzled for the fragment reads.  One barrier per stage;
-// the second wave on each SIMD keeps the matrix pipe busy while the first
-// waits at it.  The reference-output GEMM reads the caller's row-major W as
-// its B operand instead (B_TILED = false): each lane then fetches its swizzled
-// chunk of a row directly, and rows past N read as zero.
+// arrangement, each wave owning a 128 x 64 block = 8 x 4 MFMA 16x16x32
+// accumulators (128 fp32 registers).  K advances 32 per stage through a ring of
+// 4 LDS stages (32 KB each: the A and B tiles, 256 rows x 64 bytes).  Operands
+// are read in the tiled layout (see common.h), so each stage of each operand is
+// one contiguous 16 KB block: wave-wide global -> LDS transfers
+// (buffer_load_dwordx4 ... lds) of 1 KB, i.e. whole 128-byte lines, issued
+// four stages ahead of their MFMAs and copied verbatim, already swizzled for
+// the fragment reads.
+//
+// The waves run ping-pong: group 0 (waves 0-3, tile rows 0-127) and group 1
+// (waves 4-7, rows 128-255) hold one wave on each SIMD.  In the first half of
+// stage k group 0 issues its 32 MFMAs while group 1 reads stage k's fragments;
+// in the second half group 1 issues its MFMAs while group 0 issues the
+// transfers of stage k + 4 and reads stage k + 1's fragments.  A barrier
+// separates the halves, so each SIMD's matrix pipe is fed by the two waves in
+// turn and the memory work of one hides behind the MFMAs of the other.
+//
+// The reference-output GEMM reads the caller's row-major W as its B operand
+// instead (B_TILED = false): each lane then fetches its swizzled chunk of a
+// row directly, and rows past N read as zero.
 // ============================================================================
 constexpr int BM = kTileRows;    // tokens per workgroup tile
 constexpr int BN = kTileRows;    // output channels per workgroup tile
@@ -51,7 +59,7 @@ constexpr int kRowBytes = BK * 2;                       // 64
 constexpr int kTileBytes = BM * kRowBytes;              // 16 KB per operand per stage
 constexpr int kStageBytes = 2 * kTileBytes;             // A then B
 constexpr int kSlabRows = 64 * 16 / kRowBytes;          // rows one wave-wide transfer fills: 16
-constexpr int kDmaPerWave = BM / kSlabRows / kWaves;    // per operand per stage: 2
+constexpr int kDmaPerWave = BM / kSlabRows / (kWaves / 2);   // per operand per stage per group-0 wave: 4
 constexpr int kGroupM = 8;       // row tiles per raster group
 
 static_assert(BM == BN, "A and B tiles share the load mapping");
@@ -140,6 +148,10 @@ void gemm_mfma_kernel(const S* __restrict__ Xt, const S* __restrict__ B, int nb,
   // A: tiled X, block (tm, kt) at (tm * nk + kt) * 16 KB.
   const i32x4 ra = make_rsrc(Xt, (uint32_t)((uint64_t)tiles_m * nk * kBlockBytes));
   const uint32_t a_tile = (uint32_t)(tile.tm * nk) * kBlockBytes;
+  // Group 0 (waves 0-3) issues every transfer: wave gw fills 1 KB slabs
+  // gw*4 .. gw*4+3 of each 16 KB stage tile.
+  const int grp = wave >> 2;
+  const int gw = wave & 3;
   // B: tiled candidate matrices (block (tn, kt) of matrix b), or row-major W.
   i32x4 rb;
   uint32_t b_tile = 0, b_bytes = 0;
@@ -152,18 +164,17 @@ void gemm_mfma_kernel(const S* __restrict__ Xt, const S* __restrict__ B, int nb,
     rb = make_rsrc(B, b_bytes);
 #pragma unroll
     for (int i = 0; i < kDmaPerWave; ++i) {
-      const int row = (wave * kDmaPerWave + i) * kSlabRows + (lane >> 2);
+      const int row = (gw * kDmaPerWave + i) * kSlabRows + (lane >> 2);
       const int c = swizzle_chunk(row, lane & 3);
       b_off[i] = (n0 + row < N) ? (uint32_t)(((int64_t)(n0 + row) * K + c * 8) * sizeof(S)) : b_bytes;
     }
   }
   const uint32_t smem_base = (uint32_t)(uintptr_t)smem;
-  // wave w, transfer i fills 1 KB slab w*2 + i of a 16 KB stage tile
   auto issue = [&](int kt) {
     const uint32_t st = smem_base + (uint32_t)((kt % kStages) * kStageBytes);
 #pragma unroll
     for (int i = 0; i < kDmaPerWave; ++i) {
-      const uint32_t slab = (uint32_t)((wave * kDmaPerWave + i) * 1024);
+      const uint32_t slab = (uint32_t)((gw * kDmaPerWave + i) * 1024);
       dma16(ra, __builtin_amdgcn_readfirstlane(st + slab),
             a_tile + (uint32_t)kt * kBlockBytes + slab + lane * 16);
       if (B_TILED) {
@@ -200,44 +211,50 @@ void gemm_mfma_kernel(const S* __restrict__ Xt, const S* __restrict__ B, int nb,
       fb[j] = *reinterpret_cast<const i32x4*>(st + b_frag + j * 16 * kRowBytes);
   };
 
-  // Pipeline: stage s is transferred into buffer s % 4 four stages before its
-  // MFMAs; its fragments are read into registers during the previous stage's
-  // MFMAs.  At the top of iteration kt every wave has finished reading buffer
-  // kt % 4 (it read stage kt's fragments in iteration kt - 1), so after the
-  // barrier that buffer can take stage kt + 4.
-  constexpr int kPerStage = 2 * kDmaPerWave;  // transfers per lane per stage
-#pragma unroll
-  for (int s = 0; s < kStages; ++s)
-    if (s < nk) issue(s);
-  if (nk > 3) wait_vm<3 * kPerStage>();
-  else if (nk > 2) wait_vm<2 * kPerStage>();
-  else if (nk > 1) wait_vm<kPerStage>();
-  else wait_vm<0>();
-  __syncthreads();
-  i32x4 fa[MI], fb[NI], ga[MI], gb[NI];
-  read_frags(0, fa, fb);
-
-  // One stage: wait for stage kt + 1, let the ring advance, read stage
-  // kt + 1's fragments into (na, nb) while the MFMAs consume (ca, cb).
-  auto step = [&](int kt, i32x4(&ca)[MI], i32x4(&cb)[NI], i32x4(&na)[MI], i32x4(&nbf)[NI]) {
-    // stage kt + 1 has landed once only stages kt + 2 and kt + 3 may pend
-    if (kt + 3 < nk) wait_vm<2 * kPerStage>();
-    else if (kt + 2 < nk) wait_vm<kPerStage>();
-    else wait_vm<0>();
-    __syncthreads();
-    if (kt + kStages < nk) issue(kt + kStages);
-    if (kt + 1 < nk) read_frags(kt + 1, na, nbf);
+  // Pipeline.  Stage s goes into buffer s % 4; group 0 issues it in the second
+  // half of stage s - 4 (after both groups have read stage s - 4's fragments)
+  // and waits for it, before the barrier that ends the first half of stage
+  // s - 1, so both groups see it when they read its fragments.
+  auto mma = [&](i32x4 (&fa)[MI], i32x4 (&fb)[NI]) {
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int j = 0; j < NI; ++j) acc[i][j] = mfma16<S>(ca[i], cb[j], acc[i][j]);
+      for (int j = 0; j < NI; ++j) acc[i][j] = mfma16<S>(fa[i], fb[j], acc[i][j]);
   };
-  int kt = 0;
-  for (; kt + 1 < nk; kt += 2) {
-    step(kt, fa, fb, ga, gb);
-    step(kt + 1, ga, gb, fa, fb);
+  constexpr int kPerStage = 2 * kDmaPerWave;  // transfers per group-0 lane per stage
+  if (grp == 0) {
+#pragma unroll
+    for (int s = 0; s < kStages; ++s)
+      if (s < nk) issue(s);
+    if (nk > 3) wait_vm<3 * kPerStage>();
+    else if (nk > 2) wait_vm<2 * kPerStage>();
+    else if (nk > 1) wait_vm<kPerStage>();
+    else wait_vm<0>();
   }
-  if (kt < nk) step(kt, fa, fb, ga, gb);
+  __syncthreads();
+  i32x4 fa[MI], fb[NI];
+  if (grp == 0) read_frags(0, fa, fb);
+  for (int k = 0; k < nk; ++k) {
+    // first half of stage k
+    if (grp == 0) {
+      mma(fa, fb);
+      // stage k + 1 has landed once only stages k + 2 and k + 3 may pend
+      if (k + 3 < nk) wait_vm<2 * kPerStage>();
+      else if (k + 2 < nk) wait_vm<kPerStage>();
+      else wait_vm<0>();
+    } else {
+      read_frags(k, fa, fb);
+    }
+    __syncthreads();
+    // second half of stage k
+    if (grp == 1) {
+      mma(fa, fb);
+    } else {
+      if (k + kStages < nk) issue(k + kStages);
+      if (k + 1 < nk) read_frags(k + 1, fa, fb);
+    }
+    __syncthreads();
+  }
 
   // Epilogue.  Lane l of a 16x16 block holds rows 4*(l/16) + r, column l%16.
   const int ecol = lane & 15;
