@@ -8,12 +8,23 @@
 // scales' codes are saved with their per-group metadata.
 //
 // This file is compiled with -ffp-contract=off.  Every quantiser operation is
-// a single IEEE fp32 operation with round-to-nearest-even (division is the
-// correctly rounded sequence, rint is v_rndne_f32, denormals are kept), in
-// the order: w' = w*s; mx, mn over the group; delta = (mx - mn)/qmax floored
-// at 1e-10; z = clamp(rint(-mn/delta)); c = clamp(rint(w'/delta) + z);
-// W_hat = ((c - z)*delta)/s.  So codes, steps and zero-points match any other
-// IEEE evaluation of that order bit for bit.
+// a single IEEE fp32 operation with round-to-nearest-even (rint is
+// v_rndne_f32, denormals are kept), in the order: w' = w*s; mx, mn over the
+// group; delta = (mx - mn)/qmax floored at 1e-10; z = clamp(rint(-mn/delta));
+// c = clamp(rint(w'/delta) + z); W_hat = ((c - z)*delta)/s.  So codes, steps
+// and zero-points match any other IEEE evaluation of that order bit for bit.
+//
+// Every quotient is the correctly rounded one, computed from a reciprocal
+// taken once and reused: with y = RN(1/b) (a correctly rounded division),
+// q = RN(a*y) followed by two corrections q = fma(fma(-b, q, a), y, q) gives
+// exactly RN(a/b) (Markstein's theorem: after the first correction q is
+// within an ulp of a/b, so the residual a - b*q is exact and the second
+// correction rounds correctly), in 5 VALU operations instead of the ~12 of
+// the division sequence.  The theorem needs the intermediate values to stay
+// normal; the quantiser's quotients by delta always do (delta >= 1e-10, and
+// a tiny quotient only ever feeds rint), and for W_hat = deq/s a wave falls
+// back to true divisions whenever one of its scales lies outside
+// [2^-60, 2^60].
 #include "common.h"
 
 namespace awq {
@@ -61,20 +72,33 @@ __device__ __forceinline__ void group_minmax(float& mn, float& mx, int lanes) {
   }
 }
 
+// RN(a/b) from y = RN(1/b): see the file header.
+__device__ __forceinline__ float div_rn(float a, float b, float y) {
+  float q = a * y;
+  float r = fmaf(-b, q, a);
+  q = fmaf(r, y, q);
+  r = fmaf(-b, q, a);
+  return fmaf(r, y, q);
+}
+
 struct GroupQ {
-  float delta, z;
+  float delta, rdelta, z;   // step, RN(1 / step), zero-point
 };
 
-__device__ __forceinline__ GroupQ group_params(float mn, float mx, float qmax) {
+// qmax and rq = RN(1/qmax) are per-launch constants.
+__device__ __forceinline__ GroupQ group_params(float mn, float mx, float qmax, float rq) {
   GroupQ g;
-  g.delta = fmaxf((mx - mn) / qmax, kDeltaMin);
-  g.z = fminf(fmaxf(__builtin_rintf(-mn / g.delta), 0.0f), qmax);
+  g.delta = fmaxf(div_rn(mx - mn, qmax, rq), kDeltaMin);
+  g.rdelta = 1.0f / g.delta;
+  g.z = fminf(fmaxf(__builtin_rintf(div_rn(-mn, g.delta, g.rdelta)), 0.0f), qmax);
   return g;
 }
 
 __device__ __forceinline__ float code_of(float wp, const GroupQ& g, float qmax) {
-  return fminf(fmaxf(__builtin_rintf(wp / g.delta) + g.z, 0.0f), qmax);
+  return fminf(fmaxf(__builtin_rintf(div_rn(wp, g.delta, g.rdelta)) + g.z, 0.0f), qmax);
 }
+
+constexpr float kRecipSafeLo = 0x1p-60f, kRecipSafeHi = 0x1p60f;
 
 template <typename S>
 __device__ __forceinline__ void load8(const S* p, float (&v)[8]);
@@ -123,18 +147,19 @@ __global__ __launch_bounds__(256) void scale_table_kernel(const float* __restric
 // ---------------------------------------------------------------------------
 // Fake quantisation of W diag(s_k) for n_s scale vectors in one pass over W.
 //
-// A workgroup owns a tile of 16 rows x 512 columns.  Each wave covers one
+// A workgroup owns a tile of 32 rows x 512 columns.  Each wave covers one
 // 512-column row segment per step (8 consecutive columns per lane, 16-byte
-// loads), so the tile is read from HBM once into registers (4 rows x 8
+// loads), so the tile is read from HBM once into registers (8 rows x 8
 // values per lane) and reused for every scale vector; only the 8 scales of
-// the lane's columns are fetched per vector.  A group of G channels lives in
+// the lane's columns are fetched per vector, with their reciprocals shared by
+// the 8 rows.  A group of G channels lives in
 // G/8 consecutive lanes and is reduced with DPP.  Output k is written to
 // out + k*out_rows*K, row-major or in the GEMM's tiled layout (16-byte chunks
 // land on their swizzled slot; padding rows up to a multiple of 256 get zeros).
 // ---------------------------------------------------------------------------
 constexpr int kFqThreads = 256;
 constexpr int kFqCols = 512;                  // columns per workgroup (one wave-row)
-constexpr int kFqRowSteps = 4;                // rows per wave
+constexpr int kFqRowSteps = 8;                // rows per wave
 constexpr int kFqRows = kFqRowSteps * (kFqThreads / 64);
 
 template <typename S, typename O, bool kDelta, bool kTiled>
@@ -161,14 +186,22 @@ __global__ __launch_bounds__(kFqThreads) void fake_quant_kernel(
     }
   }
 
+  const float rq = 1.0f / qmax;
   for (int k = 0; k < n_s; ++k) {
-    float sv[8];
+    float sv[8], ys[8];
     if (col_ok) {
       load8(s + (int64_t)k * K + col, sv);
     } else {
 #pragma unroll
       for (int i = 0; i < 8; ++i) sv[i] = 1.0f;
     }
+    bool extreme = false;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      ys[i] = 1.0f / sv[i];
+      extreme |= !(fabsf(sv[i]) >= kRecipSafeLo && fabsf(sv[i]) <= kRecipSafeHi);
+    }
+    const bool exact_div = __builtin_amdgcn_ballot_w64(extreme) != 0;   // wave-uniform
     O* outk = out + (int64_t)k * out_rows * K;
 #pragma unroll
     for (int p = 0; p < kFqRowSteps; ++p) {
@@ -184,13 +217,13 @@ __global__ __launch_bounds__(kFqThreads) void fake_quant_kernel(
         mx = fmaxf(mx, wp[i]);
       }
       group_minmax(mn, mx, lanes);
-      const GroupQ g = group_params(mn, mx, qmax);
+      const GroupQ g = group_params(mn, mx, qmax, rq);
       float o[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float c = code_of(wp[i], g, qmax);
         const float deq = (c - g.z) * g.delta;
-        const float what = deq / sv[i];
+        const float what = exact_div ? deq / sv[i] : div_rn(deq, sv[i], ys[i]);
         o[i] = kDelta ? (w[p][i] - what) : what;
       }
       const int64_t r = row0 + (int64_t)p * (kFqThreads / 64);
@@ -253,7 +286,7 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(
     mx = fmaxf(mx, wp[i]);
   }
   group_minmax(mn, mx, lanes);
-  const GroupQ g = group_params(mn, mx, qmax);
+  const GroupQ g = group_params(mn, mx, qmax, 1.0f / qmax);
 
   // 32 codes of `bits` bits -> `bits` words; bit p of the slice is bit
   // p%32 of word p/32.
