@@ -34,11 +34,12 @@ namespace {
 //
 // The waves run ping-pong: group 0 (waves 0-3, tile rows 0-127) and group 1
 // (waves 4-7, rows 128-255) hold one wave on each SIMD.  In the first half of
-// stage k group 0 issues its 32 MFMAs while group 1 reads stage k's fragments;
-// in the second half group 1 issues its MFMAs while group 0 issues the
-// transfers of stage k + 4 and reads stage k + 1's fragments.  A barrier
-// separates the halves, so each SIMD's matrix pipe is fed by the two waves in
-// turn and the memory work of one hides behind the MFMAs of the other.
+// stage k group 0 issues its 32 MFMAs while group 1 reads stage k's fragments
+// and transfers the B tile of stage k + 3; in the second half group 1 issues
+// its MFMAs while group 0 transfers the A tile of stage k + 4 and reads stage
+// k + 1's fragments.  A barrier separates the halves, so each SIMD's matrix
+// pipe is fed by the two waves in turn and the memory work of one hides behind
+// the MFMAs of the other.
 //
 // The reference-output GEMM reads the caller's row-major W as its B operand
 // instead (B_TILED = false): each lane then fetches its swizzled chunk of a
@@ -59,7 +60,7 @@ constexpr int kRowBytes = BK * 2;                       // 64
 constexpr int kTileBytes = BM * kRowBytes;              // 16 KB per operand per stage
 constexpr int kStageBytes = 2 * kTileBytes;             // A then B
 constexpr int kSlabRows = 64 * 16 / kRowBytes;          // rows one wave-wide transfer fills: 16
-constexpr int kDmaPerWave = BM / kSlabRows / (kWaves / 2);   // per operand per stage per group-0 wave: 4
+constexpr int kDmaPerWave = BM / kSlabRows / (kWaves / 2);   // per operand per stage per wave of its group: 4
 constexpr int kGroupM = 8;       // row tiles per raster group
 
 static_assert(BM == BN, "A and B tiles share the load mapping");
@@ -148,10 +149,10 @@ void gemm_mfma_kernel(const S* __restrict__ Xt, const S* __restrict__ B, int nb,
   // A: tiled X, block (tm, kt) at (tm * nk + kt) * 16 KB.
   const i32x4 ra = make_rsrc(Xt, (uint32_t)((uint64_t)tiles_m * nk * kBlockBytes));
   const uint32_t a_tile = (uint32_t)(tile.tm * nk) * kBlockBytes;
-  // Group 0 (waves 0-3) issues every transfer: wave gw fills 1 KB slabs
-  // gw*4 .. gw*4+3 of each 16 KB stage tile.
+  // Group 0 (waves 0-3) transfers the A tiles, group 1 (waves 4-7) the B
+  // tiles: wave gw of a group fills 1 KB slabs gw*4 .. gw*4+3 of the 16 KB tile.
   const int grp = wave >> 2;
-  const int gw = wave & 3;
+  const uint32_t gw = (uint32_t)__builtin_amdgcn_readfirstlane(wave & 3);
   // B: tiled candidate matrices (block (tn, kt) of matrix b), or row-major W.
   i32x4 rb;
   uint32_t b_tile = 0, b_bytes = 0;
@@ -164,26 +165,30 @@ void gemm_mfma_kernel(const S* __restrict__ Xt, const S* __restrict__ B, int nb,
     rb = make_rsrc(B, b_bytes);
 #pragma unroll
     for (int i = 0; i < kDmaPerWave; ++i) {
-      const int row = (gw * kDmaPerWave + i) * kSlabRows + (lane >> 2);
+      const int row = ((int)gw * kDmaPerWave + i) * kSlabRows + (lane >> 2);
       const int c = swizzle_chunk(row, lane & 3);
       b_off[i] = (n0 + row < N) ? (uint32_t)(((int64_t)(n0 + row) * K + c * 8) * sizeof(S)) : b_bytes;
     }
   }
   const uint32_t smem_base = (uint32_t)(uintptr_t)smem;
-  auto issue = [&](int kt) {
+  auto issue_a = [&](int kt) {
     const uint32_t st = smem_base + (uint32_t)((kt % kStages) * kStageBytes);
 #pragma unroll
     for (int i = 0; i < kDmaPerWave; ++i) {
-      const uint32_t slab = (uint32_t)((gw * kDmaPerWave + i) * 1024);
-      dma16(ra, __builtin_amdgcn_readfirstlane(st + slab),
-            a_tile + (uint32_t)kt * kBlockBytes + slab + lane * 16);
+      const uint32_t slab = (gw * kDmaPerWave + i) * 1024u;
+      dma16(ra, st + slab, a_tile + (uint32_t)kt * kBlockBytes + slab + lane * 16);
+    }
+  };
+  auto issue_b = [&](int kt) {
+    const uint32_t st = smem_base + (uint32_t)((kt % kStages) * kStageBytes) + kTileBytes;
+#pragma unroll
+    for (int i = 0; i < kDmaPerWave; ++i) {
+      const uint32_t slab = (gw * kDmaPerWave + i) * 1024u;
       if (B_TILED) {
-        dma16(rb, __builtin_amdgcn_readfirstlane(st + kTileBytes + slab),
-              b_tile + (uint32_t)kt * kBlockBytes + slab + lane * 16);
+        dma16(rb, st + slab, b_tile + (uint32_t)kt * kBlockBytes + slab + lane * 16);
       } else {
         const uint32_t kb = (uint32_t)(kt * BK * sizeof(S));
-        dma16(rb, __builtin_amdgcn_readfirstlane(st + kTileBytes + slab),
-              b_off[i] == b_bytes ? b_bytes : b_off[i] + kb);
+        dma16(rb, st + slab, b_off[i] == b_bytes ? b_bytes : b_off[i] + kb);
       }
     }
   };
@@ -211,24 +216,38 @@ void gemm_mfma_kernel(const S* __restrict__ Xt, const S* __restrict__ B, int nb,
       fb[j] = *reinterpret_cast<const i32x4*>(st + b_frag + j * 16 * kRowBytes);
   };
 
-  // Pipeline.  Stage s goes into buffer s % 4; group 0 issues it in the second
-  // half of stage s - 4 (after both groups have read stage s - 4's fragments)
-  // and waits for it, before the barrier that ends the first half of stage
-  // s - 1, so both groups see it when they read its fragments.
+  // Pipeline.  Stage s goes into buffer s % 4: group 0 transfers its A tile in
+  // the second half of stage s - 4, group 1 its B tile in the first half of
+  // stage s - 3 (in both cases after both groups have read the fragments of
+  // the stage that buffer held).  Each group waits for its own transfers of
+  // stage s before the barrier that ends the first half of stage s - 1, so
+  // both groups see the whole stage when they read its fragments.
   auto mma = [&](i32x4 (&fa)[MI], i32x4 (&fb)[NI]) {
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int j = 0; j < NI; ++j) acc[i][j] = mfma16<S>(fa[i], fb[j], acc[i][j]);
   };
-  constexpr int kPerStage = 2 * kDmaPerWave;  // transfers per group-0 lane per stage
+  // transfers of this lane's group still allowed to pend once stage k + 1 is in
+  auto wait_next = [&](int k) {
+    if (k + 3 < nk) wait_vm<2 * kDmaPerWave>();
+    else if (k + 2 < nk) wait_vm<kDmaPerWave>();
+    else wait_vm<0>();
+  };
   if (grp == 0) {
 #pragma unroll
     for (int s = 0; s < kStages; ++s)
-      if (s < nk) issue(s);
-    if (nk > 3) wait_vm<3 * kPerStage>();
-    else if (nk > 2) wait_vm<2 * kPerStage>();
-    else if (nk > 1) wait_vm<kPerStage>();
+      if (s < nk) issue_a(s);
+    if (nk > 3) wait_vm<3 * kDmaPerWave>();
+    else if (nk > 2) wait_vm<2 * kDmaPerWave>();
+    else if (nk > 1) wait_vm<kDmaPerWave>();
+    else wait_vm<0>();
+  } else {
+#pragma unroll
+    for (int s = 0; s < kStages - 1; ++s)
+      if (s < nk) issue_b(s);
+    if (nk > 2) wait_vm<2 * kDmaPerWave>();
+    else if (nk > 1) wait_vm<kDmaPerWave>();
     else wait_vm<0>();
   }
   __syncthreads();
@@ -238,19 +257,18 @@ void gemm_mfma_kernel(const S* __restrict__ Xt, const S* __restrict__ B, int nb,
     // first half of stage k
     if (grp == 0) {
       mma(fa, fb);
-      // stage k + 1 has landed once only stages k + 2 and k + 3 may pend
-      if (k + 3 < nk) wait_vm<2 * kPerStage>();
-      else if (k + 2 < nk) wait_vm<kPerStage>();
-      else wait_vm<0>();
+      wait_next(k);
     } else {
       read_frags(k, fa, fb);
+      if (k + kStages - 1 < nk) issue_b(k + kStages - 1);
+      wait_next(k);
     }
     __syncthreads();
     // second half of stage k
     if (grp == 1) {
       mma(fa, fb);
     } else {
-      if (k + kStages < nk) issue(k + kStages);
+      if (k + kStages < nk) issue_a(k + kStages);
       if (k + 1 < nk) read_frags(k + 1, fa, fb);
     }
     __syncthreads();
