@@ -153,7 +153,9 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # timed steps: HIP events only around the candidate GEMM launches
     awq.awq_profile_reset()
+    awq.awq_profile_select("awq_gemm_sse")
     awq.awq_profile_enable(True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -163,10 +165,21 @@ def main():
     elapsed = time.perf_counter() - t0
     awq.awq_profile_enable(False)
     n_gemm, ms_gemm = awq.awq_profile_read("awq_gemm_sse")
+    awq.awq_profile_reset()
+    # untimed breakdown: events around every kernel of two more steps
+    awq.awq_profile_select("")
+    awq.awq_profile_enable(True)
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    awq.awq_profile_enable(False)
     n_fq, ms_fq = awq.awq_profile_read("awq_fake_quant")
-    n_st, ms_st = awq.awq_profile_read("awq_act_stats_partial")
+    n_st, ms_st = awq.awq_profile_read("awq_act_stats")
     n_pk, ms_pk = awq.awq_profile_read("awq_quantize_pack")
     n_ref, ms_ref = awq.awq_profile_read("awq_gemm_ref_output")
+    n_tl, ms_tl = awq.awq_profile_read("awq_tile_rows")
+    n_la, ms_la = awq.awq_profile_read("awq_loss_argmin")
+    n_sc, ms_sc = awq.awq_profile_read("awq_scale_table")
     awq.awq_profile_reset()
 
     ms_per_step = 1e3 * elapsed / args.steps
@@ -178,16 +191,22 @@ def main():
     peak = PEAK_TFLOPS[spec.dtype]
     traffic = measured_traffic(f"{args.config}:{args.flags}")
     esize = 4 if spec.dtype == "fp32" else 2
+    def avg(ms, n):
+        return ms / max(n, 1)
+
     detail = {
         "gemm_sse": {"launches": n_gemm, "avg_ms": avg_ms, "tflops": achieved},
-        "fake_quant": {"launches": n_fq, "avg_ms": ms_fq / max(n_fq, 1),
-                       "gbps": (N * K * esize * (1 + batch)) / (ms_fq / max(n_fq, 1) * 1e-3) / 1e9},
-        "act_stats": {"avg_ms": ms_st / max(n_st, 1),
-                      "gbps": (T * K * esize) / (ms_st / max(n_st, 1) * 1e-3) / 1e9},
-        "quantize_pack": {"avg_ms": ms_pk / max(n_pk, 1),
+        "fake_quant": {"avg_ms": avg(ms_fq, n_fq),
+                       "gbps": (N * K * esize + batch * N * K * esize) / (avg(ms_fq, n_fq) * 1e-3) / 1e9},
+        "act_stats": {"avg_ms": avg(ms_st, 2),
+                      "gbps": (T * K * esize) / (avg(ms_st, 2) * 1e-3) / 1e9},
+        "quantize_pack": {"avg_ms": avg(ms_pk, n_pk),
                           "gbps": (N * K * esize + N * K * spec.bits / 8 + 5 * N * K / spec.group)
-                          / (ms_pk / max(n_pk, 1) * 1e-3) / 1e9},
-        "ref_output_gemm_ms": ms_ref / max(n_ref, 1) if n_ref else None,
+                          / (avg(ms_pk, n_pk) * 1e-3) / 1e9},
+        "tile_rows_ms": avg(ms_tl, n_tl) if n_tl else None,
+        "scale_table_ms": avg(ms_sc, n_sc) if n_sc else None,
+        "loss_argmin_ms": avg(ms_la, n_la) if n_la else None,
+        "ref_output_gemm_ms": avg(ms_ref, n_ref) if n_ref else None,
     }
     out = {
         "metric": METRIC,

@@ -221,13 +221,18 @@ awq_status_t awq_quantize_pack(const void* W, awq_dtype_t w_dtype, int64_t N, in
                                hipStream_t stream);
 
 /* ------------------------------------------------------------------------ *
- * Kernel timing.  While enabled, every kernel the library launches is
- * bracketed by a pair of HIP events on its stream; awq_profile_read()
- * synchronises on them and returns, for kernels whose name starts with
- * `prefix` (NULL or "" = all), the launch count and the summed elapsed
- * milliseconds.  awq_profile_reset() drops the records.  Thread-safe.
+ * Kernel timing.  While enabled, every kernel the library launches (or, after
+ * awq_profile_select(prefix), every kernel whose name starts with prefix) is
+ * bracketed by a pair of HIP events on its stream; each event pair adds a few
+ * microseconds between launches.  awq_profile_read() synchronises on them and
+ * returns, for kernels whose name starts with `prefix` (NULL or "" = all),
+ * the launch count and the summed elapsed milliseconds.  Kernel names:
+ * awq_act_stats_partial, awq_act_stats_finish, awq_scale_table, awq_tile_rows,
+ * awq_fake_quant, awq_gemm_ref_output, awq_gemm_sse, awq_loss_argmin,
+ * awq_quantize_pack.  awq_profile_reset() drops the records.  Thread-safe.
  * ------------------------------------------------------------------------ */
 awq_status_t awq_profile_enable(int enable);
+awq_status_t awq_profile_select(const char* prefix);
 awq_status_t awq_profile_read(const char* prefix, int64_t* launches, double* total_ms);
 awq_status_t awq_profile_reset(void);
 

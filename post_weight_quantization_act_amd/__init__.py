@@ -21,7 +21,8 @@ __all__ = [
     "AWQ_FQ_WEIGHT_DELTA",
     "awq_version", "awq_act_stats", "awq_act_stats_workspace_size", "awq_scale_table",
     "awq_fake_quant", "awq_search_layout", "awq_search_scales", "awq_quantize_pack",
-    "awq_profile_enable", "awq_profile_read", "awq_profile_reset", "packed_words_per_row",
+    "awq_profile_enable", "awq_profile_select", "awq_profile_read", "awq_profile_reset",
+    "packed_words_per_row",
 ]
 
 AWQ_F32, AWQ_F16, AWQ_BF16 = 0, 1, 2
@@ -81,6 +82,7 @@ _SIGS = {
                            _P, _P, _P, _P, _SZ, _P], _I32),
     "awq_quantize_pack": ([_P, _I32, _I64, _I64, _P, _I32, _I32, _P, _P, _P, _P], _I32),
     "awq_profile_enable": ([_I32], _I32),
+    "awq_profile_select": ([ctypes.c_char_p], _I32),
     "awq_profile_read": ([ctypes.c_char_p, ctypes.POINTER(_I64), ctypes.POINTER(_D)], _I32),
     "awq_profile_reset": ([], _I32),
 }
@@ -242,6 +244,11 @@ def awq_quantize_pack(W: torch.Tensor, s: torch.Tensor, bits: int, group: int):
 
 def awq_profile_enable(enable: bool = True) -> None:
     _check(library().awq_profile_enable(1 if enable else 0))
+
+
+def awq_profile_select(prefix: str = "") -> None:
+    """Record events only around kernels whose name starts with prefix ("" = all)."""
+    _check(library().awq_profile_select(prefix.encode()))
 
 
 def awq_profile_read(prefix: str = "") -> tuple[int, float]:

@@ -9,8 +9,8 @@
 // reads rows: 16 lanes cover 256 contiguous bytes of one row and the 4 lane
 // sets of a wave read 4 rows.  Every lane accumulates its columns in fp64.
 // Pass 1 sums a fixed chunk of rows per workgroup into fp64 partials
-// [chunks, K]; pass 2 adds the chunks in index order and divides by T, so the
-// result does not depend on scheduling.
+// [chunks, K]; pass 2 adds the chunks in a fixed order (four interleaved
+// running sums) and divides by T, so the result does not depend on scheduling.
 #include "common.h"
 
 namespace awq {
@@ -115,9 +115,18 @@ __global__ __launch_bounds__(256) void act_stats_finish(const double* __restrict
                                                         float* __restrict__ a) {
   const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (j >= K) return;
-  double s = 0.0;
-  for (int64_t c = 0; c < chunks; ++c) s += part[c * K + j];
-  a[j] = (float)(s / (double)T);
+  // four interleaved running sums (chunks c = 0,4,8,.. / 1,5,9,.. / ...),
+  // added together in a fixed order: deterministic, and four loads in flight
+  double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
+  int64_t c = 0;
+  for (; c + 3 < chunks; c += 4) {
+    s0 += part[c * K + j];
+    s1 += part[(c + 1) * K + j];
+    s2 += part[(c + 2) * K + j];
+    s3 += part[(c + 3) * K + j];
+  }
+  for (; c < chunks; ++c) s0 += part[c * K + j];
+  a[j] = (float)(((s0 + s1) + (s2 + s3)) / (double)T);
 }
 
 template <typename S>

@@ -122,6 +122,7 @@ struct ProfRec {
 std::mutex g_prof_mu;
 std::vector<ProfRec> g_prof;
 std::atomic<bool> g_prof_on{false};
+std::string g_prof_prefix;   // guarded by g_prof_mu
 
 }  // namespace
 
@@ -130,6 +131,8 @@ namespace awq {
 int prof_begin(const char* kernel, hipStream_t stream) {
   if (!g_prof_on.load(std::memory_order_relaxed)) return -1;
   std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (!g_prof_prefix.empty() && std::strncmp(kernel, g_prof_prefix.c_str(), g_prof_prefix.size()) != 0)
+    return -1;
   ProfRec r;
   r.name = kernel;
   if (hipEventCreate(&r.start) != hipSuccess) return -1;
@@ -344,6 +347,14 @@ awq_status_t awq_quantize_pack(const void* W, awq_dtype_t w_dtype, int64_t N, in
 awq_status_t awq_profile_enable(int enable) {
   g_prof_on.store(enable != 0);
   return AWQ_OK;
+}
+
+awq_status_t awq_profile_select(const char* prefix) {
+  AWQ_GUARD_BEGIN
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_prefix = prefix ? prefix : "";
+  return AWQ_OK;
+  AWQ_GUARD_END
 }
 
 awq_status_t awq_profile_read(const char* prefix, int64_t* launches, double* total_ms) {

@@ -420,29 +420,29 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(Epi epi, const float* __r
 
 // ============================================================================
 // loss[k] = (sum of partials of alpha k, fixed order) / (T N); argmin (lowest
-// index on a tie); s_best = s_table[argmin].  One workgroup.
+// index on a tie); s_best = s_table[argmin].  One workgroup of 16 waves: wave w
+// reduces alphas w, w + 16, ... (each lane a strided slice of the tiles, then a
+// fixed butterfly across the wave), then one lane takes the argmin and all
+// lanes copy the winning row of the scale table.
 // ============================================================================
-__global__ __launch_bounds__(256) void loss_argmin_kernel(const double* __restrict__ partials,
-                                                          int n_alpha, int64_t tiles,
-                                                          double inv_count,
-                                                          const float* __restrict__ s_table,
-                                                          int64_t K, double* __restrict__ losses,
-                                                          int32_t* __restrict__ best,
-                                                          float* __restrict__ s_best) {
-  __shared__ double red[256];
+constexpr int kLossThreads = 1024;
+
+__global__ __launch_bounds__(kLossThreads) void loss_argmin_kernel(
+    const double* __restrict__ partials, int n_alpha, int64_t tiles, double inv_count,
+    const float* __restrict__ s_table, int64_t K, double* __restrict__ losses,
+    int32_t* __restrict__ best, float* __restrict__ s_best) {
   __shared__ int best_sh;
-  for (int k = 0; k < n_alpha; ++k) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int k = wave; k < n_alpha; k += kLossThreads / 64) {
+    const double* p = partials + (int64_t)k * tiles;
     double s = 0.0;
-    for (int64_t i = threadIdx.x; i < tiles; i += 256) s += partials[(int64_t)k * tiles + i];
-    red[threadIdx.x] = s;
-    __syncthreads();
-    for (int w = 128; w >= 1; w >>= 1) {
-      if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
-      __syncthreads();
-    }
-    if (threadIdx.x == 0) losses[k] = red[0] * inv_count;
-    __syncthreads();
+    for (int64_t i = lane; i < tiles; i += 64) s += p[i];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+    if (lane == 0) losses[k] = s * inv_count;
   }
+  __threadfence_block();
+  __syncthreads();
   if (threadIdx.x == 0) {
     int bi = 0;
     for (int k = 1; k < n_alpha; ++k)
@@ -452,7 +452,7 @@ __global__ __launch_bounds__(256) void loss_argmin_kernel(const double* __restri
   }
   __syncthreads();
   const float* src = s_table + (int64_t)best_sh * K;
-  for (int64_t j = threadIdx.x; j < K; j += 256) s_best[j] = src[j];
+  for (int64_t j = threadIdx.x; j < K; j += kLossThreads) s_best[j] = src[j];
 }
 
 template <typename S, Epi kEpi, bool B_TILED>
@@ -522,7 +522,7 @@ hipError_t launch_loss_argmin(const double* partials, int n_alpha, int64_t tiles
                               double inv_count, const float* s_table, int64_t K, double* losses,
                               int32_t* best, float* s_best, hipStream_t st) {
   ProfScope p("awq_loss_argmin", st);
-  loss_argmin_kernel<<<1, 256, 0, st>>>(partials, n_alpha, tiles_per_alpha, inv_count, s_table, K,
+  loss_argmin_kernel<<<1, kLossThreads, 0, st>>>(partials, n_alpha, tiles_per_alpha, inv_count, s_table, K,
                                         losses, best, s_best);
   return hipGetLastError();
 }

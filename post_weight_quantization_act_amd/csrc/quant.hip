@@ -139,9 +139,10 @@ __device__ __forceinline__ void store8(S* p, const float (&v)[8]) {
 __global__ __launch_bounds__(256) void scale_table_kernel(const float* __restrict__ a, int64_t K,
                                                           AlphaChunk al, float* __restrict__ s) {
   const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (j >= K) return;
+  const int k = blockIdx.y;
+  if (j >= K || k >= al.n) return;
   const double x = (double)fmaxf(a[j], kAMin);
-  for (int k = 0; k < al.n; ++k) s[(int64_t)k * K + j] = (float)pow(x, (double)al.v[k]);
+  s[(int64_t)k * K + j] = (float)pow(x, (double)al.v[k]);
 }
 
 // ---------------------------------------------------------------------------
@@ -355,7 +356,7 @@ hipError_t pack_dispatch(const void* W, int64_t N, int64_t K, const float* s, in
 hipError_t launch_scale_table(const float* a, int64_t K, const AlphaChunk& al, float* s_out,
                               hipStream_t st) {
   ProfScope p("awq_scale_table", st);
-  scale_table_kernel<<<(unsigned)((K + 255) / 256), 256, 0, st>>>(a, K, al, s_out);
+  scale_table_kernel<<<dim3((unsigned)((K + 255) / 256), (unsigned)al.n), 256, 0, st>>>(a, K, al, s_out);
   return hipGetLastError();
 }
 
