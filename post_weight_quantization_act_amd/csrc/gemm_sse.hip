@@ -41,6 +41,11 @@ namespace {
 // pipe is fed by the two waves in turn and the memory work of one hides behind
 // the MFMAs of the other.
 //
+// The kernel is persistent: one workgroup per CU walks the tiles
+// first, first + G, first + 2G, ... (G workgroups), and the ring runs on across
+// tile boundaries, so the first stages of the next tile are in flight while the
+// last stages and the epilogue of the current one execute.
+//
 // The reference-output GEMM reads the caller's row-major W as its B operand
 // instead (B_TILED = false): each lane then fetches its swizzled chunk of a
 // row directly, and rows past N read as zero.
@@ -103,17 +108,15 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Workgroup id -> (batch, tile_m, tile_n).  The dispatcher hands consecutive
-// workgroup ids to the 8 XCDs in turn; the first remap makes the ids one XCD
-// receives consecutive logical tiles (so they share operand blocks in that
-// XCD's L2), the second orders tiles in groups of kGroupM row tiles.
+// Logical tile index -> (batch, tile_m, tile_n), in groups of kGroupM row tiles
+// so that consecutive indices share X row tiles and candidate column tiles.
+// Workgroup g runs on XCD g % 8 (the dispatcher deals workgroup ids to the 8
+// XCDs in turn); the kernel gives the workgroups of one XCD consecutive
+// logical indices in every round, so they share operand blocks in its L2.
 struct TileId {
   int b, tm, tn;
 };
-__device__ __forceinline__ TileId map_tile(int g, int total, int tiles_m, int tiles_n) {
-  const int per = total / 8, rem = total % 8;
-  const int xcd = g % 8, idx = g / 8;
-  const int L = (xcd < rem) ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+__device__ __forceinline__ TileId raster(int L, int tiles_m, int tiles_n) {
   const int per_b = tiles_m * tiles_n;
   TileId t;
   t.b = L / per_b;
@@ -128,116 +131,129 @@ __device__ __forceinline__ TileId map_tile(int g, int total, int tiles_m, int ti
   return t;
 }
 
+// Workgroup barrier that the instruction scheduler may not move anything
+// across (it would otherwise hoist register-only MFMAs over it and break the
+// alternation of the two wave groups).
+__device__ __forceinline__ void sync_sched() {
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 template <typename S, Epi kEpi, bool B_TILED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_mfma_kernel(const S* __restrict__ Xt, const S* __restrict__ B, int nb, int T, int N,
-                      int K, float* __restrict__ Y, double* __restrict__ partials, int a0,
-                      int tiles_m, int tiles_n) {
+                         int K, float* __restrict__ Y, double* __restrict__ partials, int a0,
+                         int tiles_m, int tiles_n) {
   __shared__ __attribute__((aligned(1024))) char smem[kStages * kStageBytes];
   __shared__ double red[kWaves];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / kWavesN, wn = wave % kWavesN;
-
-  const TileId tile = map_tile(blockIdx.x, gridDim.x, tiles_m, tiles_n);
-  const int m0 = tile.tm * BM;
-  const int n0 = tile.tn * BN;
-  const int nk = K / BK;                      // K is a multiple of 32
-
-  // A: tiled X, block (tm, kt) at (tm * nk + kt) * 16 KB.
-  const i32x4 ra = make_rsrc(Xt, (uint32_t)((uint64_t)tiles_m * nk * kBlockBytes));
-  const uint32_t a_tile = (uint32_t)(tile.tm * nk) * kBlockBytes;
-  // Group 0 (waves 0-3) transfers the A tiles, group 1 (waves 4-7) the B
-  // tiles: wave gw of a group fills 1 KB slabs gw*4 .. gw*4+3 of the 16 KB tile.
-  const int grp = wave >> 2;
+  const int grp = __builtin_amdgcn_readfirstlane(wave >> 2);
   const uint32_t gw = (uint32_t)__builtin_amdgcn_readfirstlane(wave & 3);
-  // B: tiled candidate matrices (block (tn, kt) of matrix b), or row-major W.
-  i32x4 rb;
-  uint32_t b_tile = 0, b_bytes = 0;
-  uint32_t b_off[kDmaPerWave];
-  if (B_TILED) {
-    rb = make_rsrc(B + (int64_t)tile.b * tiles_n * BN * K, (uint32_t)((uint64_t)tiles_n * nk * kBlockBytes));
-    b_tile = (uint32_t)(tile.tn * nk) * kBlockBytes;
-  } else {
-    b_bytes = (uint32_t)((uint64_t)N * K * sizeof(S));
-    rb = make_rsrc(B, b_bytes);
-#pragma unroll
-    for (int i = 0; i < kDmaPerWave; ++i) {
-      const int row = ((int)gw * kDmaPerWave + i) * kSlabRows + (lane >> 2);
-      const int c = swizzle_chunk(row, lane & 3);
-      b_off[i] = (n0 + row < N) ? (uint32_t)(((int64_t)(n0 + row) * K + c * 8) * sizeof(S)) : b_bytes;
-    }
-  }
+  const int nk = K / BK;                        // K is a multiple of 32
+  // Tiles of this workgroup: first + r * G for r < n_rounds.  G is a multiple
+  // of 8; when nk < kStages the host launches one workgroup per tile, so the
+  // look-ahead never has to reach past the next tile.
+  const int G = gridDim.x;
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8, per_xcd = G / 8;
+  const int total = tiles_m * tiles_n * nb;
+  const int first = xcd * per_xcd + slot;
+  const int n_rounds = first < total ? (total - first + G - 1) / G : 0;
+  if (n_rounds == 0) return;
+  const int nq = n_rounds * nk;                 // stages over all tiles
+  auto tile_of = [&](int r) {
+    TileId t = raster(r * G + first, tiles_m, tiles_n);
+    t.b = __builtin_amdgcn_readfirstlane(t.b);
+    t.tm = __builtin_amdgcn_readfirstlane(t.tm);
+    t.tn = __builtin_amdgcn_readfirstlane(t.tn);
+    return t;
+  };
+  const i32x4 ra = make_rsrc(Xt, (uint32_t)((uint64_t)tiles_m * nk * kBlockBytes));
+  const uint32_t b_bytes_rm = (uint32_t)((uint64_t)N * K * sizeof(S));
   const uint32_t smem_base = (uint32_t)(uintptr_t)smem;
-  auto issue_a = [&](int kt) {
-    const uint32_t st = smem_base + (uint32_t)((kt % kStages) * kStageBytes);
+  // Operand addressing of one tile.  A candidate matrix gets its own buffer
+  // resource: all candidates of a batch together can exceed a 32-bit range.
+  struct Ops {
+    uint32_t a_base, b_base;
+    i32x4 rb;
+    int n0;
+  };
+  auto ops_of = [&](TileId t) {
+    Ops o;
+    o.a_base = (uint32_t)(t.tm * nk) * kBlockBytes;
+    o.n0 = t.tn * BN;
+    if (B_TILED) {
+      o.rb = make_rsrc(B + (int64_t)t.b * tiles_n * BN * K, (uint32_t)((uint64_t)tiles_n * nk * kBlockBytes));
+      o.b_base = (uint32_t)(t.tn * nk) * kBlockBytes;
+    } else {
+      o.rb = make_rsrc(B, b_bytes_rm);
+      o.b_base = 0;
+    }
+    return o;
+  };
+  auto issue_a = [&](const Ops& o, int kt, int buf) {
+    const uint32_t st = smem_base + (uint32_t)(buf * kStageBytes);
 #pragma unroll
     for (int i = 0; i < kDmaPerWave; ++i) {
       const uint32_t slab = (gw * kDmaPerWave + i) * 1024u;
-      dma16(ra, st + slab, a_tile + (uint32_t)kt * kBlockBytes + slab + lane * 16);
+      dma16(ra, st + slab, o.a_base + (uint32_t)kt * kBlockBytes + slab + lane * 16);
     }
   };
-  auto issue_b = [&](int kt) {
-    const uint32_t st = smem_base + (uint32_t)((kt % kStages) * kStageBytes) + kTileBytes;
+  auto issue_b = [&](const Ops& o, int kt, int buf) {
+    const uint32_t st = smem_base + (uint32_t)(buf * kStageBytes) + kTileBytes;
 #pragma unroll
     for (int i = 0; i < kDmaPerWave; ++i) {
       const uint32_t slab = (gw * kDmaPerWave + i) * 1024u;
       if (B_TILED) {
-        dma16(rb, st + slab, b_tile + (uint32_t)kt * kBlockBytes + slab + lane * 16);
+        dma16(o.rb, st + slab, o.b_base + (uint32_t)kt * kBlockBytes + slab + lane * 16);
       } else {
-        const uint32_t kb = (uint32_t)(kt * BK * sizeof(S));
-        dma16(rb, st + slab, b_off[i] == b_bytes ? b_bytes : b_off[i] + kb);
+        const int row = ((int)gw * kDmaPerWave + i) * kSlabRows + (lane >> 2);
+        const int c = swizzle_chunk(row, lane & 3);
+        const uint32_t off = (o.n0 + row < N)
+            ? (uint32_t)(((int64_t)(o.n0 + row) * K + kt * BK + c * 8) * sizeof(S)) : b_bytes_rm;
+        dma16(o.rb, st + slab, off);
       }
     }
   };
 
-  // Fragment reads: row = wave block + i*16 + lane%16, chunk lane/16; the
-  // swizzle term depends on lane%16 only, so the in-block offset is per-lane.
   const int frow = lane & 15;
   const uint32_t frag_off = (uint32_t)(frow * kRowBytes + 16 * swizzle_chunk(frow, lane >> 4));
   const uint32_t a_frag = (uint32_t)(wm * WTM * kRowBytes) + frag_off;
   const uint32_t b_frag = (uint32_t)(kTileBytes + wn * WTN * kRowBytes) + frag_off;
-
   f32x4 acc[MI][NI];
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < NI; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  auto read_frags = [&](int kt, i32x4 (&fa)[MI], i32x4 (&fb)[NI]) {
-    const char* st = smem + (kt % kStages) * kStageBytes;
+  auto read_frags = [&](int buf, i32x4 (&fa)[MI], i32x4 (&fb)[NI]) {
+    const char* st = smem + buf * kStageBytes;
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
-      fa[i] = *reinterpret_cast<const i32x4*>(st + a_frag + i * 16 * kRowBytes);
+    for (int i = 0; i < MI; ++i) fa[i] = *reinterpret_cast<const i32x4*>(st + a_frag + i * 16 * kRowBytes);
 #pragma unroll
-    for (int j = 0; j < NI; ++j)
-      fb[j] = *reinterpret_cast<const i32x4*>(st + b_frag + j * 16 * kRowBytes);
+    for (int j = 0; j < NI; ++j) fb[j] = *reinterpret_cast<const i32x4*>(st + b_frag + j * 16 * kRowBytes);
   };
-
-  // Pipeline.  Stage s goes into buffer s % 4: group 0 transfers its A tile in
-  // the second half of stage s - 4, group 1 its B tile in the first half of
-  // stage s - 3 (in both cases after both groups have read the fragments of
-  // the stage that buffer held).  Each group waits for its own transfers of
-  // stage s before the barrier that ends the first half of stage s - 1, so
-  // both groups see the whole stage when they read its fragments.
   auto mma = [&](i32x4 (&fa)[MI], i32x4 (&fb)[NI]) {
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int j = 0; j < NI; ++j) acc[i][j] = mfma16<S>(fa[i], fb[j], acc[i][j]);
   };
-  // transfers of this lane's group still allowed to pend once stage k + 1 is in
-  auto wait_next = [&](int k) {
-    if (k + 3 < nk) wait_vm<2 * kDmaPerWave>();
-    else if (k + 2 < nk) wait_vm<kDmaPerWave>();
+  // Stage q' is transferred iff q' < nq, four (A) / three (B) stages ahead;
+  // once stage q is consumed a group may leave its transfers of stages q + 2
+  // and q + 3 pending.
+  auto wait_next = [&](int q) {
+    if (q + 3 < nq) wait_vm<2 * kDmaPerWave>();
+    else if (q + 2 < nq) wait_vm<kDmaPerWave>();
     else wait_vm<0>();
   };
+  TileId cur = tile_of(0);
+  TileId nxt = n_rounds > 1 ? tile_of(1) : cur;
+  Ops oc = ops_of(cur), on = ops_of(nxt);
   if (grp == 0) {
 #pragma unroll
     for (int s = 0; s < kStages; ++s)
-      if (s < nk) issue_a(s);
+      if (s < nk) issue_a(oc, s, s);
     if (nk > 3) wait_vm<3 * kDmaPerWave>();
     else if (nk > 2) wait_vm<2 * kDmaPerWave>();
     else if (nk > 1) wait_vm<kDmaPerWave>();
@@ -245,85 +261,107 @@ void gemm_mfma_kernel(const S* __restrict__ Xt, const S* __restrict__ B, int nb,
   } else {
 #pragma unroll
     for (int s = 0; s < kStages - 1; ++s)
-      if (s < nk) issue_b(s);
+      if (s < nk) issue_b(oc, s, s);
     if (nk > 2) wait_vm<2 * kDmaPerWave>();
     else if (nk > 1) wait_vm<kDmaPerWave>();
     else wait_vm<0>();
   }
   __syncthreads();
   i32x4 fa[MI], fb[NI];
-  if (grp == 0) read_frags(0, fa, fb);
-  for (int k = 0; k < nk; ++k) {
-    // first half of stage k
-    if (grp == 0) {
-      mma(fa, fb);
-      wait_next(k);
+  const int ecol = lane & 15, erow = (lane >> 4) * 4;
+  auto epilogue = [&]() {
+    const int m0 = cur.tm * BM, n0 = cur.tn * BN;
+    if (kEpi == Epi::kStore) {
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+          const int n = n0 + wn * WTN + j * 16 + ecol;
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const int tt = m0 + wm * WTM + i * 16 + erow + rr;
+            if (tt < T && n < N) Y[(int64_t)tt * N + n] = acc[i][j][rr];
+          }
+        }
     } else {
-      read_frags(k, fa, fb);
-      if (k + kStages - 1 < nk) issue_b(k + kStages - 1);
-      wait_next(k);
+      double sse = 0.0;
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        float part = 0.0f;
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+          const int n = n0 + wn * WTN + j * 16 + ecol;
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const int tt = m0 + wm * WTM + i * 16 + erow + rr;
+            float e;
+            if (kEpi == Epi::kSseRef) e = (tt < T && n < N) ? Y[(int64_t)tt * N + n] - acc[i][j][rr] : 0.0f;
+            else e = acc[i][j][rr];
+            part += e * e;
+          }
+        }
+        sse += (double)part;
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) sse += __shfl_xor(sse, off);
+      if (lane == 0) red[wave] = sse;
+      __syncthreads();
+      if (tid == 0) {
+        double s2 = 0.0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) s2 += red[w];
+        partials[((int64_t)(a0 + cur.b) * tiles_m + cur.tm) * tiles_n + cur.tn] = s2;
+      }
     }
-    __syncthreads();
-    // second half of stage k
-    if (grp == 1) {
-      mma(fa, fb);
-    } else {
-      if (k + kStages < nk) issue_a(k + kStages);
-      if (k + 1 < nk) read_frags(k + 1, fa, fb);
-    }
-    __syncthreads();
-  }
-
-  // Epilogue.  Lane l of a 16x16 block holds rows 4*(l/16) + r, column l%16.
-  const int ecol = lane & 15;
-  const int erow = (lane >> 4) * 4;
-  if (kEpi == Epi::kStore) {
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int j = 0; j < NI; ++j) {
-        const int n = n0 + wn * WTN + j * 16 + ecol;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = m0 + wm * WTM + i * 16 + erow + r;
-          if (t < T && n < N) Y[(int64_t)t * N + n] = acc[i][j][r];
-        }
-      }
-    return;
-  }
-  // Padding rows of the tiled operands are zero, so in the weight-delta form
-  // every accumulator outside [T, N] is zero already.
-  double sse = 0.0;
-#pragma unroll
-  for (int i = 0; i < MI; ++i) {
-    float part = 0.0f;
-#pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      const int n = n0 + wn * WTN + j * 16 + ecol;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = m0 + wm * WTM + i * 16 + erow + r;
-        float e;
-        if (kEpi == Epi::kSseRef) {
-          e = (t < T && n < N) ? Y[(int64_t)t * N + n] - acc[i][j][r] : 0.0f;
-        } else {
-          e = acc[i][j][r];
-        }
-        part += e * e;
-      }
+      for (int j = 0; j < NI; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  // Tile r + 1 becomes current; its stages are already in flight.
+  auto advance = [&](int r) {
+    cur = nxt;
+    oc = on;
+    if (r + 2 < n_rounds) {
+      nxt = tile_of(r + 2);
+      on = ops_of(nxt);
     }
-    sse += (double)part;
-  }
-  // wave reduction in fp64, then the 8 waves in order
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) sse += __shfl_xor(sse, off);
-  if (lane == 0) red[wave] = sse;
-  __syncthreads();
-  if (tid == 0) {
-    double s = 0.0;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) s += red[w];
-    partials[((int64_t)(a0 + tile.b) * tiles_m + tile.tm) * tiles_n + tile.tn] = s;
+  };
+  // The two groups run separate loops (grp is wave-uniform) that meet at the
+  // same sequence of barriers: two per stage and one per tile epilogue.
+  if (grp == 0) {
+    read_frags(0, fa, fb);
+    for (int r = 0; r < n_rounds; ++r) {
+      const bool more = r + 1 < n_rounds;
+      for (int kt = 0; kt < nk; ++kt) {
+        const int q = r * nk + kt;
+        mma(fa, fb);
+        wait_next(q);
+        sync_sched();
+        if (kt + 4 < nk) issue_a(oc, kt + 4, q & 3);
+        else if (more) issue_a(on, kt + 4 - nk, q & 3);
+        read_frags((q + 1) & 3, fa, fb);   // past the last stage: unused
+        sync_sched();
+      }
+      epilogue();
+      advance(r);
+    }
+  } else {
+    for (int r = 0; r < n_rounds; ++r) {
+      const bool more = r + 1 < n_rounds;
+      for (int kt = 0; kt < nk; ++kt) {
+        const int q = r * nk + kt;
+        read_frags(q & 3, fa, fb);
+        if (kt + 3 < nk) issue_b(oc, kt + 3, (q + 3) & 3);
+        else if (more) issue_b(on, kt + 3 - nk, (q + 3) & 3);
+        wait_next(q);
+        sync_sched();
+        mma(fa, fb);
+        sync_sched();
+      }
+      epilogue();
+      advance(r);
+    }
   }
 }
 
@@ -455,13 +493,37 @@ __global__ __launch_bounds__(kLossThreads) void loss_argmin_kernel(
   for (int64_t j = threadIdx.x; j < K; j += kLossThreads) s_best[j] = src[j];
 }
 
+// Compute units of the current device rounded down to a multiple of 8 (cached
+// per device).
+int persistent_workgroups() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < 8)
+      cus = 8;
+    cached[dev] = cus / 8 * 8;
+  }
+  return cached[dev];
+}
+
 template <typename S, Epi kEpi, bool B_TILED>
 hipError_t launch_mfma(const void* X, const void* B, int nb, int64_t T, int64_t N, int64_t K,
                        float* Y, double* partials, int a0, hipStream_t st) {
   const int tiles_m = (int)((T + BM - 1) / BM);
   const int tiles_n = (int)((N + BN - 1) / BN);
   const int total = tiles_m * tiles_n * nb;
-  gemm_mfma_kernel<S, kEpi, B_TILED><<<total, kThreads, 0, st>>>(
+  // One workgroup per CU (a multiple of 8, one share per XCD), or one per tile
+  // when there are fewer tiles or the ring is deeper than a tile.
+  const int64_t per_tile = (total + 7) / 8 * 8;
+  int grid = (int)per_tile;
+  if (K / BK >= kStages) {
+    const int cus = persistent_workgroups();
+    if (cus < grid) grid = cus;
+  }
+  gemm_mfma_kernel<S, kEpi, B_TILED><<<grid, kThreads, 0, st>>>(
       static_cast<const S*>(X), static_cast<const S*>(B), nb, (int)T, (int)N, (int)K, Y, partials,
       a0, tiles_m, tiles_n);
   return hipGetLastError();
