@@ -33,8 +33,8 @@ PROFILES = ROOT / "profiles"
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=10)
-    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=30)
     p.add_argument("--config", default="llama7b-qproj")
     p.add_argument("--flags", type=int, default=0, help="0 weight-delta form, 1 reference-output form")
     p.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")

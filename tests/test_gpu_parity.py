@@ -255,6 +255,62 @@ def test_search_matches_oracle(dtype, bits, group, N, K, T, flags):
         np.testing.assert_allclose(Y, Yr, rtol=0, atol=2e-6 * np.abs(Yr).max() + 1e-30)
 
 
+# The candidate GEMM is persistent (one workgroup per CU walking several
+# 256 x 256 tiles, its LDS ring running on across tile boundaries): layers with
+# more tiles than workgroups, a ragged last round, the ring exactly one tile
+# deep (K = 128), one stage deeper (K = 160) and deeper than a tile (K = 64,
+# one workgroup per tile), plus a reference-output GEMM over two rounds.
+MULTI_ROUND_CASES = [
+    # dtype, bits, group, N, K, T, number of alphas
+    ("fp16", 4, 128, 1100, 256, 1300, 20),   # 600 candidate tiles: 3 rounds, ragged
+    ("bf16", 3, 64, 1024, 64, 1100, 20),     # 2 stages per tile, 400 tiles
+    ("fp16", 4, 32, 700, 160, 2500, 20),     # 5 stages per tile, 600 tiles
+    ("fp16", 4, 128, 4352, 128, 4100, 4),    # 4 stages per tile; 289-tile reference GEMM
+]
+
+
+@pytest.mark.parametrize("dtype,bits,group,N,K,T,n_alpha", MULTI_ROUND_CASES)
+@pytest.mark.parametrize("flags", [awq.AWQ_SEARCH_WEIGHT_DELTA, awq.AWQ_SEARCH_REFERENCE_OUTPUT])
+def test_search_multi_round(dtype, bits, group, N, K, T, n_alpha, flags):
+    if dtype == "bf16" and flags == awq.AWQ_SEARCH_REFERENCE_OUTPUT:
+        pytest.skip("reference-output form is not offered for bf16")
+    log_case(test="search_multi_round", dtype=dtype, bits=bits, group=group, N=N, K=K, T=T,
+             n_alpha=n_alpha, flags=flags)
+    W, X = random_layer(3 * N + K + T, N, K, T, dtype=dtype, outlier_factor=30.0)
+    Wn, Xn = to_numpy(W), to_numpy(X)
+    alphas = oracle.alpha_grid(20)[::20 // n_alpha]
+    ref = oracle.search(Wn, Xn, bits, group, alphas)
+    Wd, Xd = W.cuda(), X.cuda()
+    a = awq.awq_act_stats(Xd)
+    res = awq.awq_search_scales(Wd, Xd, a, bits, group, alphas, flags=flags)
+    torch.cuda.synchronize()
+    lay = res["layout"]
+    assert lay["tiles_m"] * lay["tiles_n"] * n_alpha > 256
+    losses = res["losses"].cpu().numpy()
+    best = int(res["best_idx"].cpu()[0])
+    check_losses(losses, ref["losses"], best, ref["best"])
+    assert best == oracle.argmin_lowest(losses)
+    # every tile's partial against the oracle's per-tile sum for the chosen alpha
+    ws = res["workspace"]
+    tm_n, tn_n = lay["tiles_m"], lay["tiles_n"]
+    p0 = lay["partials_offset"]
+    parts = ws[p0:p0 + n_alpha * tm_n * tn_n * 8].view(torch.float64).view(n_alpha, tm_n, tn_n)
+    parts = parts.cpu().numpy()
+    np.testing.assert_allclose(parts.reshape(n_alpha, -1).sum(1) / (T * N), losses, rtol=1e-12)
+    D = Wn.astype(np.float64) - oracle.fake_quant(Wn, ref["s_table"][best], bits, group).astype(np.float64)
+    E = Xn.astype(np.float64) @ D.T
+    for tm in range(tm_n):
+        for tn in range(tn_n):
+            blk = E[tm * 256:(tm + 1) * 256, tn * 256:(tn + 1) * 256]
+            sse = float(np.sum(blk * blk))
+            assert abs(parts[best, tm, tn] - sse) <= 1e-3 * sse, (tm, tn, parts[best, tm, tn], sse)
+    if flags == awq.AWQ_SEARCH_REFERENCE_OUTPUT:
+        y0 = lay["y_ref_offset"]
+        Y = ws[y0:y0 + T * N * 4].view(torch.float32).view(T, N).cpu().numpy()
+        Yr = oracle.reference_output(Wn, Xn)
+        np.testing.assert_allclose(Y, Yr, rtol=0, atol=2e-6 * np.abs(Yr).max() + 1e-30)
+
+
 def test_search_batched_workspace_is_identical():
     log_case(test="search_batched")
     W, X = random_layer(5, 200, 512, 300, dtype="fp16", outlier_factor=20.0)
