@@ -173,7 +173,8 @@ awq_status_t awq_fake_quant(const void* W, awq_dtype_t w_dtype, int64_t N, int64
  * ------------------------------------------------------------------------ */
 typedef struct {
   size_t total_bytes;       /* bytes the call uses */
-  size_t s_table_offset;    /* fp32 [n_alpha][K] */
+  size_t s_table_offset;    /* fp32 [n_alpha][K] scale table, followed by fp32
+                               [n_alpha][K] of its reciprocals RN(1/s) */
   size_t y_ref_offset;      /* fp32 [T][N]; SIZE_MAX in the WEIGHT_DELTA form */
   size_t x_tiled_offset;    /* fp16/bf16: X in the tiled layout below, Tp = T rounded
                                up to a multiple of 256 rows; SIZE_MAX for fp32 */

@@ -25,9 +25,10 @@ COMMON = [
 ]
 # Quantiser arithmetic must be one IEEE fp32 op per source op: no contraction
 # into FMA, correctly rounded division (the HIP default), denormals kept.
+# Inputs are finite, so min/max need not order NaNs (no canonicalising moves).
 PER_FILE = {
     "quant.hip": ["-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
-                  "-fno-gpu-flush-denormals-to-zero"],
+                  "-fno-gpu-flush-denormals-to-zero", "-fno-honor-nans"],
 }
 SOURCES = ["act_stats.hip", "quant.hip", "gemm_sse.hip", "awq_api.cpp"]
 

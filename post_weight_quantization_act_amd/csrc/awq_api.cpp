@@ -75,8 +75,8 @@ awq_status_t compute_layout(awq_dtype_t dt, int64_t N, int64_t K, int64_t T, int
   L->tiles_m = (int32_t)((T + gt.tile_m - 1) / gt.tile_m);
   L->tiles_n = (int32_t)((N + gt.tile_n - 1) / gt.tile_n);
   size_t off = 0;
-  L->s_table_offset = off;
-  off = align_up(off + (size_t)n_alpha * (size_t)K * 4);
+  L->s_table_offset = off;   // s [n_alpha][K], then RN(1/s) [n_alpha][K]
+  off = align_up(off + 2 * (size_t)n_alpha * (size_t)K * 4);
   L->partials_offset = off;
   off = align_up(off + (size_t)n_alpha * (size_t)L->tiles_m * (size_t)L->tiles_n * 8);
   if (delta) {
@@ -200,7 +200,7 @@ awq_status_t awq_scale_table(const float* a, int64_t K, const float* alphas, int
     awq::AlphaChunk ch;
     ch.n = std::min(64, n_alpha - c0);
     for (int i = 0; i < ch.n; ++i) ch.v[i] = alphas[c0 + i];
-    hipError_t e = awq::launch_scale_table(a, K, ch, s_out + (size_t)c0 * K, stream);
+    hipError_t e = awq::launch_scale_table(a, K, ch, s_out + (size_t)c0 * K, nullptr, stream);
     if (e != hipSuccess) return hip_fail(e, "scale_table launch");
   }
   return AWQ_OK;
@@ -220,7 +220,7 @@ awq_status_t awq_fake_quant(const void* W, awq_dtype_t w_dtype, int64_t N, int64
     return fail(AWQ_ERR_UNSUPPORTED, "out_dtype must equal w_dtype");
   if (!aligned(W, 16) || !aligned(s, 16) || !aligned(out, 16))
     return fail(AWQ_ERR_UNSUPPORTED, "W, s and out must be 16-byte aligned");
-  hipError_t e = awq::launch_fake_quant(W, w_dtype, N, K, s, n_s, bits, group,
+  hipError_t e = awq::launch_fake_quant(W, w_dtype, N, K, s, nullptr, n_s, bits, group,
                                         (flags & AWQ_FQ_WEIGHT_DELTA) != 0, false, out, stream);
   if (e != hipSuccess) return hip_fail(e, "fake_quant launch");
   return AWQ_OK;
@@ -279,6 +279,7 @@ awq_status_t awq_search_scales(const void* W, const void* X, awq_dtype_t dtype, 
 
   char* ws = static_cast<char*>(workspace);
   float* s_table = reinterpret_cast<float*>(ws + L.s_table_offset);
+  float* rs_table = s_table + (size_t)n_alpha * K;
   double* partials = reinterpret_cast<double*>(ws + L.partials_offset);
   const bool delta = (flags & AWQ_SEARCH_REFERENCE_OUTPUT) == 0;
   float* y_ref = delta ? nullptr : reinterpret_cast<float*>(ws + L.y_ref_offset);
@@ -290,7 +291,8 @@ awq_status_t awq_search_scales(const void* W, const void* X, awq_dtype_t dtype, 
     awq::AlphaChunk ch;
     ch.n = std::min(64, n_alpha - c0);
     for (int i = 0; i < ch.n; ++i) ch.v[i] = alphas[c0 + i];
-    e = awq::launch_scale_table(a, K, ch, s_table + (size_t)c0 * K, stream);
+    e = awq::launch_scale_table(a, K, ch, s_table + (size_t)c0 * K, rs_table + (size_t)c0 * K,
+                                stream);
     if (e != hipSuccess) return hip_fail(e, "scale_table launch");
   }
   // fp16/bf16: X in the GEMM's tiled layout, once per call
@@ -311,8 +313,8 @@ awq_status_t awq_search_scales(const void* W, const void* X, awq_dtype_t dtype, 
   // steps 3-4 over the grid, alpha_batch candidates per pass
   for (int a0 = 0; a0 < n_alpha; a0 += L.alpha_batch) {
     const int nb = std::min(L.alpha_batch, n_alpha - a0);
-    e = awq::launch_fake_quant(W, dtype, N, K, s_table + (size_t)a0 * K, nb, bits, group, delta,
-                               tiled, w_hat, stream);
+    e = awq::launch_fake_quant(W, dtype, N, K, s_table + (size_t)a0 * K, rs_table + (size_t)a0 * K,
+                               nb, bits, group, delta, tiled, w_hat, stream);
     if (e != hipSuccess) return hip_fail(e, "fake_quant launch");
     e = awq::launch_gemm(delta ? awq::Epi::kSseDelta : awq::Epi::kSseRef, dtype, gemm_x, w_hat,
                          tiled, nb, T, N, K, y_ref, partials, a0, stream);

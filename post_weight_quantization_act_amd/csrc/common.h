@@ -79,13 +79,15 @@ struct AlphaChunk {
   int n;
   float v[64];
 };
+// s_out [al.n, K]; rs_out (may be null) [al.n, K] = RN(1 / s).
 hipError_t launch_scale_table(const float* a, int64_t K, const AlphaChunk& al, float* s_out,
-                              hipStream_t st);
-// out: n_s consecutive [N, K] row-major matrices, or (tiled = true, fp16/bf16
-// only) n_s consecutive tiled [padded_rows(N), K] matrices with zero padding rows.
+                              float* rs_out, hipStream_t st);
+// s [n_s, K]; rs (may be null) its elementwise RN(1 / s).  out: n_s consecutive
+// [N, K] row-major matrices, or (tiled = true, fp16/bf16 only) n_s consecutive
+// tiled [padded_rows(N), K] matrices with zero padding rows.
 hipError_t launch_fake_quant(const void* W, awq_dtype_t dt, int64_t N, int64_t K,
-                             const float* s, int n_s, int bits, int group, bool delta_form,
-                             bool tiled, void* out, hipStream_t st);
+                             const float* s, const float* rs, int n_s, int bits, int group,
+                             bool delta_form, bool tiled, void* out, hipStream_t st);
 // Copy a row-major [R, K] fp16/bf16 matrix into the tiled layout (zero padding rows).
 hipError_t launch_tile_rows(const void* src, int64_t R, int64_t K, void* dst, hipStream_t st);
 hipError_t launch_quantize_pack(const void* W, awq_dtype_t dt, int64_t N, int64_t K,

@@ -7,7 +7,9 @@
 // per input channel, quantised group-wise and dequantised, and the chosen
 // scales' codes are saved with their per-group metadata.
 //
-// This file is compiled with -ffp-contract=off.  Every quantiser operation is
+// This file is compiled with -ffp-contract=off and -fno-honor-nans (inputs are
+// finite; without NaNs min/max need no canonicalising moves and fuse with
+// their DPP operands).  Every quantiser operation is
 // a single IEEE fp32 operation with round-to-nearest-even (rint is
 // v_rndne_f32, denormals are kept), in the order: w' = w*s; mx, mn over the
 // group; delta = (mx - mn)/qmax floored at 1e-10; z = clamp(rint(-mn/delta));
@@ -42,7 +44,7 @@ constexpr float kDeltaMin = 1e-10f;
 // ---------------------------------------------------------------------------
 template <int kCtrl>
 __device__ __forceinline__ float dpp(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xf, 0xf, false));
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xf, 0xf, true));
 }
 
 __device__ __forceinline__ void group_minmax(float& mn, float& mx, int lanes) {
@@ -90,12 +92,19 @@ __device__ __forceinline__ GroupQ group_params(float mn, float mx, float qmax, f
   GroupQ g;
   g.delta = fmaxf(div_rn(mx - mn, qmax, rq), kDeltaMin);
   g.rdelta = 1.0f / g.delta;
-  g.z = fminf(fmaxf(__builtin_rintf(div_rn(-mn, g.delta, g.rdelta)), 0.0f), qmax);
+  g.z = __builtin_amdgcn_fmed3f(__builtin_rintf(div_rn(-mn, g.delta, g.rdelta)), 0.0f, qmax);
   return g;
 }
 
 __device__ __forceinline__ float code_of(float wp, const GroupQ& g, float qmax) {
-  return fminf(fmaxf(__builtin_rintf(div_rn(wp, g.delta, g.rdelta)) + g.z, 0.0f), qmax);
+  return __builtin_amdgcn_fmed3f(__builtin_rintf(div_rn(wp, g.delta, g.rdelta)) + g.z, 0.0f, qmax);
+}
+
+// c - z for c = clamp(rint(q) + z, 0, qmax), formed as clamp(rint(q), -z, qmax - z).
+// The two agree exactly: the integers involved are exact in fp32 unless
+// |rint(q)| >= 2^24, and then both clamp to the same bound.
+__device__ __forceinline__ float code_minus_z(float wp, const GroupQ& g, float qmax) {
+  return __builtin_amdgcn_fmed3f(__builtin_rintf(div_rn(wp, g.delta, g.rdelta)), -g.z, qmax - g.z);
 }
 
 constexpr float kRecipSafeLo = 0x1p-60f, kRecipSafeHi = 0x1p60f;
@@ -134,15 +143,19 @@ __device__ __forceinline__ void store8(S* p, const float (&v)[8]) {
 }
 
 // ---------------------------------------------------------------------------
-// s[k][j] = fp32(pow(fp64(max(a_j, 1e-8)), fp64(alpha_k)))
+// s[k][j] = fp32(pow(fp64(max(a_j, 1e-8)), fp64(alpha_k))), and optionally
+// rs[k][j] = RN(1 / s[k][j]) for the fake-quantisation kernel.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void scale_table_kernel(const float* __restrict__ a, int64_t K,
-                                                          AlphaChunk al, float* __restrict__ s) {
+                                                          AlphaChunk al, float* __restrict__ s,
+                                                          float* __restrict__ rs) {
   const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int k = blockIdx.y;
   if (j >= K || k >= al.n) return;
   const double x = (double)fmaxf(a[j], kAMin);
-  s[(int64_t)k * K + j] = (float)pow(x, (double)al.v[k]);
+  const float v = (float)pow(x, (double)al.v[k]);
+  s[(int64_t)k * K + j] = v;
+  if (rs) rs[(int64_t)k * K + j] = 1.0f / v;
 }
 
 // ---------------------------------------------------------------------------
@@ -152,8 +165,8 @@ __global__ __launch_bounds__(256) void scale_table_kernel(const float* __restric
 // 512-column row segment per step (8 consecutive columns per lane, 16-byte
 // loads), so the tile is read from HBM once into registers (8 rows x 8
 // values per lane) and reused for every scale vector; only the 8 scales of
-// the lane's columns are fetched per vector, with their reciprocals shared by
-// the 8 rows.  A group of G channels lives in
+// the lane's columns are fetched per vector, with their reciprocals (read from
+// rs when the caller has them, else computed) shared by the 8 rows.  A group of G channels lives in
 // G/8 consecutive lanes and is reduced with DPP.  Output k is written to
 // out + k*out_rows*K, row-major or in the GEMM's tiled layout (16-byte chunks
 // land on their swizzled slot; padding rows up to a multiple of 256 get zeros).
@@ -163,10 +176,13 @@ constexpr int kFqCols = 512;                  // columns per workgroup (one wave
 constexpr int kFqRowSteps = 8;                // rows per wave
 constexpr int kFqRows = kFqRowSteps * (kFqThreads / 64);
 
-template <typename S, typename O, bool kDelta, bool kTiled>
+// kLanes = G/8 lanes per group, or 0 to take it from lanes_rt.
+template <typename S, typename O, bool kDelta, bool kTiled, int kLanes>
 __global__ __launch_bounds__(kFqThreads) void fake_quant_kernel(
-    const S* __restrict__ W, int64_t N, int64_t K, const float* __restrict__ s, int n_s,
-    float qmax, int lanes, int64_t out_rows, O* __restrict__ out) {
+    const S* __restrict__ W, int64_t N, int64_t K, const float* __restrict__ s,
+    const float* __restrict__ rs, int n_s, float qmax, int lanes_rt, int64_t out_rows,
+    O* __restrict__ out) {
+  const int lanes = kLanes ? kLanes : lanes_rt;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t col = (int64_t)blockIdx.x * kFqCols + lane * 8;
@@ -192,14 +208,15 @@ __global__ __launch_bounds__(kFqThreads) void fake_quant_kernel(
     float sv[8], ys[8];
     if (col_ok) {
       load8(s + (int64_t)k * K + col, sv);
+      if (rs) load8(rs + (int64_t)k * K + col, ys);
     } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) sv[i] = 1.0f;
+      for (int i = 0; i < 8; ++i) sv[i] = ys[i] = 1.0f;
     }
     bool extreme = false;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      ys[i] = 1.0f / sv[i];
+      if (!rs) ys[i] = 1.0f / sv[i];
       extreme |= !(fabsf(sv[i]) >= kRecipSafeLo && fabsf(sv[i]) <= kRecipSafeHi);
     }
     const bool exact_div = __builtin_amdgcn_ballot_w64(extreme) != 0;   // wave-uniform
@@ -222,8 +239,7 @@ __global__ __launch_bounds__(kFqThreads) void fake_quant_kernel(
       float o[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float c = code_of(wp[i], g, qmax);
-        const float deq = (c - g.z) * g.delta;
+        const float deq = code_minus_z(wp[i], g, qmax) * g.delta;
         const float what = exact_div ? deq / sv[i] : div_rn(deq, sv[i], ys[i]);
         o[i] = kDelta ? (w[p][i] - what) : what;
       }
@@ -314,20 +330,32 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(
 }
 
 template <typename S, typename O, bool kDelta>
-hipError_t fq_dispatch(const void* W, int64_t N, int64_t K, const float* s, int n_s, int bits,
-                       int group, bool tiled, void* out, hipStream_t st) {
+hipError_t fq_dispatch(const void* W, int64_t N, int64_t K, const float* s, const float* rs,
+                       int n_s, int bits, int group, bool tiled, void* out, hipStream_t st) {
   const int64_t out_rows = tiled ? padded_rows(N) : N;
   dim3 grid((unsigned)((K + kFqCols - 1) / kFqCols), (unsigned)((out_rows + kFqRows - 1) / kFqRows));
   const float qmax = (float)((1 << bits) - 1);
   const S* w = static_cast<const S*>(W);
   O* o = static_cast<O*>(out);
+  const int lanes = group / 8;
   ProfScope p("awq_fake_quant", st);
-  if (tiled)
-    fake_quant_kernel<S, O, kDelta, true><<<grid, kFqThreads, 0, st>>>(w, N, K, s, n_s, qmax,
-                                                                       group / 8, out_rows, o);
-  else
-    fake_quant_kernel<S, O, kDelta, false><<<grid, kFqThreads, 0, st>>>(w, N, K, s, n_s, qmax,
-                                                                        group / 8, out_rows, o);
+  if (!tiled) {
+    fake_quant_kernel<S, O, kDelta, false, 0><<<grid, kFqThreads, 0, st>>>(w, N, K, s, rs, n_s,
+                                                                           qmax, lanes, out_rows, o);
+    return hipGetLastError();
+  }
+  // the search's launch: the group width is a compile-time constant
+#define AWQ_FQ_TILED(L)                                                                     \
+  fake_quant_kernel<S, O, kDelta, true, L><<<grid, kFqThreads, 0, st>>>(w, N, K, s, rs, n_s, \
+                                                                        qmax, L, out_rows, o)
+  switch (lanes) {
+    case 4: AWQ_FQ_TILED(4); break;
+    case 8: AWQ_FQ_TILED(8); break;
+    case 16: AWQ_FQ_TILED(16); break;
+    case 32: AWQ_FQ_TILED(32); break;
+    default: AWQ_FQ_TILED(64); break;
+  }
+#undef AWQ_FQ_TILED
   return hipGetLastError();
 }
 
@@ -354,29 +382,30 @@ hipError_t pack_dispatch(const void* W, int64_t N, int64_t K, const float* s, in
 }  // namespace
 
 hipError_t launch_scale_table(const float* a, int64_t K, const AlphaChunk& al, float* s_out,
-                              hipStream_t st) {
+                              float* rs_out, hipStream_t st) {
   ProfScope p("awq_scale_table", st);
-  scale_table_kernel<<<dim3((unsigned)((K + 255) / 256), (unsigned)al.n), 256, 0, st>>>(a, K, al, s_out);
+  scale_table_kernel<<<dim3((unsigned)((K + 255) / 256), (unsigned)al.n), 256, 0, st>>>(a, K, al, s_out,
+                                                                                     rs_out);
   return hipGetLastError();
 }
 
 hipError_t launch_fake_quant(const void* W, awq_dtype_t dt, int64_t N, int64_t K, const float* s,
-                             int n_s, int bits, int group, bool delta_form, bool tiled, void* out,
-                             hipStream_t st) {
+                             const float* rs, int n_s, int bits, int group, bool delta_form,
+                             bool tiled, void* out, hipStream_t st) {
   switch (dt) {
     case AWQ_F32:
       if (tiled) return hipErrorInvalidValue;
       return delta_form
-                 ? fq_dispatch<float, float, true>(W, N, K, s, n_s, bits, group, false, out, st)
-                 : fq_dispatch<float, float, false>(W, N, K, s, n_s, bits, group, false, out, st);
+                 ? fq_dispatch<float, float, true>(W, N, K, s, rs, n_s, bits, group, false, out, st)
+                 : fq_dispatch<float, float, false>(W, N, K, s, rs, n_s, bits, group, false, out, st);
     case AWQ_F16:
       return delta_form
-                 ? fq_dispatch<_Float16, _Float16, true>(W, N, K, s, n_s, bits, group, tiled, out, st)
-                 : fq_dispatch<_Float16, _Float16, false>(W, N, K, s, n_s, bits, group, tiled, out, st);
+                 ? fq_dispatch<_Float16, _Float16, true>(W, N, K, s, rs, n_s, bits, group, tiled, out, st)
+                 : fq_dispatch<_Float16, _Float16, false>(W, N, K, s, rs, n_s, bits, group, tiled, out, st);
     default:
       return delta_form
-                 ? fq_dispatch<__bf16, __bf16, true>(W, N, K, s, n_s, bits, group, tiled, out, st)
-                 : fq_dispatch<__bf16, __bf16, false>(W, N, K, s, n_s, bits, group, tiled, out, st);
+                 ? fq_dispatch<__bf16, __bf16, true>(W, N, K, s, rs, n_s, bits, group, tiled, out, st)
+                 : fq_dispatch<__bf16, __bf16, false>(W, N, K, s, rs, n_s, bits, group, tiled, out, st);
   }
 }
 

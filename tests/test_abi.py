@@ -121,6 +121,8 @@ def test_search_layout_full_and_batched():
     assert (full["tile_m"], full["tile_n"]) == (256, 256)
     assert (full["tiles_m"], full["tiles_n"]) == (16, 16)
     assert full["s_table_offset"] == 0
+    # the scale table and its reciprocals precede the partials
+    assert full["partials_offset"] - full["s_table_offset"] >= 2 * n * K * 4
     assert full["y_ref_offset"] != 2 ** 64 - 1
     per_alpha = N * K * 2
     assert full["total_bytes"] == full["w_hat_offset"] + n * per_alpha

@@ -243,6 +243,11 @@ def test_search_matches_oracle(dtype, bits, group, N, K, T, flags):
     ws = res["workspace"]
     s_tab = ws[lay["s_table_offset"]:lay["s_table_offset"] + 20 * K * 4].view(torch.float32)
     np.testing.assert_array_equal(res["s_best"].cpu().numpy(), s_tab.view(20, K)[best].cpu().numpy())
+    # the reciprocal table that follows it holds the correctly rounded 1/s
+    r0 = lay["s_table_offset"] + 20 * K * 4
+    rs_tab = ws[r0:r0 + 20 * K * 4].view(torch.float32).cpu().numpy()
+    s_np = s_tab.cpu().numpy()
+    np.testing.assert_array_equal(rs_tab, np.float32(1.0) / s_np)
     # partials: their fixed-order sum is the loss
     tiles = lay["tiles_m"] * lay["tiles_n"]
     p0 = lay["partials_offset"]
@@ -362,3 +367,48 @@ def test_search_custom_grid_and_ties():
     assert int(res["best_idx"].cpu()[0]) == (0 if losses[0] <= losses[2] else 2)
     ref = oracle.search(to_numpy(W), to_numpy(X), 4, 128, alphas)
     np.testing.assert_allclose(losses, ref["losses"], rtol=1e-3)
+
+
+def tiled_rows(flat, rows, K):
+    """Rows of a matrix stored in the GEMM's tiled layout (awq.h): 256-row tiles,
+    32-deep stages, 16-byte chunk c of row r at slot c ^ ((r >> 1) & 3)."""
+    rows = torch.as_tensor(rows, dtype=torch.int64, device=flat.device)[:, None]
+    k = torch.arange(K, dtype=torch.int64, device=flat.device)[None, :]
+    t, r, s = rows // 256, rows % 256, k // 32
+    c = (k % 32) // 8
+    return flat[((t * (K // 32) + s) * 256 + r) * 32 + 8 * (c ^ ((r >> 1) & 3)) + k % 8]
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("bits,group", [(4, 32), (3, 64), (4, 128), (2, 256), (5, 512)])
+def test_search_candidates_exact(dtype, bits, group):
+    """The search's own fake-quant launch (tiled output, group width fixed at
+    compile time, reciprocals from the scale table): every D = W - W_hat of
+    the batch equals the oracle's bit for bit, and the padding rows are zero."""
+    log_case(test="search_candidates", dtype=dtype, bits=bits, group=group)
+    N, K, T = 300, 1024, 40
+    W, X = random_layer(N + group + bits, N, K, T, dtype=dtype, outlier_factor=30.0)
+    Wn = to_numpy(W).astype(F32)
+    Wn[1, :group] = np.abs(Wn[1, :group]) + F32(0.001)   # one-signed group
+    Wn[2, :group] = F32(0.25)                             # constant group
+    W = torch.from_numpy(Wn).to(DT[dtype])
+    Wn = to_numpy(W).astype(F32)
+    alphas = np.array([0.0, 0.45, 0.95], dtype=F32)
+    Wd, Xd = W.cuda(), X.cuda()
+    a = awq.awq_act_stats(Xd)
+    res = awq.awq_search_scales(Wd, Xd, a, bits, group, alphas)
+    torch.cuda.synchronize()
+    lay, ws = res["layout"], res["workspace"]
+    n_a = len(alphas)
+    s0 = lay["s_table_offset"]
+    s_tab = ws[s0:s0 + n_a * K * 4].view(torch.float32).view(n_a, K).cpu().numpy()
+    Np = (N + 255) // 256 * 256
+    d0 = lay["w_hat_offset"]
+    esz = 2
+    D = ws[d0:d0 + n_a * Np * K * esz].view(DT[dtype]).view(n_a, Np * K)
+    for k in range(n_a):
+        got = tiled_rows(D[k], np.arange(Np), K).to(torch.float32).cpu().numpy()
+        exp = cast_like(Wn - oracle.fake_quant(Wn, s_tab[k], bits, group), DT[dtype])
+        bad = got[:N] != exp
+        assert not bad.any(), (k, np.argwhere(bad)[:5])
+        assert not got[N:].any()
