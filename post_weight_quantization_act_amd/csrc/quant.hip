@@ -263,69 +263,93 @@ __global__ __launch_bounds__(kFqThreads) void fake_quant_kernel(
 // ---------------------------------------------------------------------------
 // Final quantisation + packing for one scale vector.
 //
-// One lane owns 32 consecutive columns of a row: it loads them, reduces its
-// share of the group (G/32 lanes per group, DPP), computes the 32 codes and
-// writes them as `bits` uint32 words -- exactly its slice of the row's
-// little-endian bitstream (32 codes x bits bits).  The first lane of each
-// group writes the group's step and zero-point.
+// One lane owns 32 consecutive columns of kPackRows rows: it loads the 32
+// scales once, then per row loads the 32 weights, reduces its share of the
+// group (G/32 lanes per group, DPP), computes the 32 codes and writes them as
+// `bits` uint32 words -- exactly its slice of the row's little-endian
+// bitstream (32 codes x bits bits).  The first lane of each group writes the
+// group's step and zero-point.  Consecutive lanes own consecutive column
+// chunks (a group never straddles a wave: K/32 is a multiple of G/32).
 // ---------------------------------------------------------------------------
+constexpr int kPackRows = 4;
+
 template <typename S, int BITS>
 __global__ __launch_bounds__(256) void quantize_pack_kernel(
     const S* __restrict__ W, int64_t N, int64_t K, const float* __restrict__ s, int group,
     int lanes, uint32_t* __restrict__ codes, float* __restrict__ scales,
     uint8_t* __restrict__ zeros) {
   const int64_t chunks_per_row = K / 32;
+  const int64_t row_blocks = (N + kPackRows - 1) / kPackRows;
   const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const bool ok = q < N * chunks_per_row;
-  const int64_t row = ok ? q / chunks_per_row : 0;
+  const bool ok = q < row_blocks * chunks_per_row;
+  const int64_t rb = ok ? q / chunks_per_row : 0;
   const int64_t cc = ok ? q % chunks_per_row : 0;
   const int64_t col0 = cc * 32;
   const float qmax = (float)((1 << BITS) - 1);
+  const float rq = 1.0f / qmax;
 
-  float wp[32];
+  float sv[32];
 #pragma unroll
   for (int h = 0; h < 4; ++h) {
-    float v[8], sv[8];
+    float v[8];
     if (ok) {
-      load8(W + row * K + col0 + h * 8, v);
-      load8(s + col0 + h * 8, sv);
+      load8(s + col0 + h * 8, v);
     } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) { v[i] = 0.0f; sv[i] = 1.0f; }
+      for (int i = 0; i < 8; ++i) v[i] = 1.0f;
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) wp[h * 8 + i] = v[i] * sv[i];
+    for (int i = 0; i < 8; ++i) sv[h * 8 + i] = v[i];
   }
-  float mn = wp[0], mx = wp[0];
-#pragma unroll
-  for (int i = 1; i < 32; ++i) {
-    mn = fminf(mn, wp[i]);
-    mx = fmaxf(mx, wp[i]);
-  }
-  group_minmax(mn, mx, lanes);
-  const GroupQ g = group_params(mn, mx, qmax, 1.0f / qmax);
 
-  // 32 codes of `bits` bits -> `bits` words; bit p of the slice is bit
-  // p%32 of word p/32.
-  uint32_t words[BITS];
+  for (int r = 0; r < kPackRows; ++r) {
+    const int64_t row = rb * kPackRows + r;
+    const bool row_ok = ok && row < N;      // uniform across a group's lanes
+    float wp[32];
 #pragma unroll
-  for (int i = 0; i < BITS; ++i) words[i] = 0u;
+    for (int h = 0; h < 4; ++h) {
+      float v[8];
+      if (row_ok) {
+        load8(W + row * K + col0 + h * 8, v);
+      } else {
 #pragma unroll
-  for (int j = 0; j < 32; ++j) {
-    const uint32_t c = (uint32_t)code_of(wp[j], g, qmax);
-    const int p = BITS * j;               // compile-time after unrolling
-    const int wi = p >> 5, sh = p & 31;
-    words[wi] |= c << sh;
-    if (sh + BITS > 32) words[wi + 1] |= c >> (32 - sh);   // BITS <= 8: two words at most
-  }
-  if (!ok) return;
-  uint32_t* dst = codes + row * (chunks_per_row * BITS) + cc * BITS;
+        for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+      }
 #pragma unroll
-  for (int t = 0; t < BITS; ++t) dst[t] = words[t];
-  if ((cc % lanes) == 0) {
-    const int64_t gi = row * (K / group) + col0 / group;
-    scales[gi] = g.delta;
-    zeros[gi] = (uint8_t)g.z;
+      for (int i = 0; i < 8; ++i) wp[h * 8 + i] = v[i] * sv[h * 8 + i];
+    }
+    float mn = wp[0], mx = wp[0];
+#pragma unroll
+    for (int i = 1; i < 32; ++i) {
+      mn = fminf(mn, wp[i]);
+      mx = fmaxf(mx, wp[i]);
+    }
+    group_minmax(mn, mx, lanes);
+    const GroupQ g = group_params(mn, mx, qmax, rq);
+
+    // 32 codes of `bits` bits -> `bits` words; bit p of the slice is bit
+    // p%32 of word p/32.
+    uint32_t words[BITS];
+#pragma unroll
+    for (int i = 0; i < BITS; ++i) words[i] = 0u;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const uint32_t c = (uint32_t)code_of(wp[j], g, qmax);
+      const int p = BITS * j;               // compile-time after unrolling
+      const int wi = p >> 5, sh = p & 31;
+      words[wi] |= c << sh;
+      if (sh + BITS > 32) words[wi + 1] |= c >> (32 - sh);   // BITS <= 8: two words at most
+    }
+    if (row_ok) {
+      uint32_t* dst = codes + row * (chunks_per_row * BITS) + cc * BITS;
+#pragma unroll
+      for (int t = 0; t < BITS; ++t) dst[t] = words[t];
+      if ((cc % lanes) == 0) {
+        const int64_t gi = row * (K / group) + col0 / group;
+        scales[gi] = g.delta;
+        zeros[gi] = (uint8_t)g.z;
+      }
+    }
   }
 }
 
@@ -362,7 +386,7 @@ hipError_t fq_dispatch(const void* W, int64_t N, int64_t K, const float* s, cons
 template <typename S>
 hipError_t pack_dispatch(const void* W, int64_t N, int64_t K, const float* s, int bits, int group,
                          uint32_t* codes, float* scales, uint8_t* zeros, hipStream_t st) {
-  const int64_t threads = N * (K / 32);
+  const int64_t threads = (N + kPackRows - 1) / kPackRows * (K / 32);
   const unsigned blocks = (unsigned)((threads + 255) / 256);
   const S* w = static_cast<const S*>(W);
   ProfScope p("awq_quantize_pack", st);
