@@ -280,6 +280,32 @@ def quantize_pack(W, s, bits: int, group: int):
 
 
 # ---------------------------------------------------------------------------
+# Using the packed weights: the low-bit linear layer.
+# [P2] "Tiny Chat": the inference kernel dequantises the low-bit weights on
+# the fly and never writes the dequantised copy back to memory.  [P2]
+# "Measures" (equivalence transform): with the scales folded, y = W x is
+# computed as (W diag(s)) (diag(s)^-1 x); the stored codes quantise W diag(s),
+# so the activations the layer receives are x / s.  [P1] section 5: 1/s is
+# folded into the operator that produces x.
+# ---------------------------------------------------------------------------
+def dequantize(codes: np.ndarray, scales: np.ndarray, zeros: np.ndarray, bits: int, group: int,
+               K: int) -> np.ndarray:
+    """W'[i, j] = fp32((c[i, j] - z[i, g]) * delta[i, g]), g = j // group: the quantised W diag(s)."""
+    c = unpack_codes(codes, bits, K).astype(F32)
+    d_full = np.repeat(np.asarray(scales, dtype=F32), group, axis=1)
+    z_full = np.repeat(np.asarray(zeros).astype(F32), group, axis=1)
+    return (c - z_full) * d_full
+
+
+def lowbit_matmul(Xs: np.ndarray, codes: np.ndarray, scales: np.ndarray, zeros: np.ndarray,
+                  bits: int, group: int) -> np.ndarray:
+    """Y = Xs W'^T in fp64 ([M, N]); Xs [M, K] are the activations already divided by s."""
+    Xs = np.asarray(Xs)
+    Wd = dequantize(codes, scales, zeros, bits, group, Xs.shape[1])
+    return Xs.astype(F64) @ Wd.astype(F64).T
+
+
+# ---------------------------------------------------------------------------
 # Helpers that exist only to pin the pages' worked examples.
 # ---------------------------------------------------------------------------
 def fake_quant_sym(w, bits: int) -> np.ndarray:

@@ -386,3 +386,67 @@ def test_pack_round_trip(bits):
     words = oracle.pack_codes(codes, bits)
     assert words.shape == (5, oracle.packed_words_per_row(96, bits))
     np.testing.assert_array_equal(oracle.unpack_codes(words, bits, 96), codes)
+
+
+# ---------------------------------------------------------------------------
+# The low-bit layer that consumes the packed weights
+# ---------------------------------------------------------------------------
+def test_dequantize_hand_example():
+    """INT4, one group of 32: codes 0..15 then 15..0, step 0.25, zero-point 8."""
+    codes = np.concatenate([np.arange(16), np.arange(15, -1, -1)]).astype(np.uint8)[None, :]
+    words = oracle.pack_codes(codes, 4)
+    assert int(words[0, 0]) == 0x76543210 and int(words[0, 3]) == 0x01234567
+    Wd = oracle.dequantize(words, np.array([[0.25]], np.float32), np.array([[8]], np.uint8),
+                           4, 32, 32)
+    expect = (codes[0].astype(np.float64) - 8) * 0.25
+    np.testing.assert_array_equal(Wd[0], expect.astype(np.float32))
+    assert Wd[0, 0] == -2.0 and Wd[0, 15] == 1.75 and Wd[0, 16] == 1.75
+
+
+@pytest.mark.parametrize("bits,group", [(4, 128), (3, 64), (2, 32), (8, 256)])
+def test_dequantize_then_divide_is_fake_quant(bits, group):
+    """The packed artefact carries exactly the candidate the search scored:
+    dequantise, divide by s in fp32, and fake_quant's W_hat comes back bit for bit."""
+    W, _ = random_layer(40 + bits, 24, 512, 1, dtype="fp16")
+    Wn = to_numpy(W).astype(np.float32)
+    rng = np.random.default_rng(bits)
+    s = np.exp(rng.uniform(-2, 2, 512)).astype(np.float32)
+    codes, delta, zero = oracle.quantize_pack(Wn, s, bits, group)
+    back = oracle.dequantize(codes, delta, zero, bits, group, 512) / s[None, :]
+    np.testing.assert_array_equal(back, oracle.fake_quant(Wn, s, bits, group))
+
+
+def test_lowbit_matmul_is_the_layer_output():
+    """[P2] "Measures" equivalence: the packed layer fed x / s gives x W_hat^T,
+    up to the fp32 rounding of W_hat = deq / s (half an ulp per weight)."""
+    W, X = random_layer(9, 48, 256, 5, dtype="fp16", outlier_factor=20.0)
+    Wn, Xn = to_numpy(W).astype(np.float32), to_numpy(X).astype(np.float64)
+    s = oracle.scales_for_alpha(oracle.act_stats(to_numpy(X)), np.float32(0.5))
+    codes, delta, zero = oracle.quantize_pack(Wn, s, 4, 128)
+    Y = oracle.lowbit_matmul(Xn / s[None, :].astype(np.float64), codes, delta, zero, 4, 128)
+    W_hat = oracle.fake_quant(Wn, s, 4, 128).astype(np.float64)
+    ref = Xn @ W_hat.T
+    bound = 2.0 ** -24 * (np.abs(Xn) @ np.abs(W_hat).T) * 1.01 + 1e-300
+    assert np.all(np.abs(Y - ref) <= bound)
+
+
+def test_lowbit_matmul_brute_force():
+    """Every output of a tiny packed layer against the exact rational sum."""
+    rng = np.random.default_rng(3)
+    M, N, K, bits, group = 2, 3, 64, 3, 32
+    codes = rng.integers(0, 8, size=(N, K), dtype=np.uint8)
+    delta = np.exp(rng.uniform(-4, 0, (N, K // group))).astype(np.float32)
+    zero = rng.integers(0, 8, size=(N, K // group), dtype=np.uint8)
+    Xs = rng.standard_normal((M, K)).astype(np.float16)
+    Y = oracle.lowbit_matmul(Xs, oracle.pack_codes(codes, bits), delta, zero, bits, group)
+    for m in range(M):
+        for i in range(N):
+            exact, mag = Fraction(0), Fraction(0)
+            for j in range(K):
+                g = j // group
+                w = np.float32(np.float32(int(codes[i, j]) - int(zero[i, g])) * delta[i, g])
+                term = Fraction(float(Xs[m, j])) * Fraction(float(w))
+                exact += term
+                mag += abs(term)
+            # fp64 accumulation of K products of fp16 x fp32 values (exact in fp64)
+            assert abs(Fraction(float(Y[m, i])) - exact) <= K * Fraction(1, 2 ** 53) * mag
