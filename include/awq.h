@@ -222,6 +222,37 @@ awq_status_t awq_quantize_pack(const void* W, awq_dtype_t w_dtype, int64_t N, in
                                hipStream_t stream);
 
 /* ------------------------------------------------------------------------ *
+ * Using the packed weights: the low-bit linear layer for decode-shaped
+ * inputs ([P2] "Tiny Chat": dequantise on the fly inside the kernel, never
+ * write the dequantised weights back, reorder the low-bit weights offline so
+ * the kernel unpacks them cheaply; [P2] "Measures": the layer computes
+ * (W diag(s)) (diag(s)^-1 x), so it receives activations already divided by
+ * s, which [P1] section 5 folds into the operator that produces them).
+ *
+ * awq_lowbit_repack: one-off reordering of awq_quantize_pack's output.
+ *   codes [N, bits*K/32] uint32, scales [N, K/group] fp32, zeros
+ *   [N, K/group] uint8 (device) ->
+ *   codes_t uint32 [K/32][N][bits]: the `bits` words of chunk j (columns
+ *     32j .. 32j+31) of row n at word ((j*N) + n)*bits, same bit order;
+ *   meta_t  [K/group][N] pairs of fp32 (delta, z) (8 bytes each).
+ * awq_lowbit_gemv: Y [M, N] fp32 = Xs W'^T, Xs [M, K] of x_dtype (the
+ *   activations divided by s), W'[n, k] = fp32((c[n,k] - z) * delta) of k's
+ *   group: exactly the quantiser's dequantised value.  Products and sums in
+ *   fp32; K is split into chunks whose partial sums go to the workspace
+ *   (awq_lowbit_gemv_workspace_size(M, N, K) bytes) and are added in a fixed
+ *   order, so results are reproducible.  Built for small M (decode, up to a
+ *   few tens of rows): the packed weights are read once per 8 rows of Xs.
+ * ------------------------------------------------------------------------ */
+awq_status_t awq_lowbit_repack(const uint32_t* codes, const float* scales, const uint8_t* zeros,
+                               int64_t N, int64_t K, int bits, int group,
+                               uint32_t* codes_t, void* meta_t, hipStream_t stream);
+size_t awq_lowbit_gemv_workspace_size(int64_t M, int64_t N, int64_t K);
+awq_status_t awq_lowbit_gemv(const void* X, awq_dtype_t x_dtype, int64_t M, int64_t K,
+                             const uint32_t* codes_t, const void* meta_t, int64_t N, int bits,
+                             int group, float* Y, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
+/* ------------------------------------------------------------------------ *
  * Kernel timing.  While enabled, every kernel the library launches (or, after
  * awq_profile_select(prefix), every kernel whose name starts with prefix) is
  * bracketed by a pair of HIP events on its stream; each event pair adds a few
@@ -230,7 +261,8 @@ awq_status_t awq_quantize_pack(const void* W, awq_dtype_t w_dtype, int64_t N, in
  * the launch count and the summed elapsed milliseconds.  Kernel names:
  * awq_act_stats_partial, awq_act_stats_finish, awq_scale_table, awq_tile_rows,
  * awq_fake_quant, awq_gemm_ref_output, awq_gemm_sse, awq_loss_argmin,
- * awq_quantize_pack.  awq_profile_reset() drops the records.  Thread-safe.
+ * awq_quantize_pack, awq_lowbit_repack, awq_lowbit_gemv, awq_lowbit_reduce.
+ * awq_profile_reset() drops the records.  Thread-safe.
  * ------------------------------------------------------------------------ */
 awq_status_t awq_profile_enable(int enable);
 awq_status_t awq_profile_select(const char* prefix);

@@ -81,6 +81,9 @@ _SIGS = {
     "awq_search_scales": ([_P, _P, _I32, _I64, _I64, _I64, _P, _I32, _I32, _P, _I32, _U32,
                            _P, _P, _P, _P, _SZ, _P], _I32),
     "awq_quantize_pack": ([_P, _I32, _I64, _I64, _P, _I32, _I32, _P, _P, _P, _P], _I32),
+    "awq_lowbit_repack": ([_P, _P, _P, _I64, _I64, _I32, _I32, _P, _P, _P], _I32),
+    "awq_lowbit_gemv_workspace_size": ([_I64, _I64, _I64], _SZ),
+    "awq_lowbit_gemv": ([_P, _I32, _I64, _I64, _P, _P, _I64, _I32, _I32, _P, _P, _SZ, _P], _I32),
     "awq_profile_enable": ([_I32], _I32),
     "awq_profile_select": ([ctypes.c_char_p], _I32),
     "awq_profile_read": ([ctypes.c_char_p, ctypes.POINTER(_I64), ctypes.POINTER(_D)], _I32),
@@ -240,6 +243,45 @@ def awq_quantize_pack(W: torch.Tensor, s: torch.Tensor, bits: int, group: int):
                                        codes.data_ptr(), scales.data_ptr(), zeros.data_ptr(),
                                        _stream(W.device)))
     return codes, scales, zeros
+
+
+def awq_lowbit_repack(codes: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor, K: int,
+                      bits: int, group: int):
+    """awq_quantize_pack output -> (codes_t int32 [K/32, N, bits], meta_t fp32 [K/group, N, 2])."""
+    for t, name in ((codes, "codes"), (scales, "scales"), (zeros, "zeros")):
+        _dev(t, name)
+    N = scales.shape[0]
+    codes_t = torch.empty((K // 32, N, bits), dtype=torch.int32, device=codes.device)
+    meta_t = torch.empty((K // group, N, 2), dtype=torch.float32, device=codes.device)
+    _check(library().awq_lowbit_repack(codes.data_ptr(), scales.data_ptr(), zeros.data_ptr(), N, K,
+                                       bits, group, codes_t.data_ptr(), meta_t.data_ptr(),
+                                       _stream(codes.device)))
+    return codes_t, meta_t
+
+
+def awq_lowbit_gemv_workspace_size(M: int, N: int, K: int) -> int:
+    return int(library().awq_lowbit_gemv_workspace_size(M, N, K))
+
+
+def awq_lowbit_gemv(Xs: torch.Tensor, codes_t: torch.Tensor, meta_t: torch.Tensor, bits: int,
+                    group: int, out: torch.Tensor | None = None,
+                    workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Y [M, N] fp32 = Xs [M, K] times the dequantised packed weights (repacked layout)."""
+    _dev(Xs, "Xs")
+    _dev(codes_t, "codes_t")
+    _dev(meta_t, "meta_t")
+    M, K = Xs.shape
+    N = codes_t.shape[1]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=Xs.device)
+    need = awq_lowbit_gemv_workspace_size(M, N, K)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=Xs.device)
+    _check(library().awq_lowbit_gemv(Xs.data_ptr(), _dtype(Xs), M, K, codes_t.data_ptr(),
+                                     meta_t.data_ptr(), N, bits, group, out.data_ptr(),
+                                     workspace.data_ptr(), workspace.numel(),
+                                     _stream(Xs.device)))
+    return out
 
 
 def awq_profile_enable(enable: bool = True) -> None:

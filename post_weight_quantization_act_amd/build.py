@@ -30,7 +30,7 @@ PER_FILE = {
     "quant.hip": ["-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
                   "-fno-gpu-flush-denormals-to-zero", "-fno-honor-nans"],
 }
-SOURCES = ["act_stats.hip", "quant.hip", "gemm_sse.hip", "awq_api.cpp"]
+SOURCES = ["act_stats.hip", "quant.hip", "gemm_sse.hip", "lowbit.hip", "awq_api.cpp"]
 
 
 def hipcc() -> str:

@@ -329,6 +329,56 @@ awq_status_t awq_search_scales(const void* W, const void* X, awq_dtype_t dtype, 
   AWQ_GUARD_END
 }
 
+// ---------------------------------------------------------------------------
+// The low-bit layer on the packed weights.
+// ---------------------------------------------------------------------------
+awq_status_t awq_lowbit_repack(const uint32_t* codes, const float* scales, const uint8_t* zeros,
+                               int64_t N, int64_t K, int bits, int group, uint32_t* codes_t,
+                               void* meta_t, hipStream_t stream) {
+  AWQ_GUARD_BEGIN
+  awq_status_t st = check_quant_args(AWQ_F16, N, K, bits, group);
+  if (st != AWQ_OK) return st;
+  if (!codes || !scales || !zeros || !codes_t || !meta_t)
+    return fail(AWQ_ERR_INVALID_ARG, "null pointer");
+  if (!aligned(codes, 4) || !aligned(scales, 4) || !aligned(codes_t, 4) || !aligned(meta_t, 8))
+    return fail(AWQ_ERR_UNSUPPORTED, "codes, scales, codes_t 4-byte and meta_t 8-byte aligned");
+  if ((uint64_t)N * (uint64_t)K / 32 * (uint64_t)bits * 4 > kMaxBufferBytes ||
+      (uint64_t)N * (uint64_t)(K / group) * 8 > kMaxBufferBytes)
+    return fail(AWQ_ERR_UNSUPPORTED, "packed layer exceeds the 4 GiB operand limit");
+  hipError_t e = awq::launch_lowbit_repack(codes, scales, zeros, N, K, bits, group, codes_t,
+                                           meta_t, stream);
+  if (e != hipSuccess) return hip_fail(e, "lowbit repack launch");
+  return AWQ_OK;
+  AWQ_GUARD_END
+}
+
+size_t awq_lowbit_gemv_workspace_size(int64_t M, int64_t N, int64_t K) {
+  if (M < 1 || N < 1 || K < 32) return 0;
+  return awq::lowbit_gemv_ws_bytes(M, N, K);
+}
+
+awq_status_t awq_lowbit_gemv(const void* X, awq_dtype_t x_dtype, int64_t M, int64_t K,
+                             const uint32_t* codes_t, const void* meta_t, int64_t N, int bits,
+                             int group, float* Y, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+  AWQ_GUARD_BEGIN
+  awq_status_t st = check_quant_args(x_dtype, N, K, bits, group);
+  if (st != AWQ_OK) return st;
+  if (M < 1) return fail(AWQ_ERR_INVALID_ARG, "M must be >= 1");
+  if (!X || !codes_t || !meta_t || !Y) return fail(AWQ_ERR_INVALID_ARG, "null pointer");
+  if (!aligned(codes_t, 4) || !aligned(meta_t, 8) || !aligned(Y, 4))
+    return fail(AWQ_ERR_UNSUPPORTED, "codes_t and Y 4-byte, meta_t 8-byte aligned");
+  const size_t need = awq::lowbit_gemv_ws_bytes(M, N, K);
+  if (!workspace || workspace_bytes < need)
+    return fail(AWQ_ERR_WORKSPACE, "workspace of %zu bytes is below %zu", workspace_bytes, need);
+  if (!aligned(workspace, 4)) return fail(AWQ_ERR_WORKSPACE, "workspace must be 4-byte aligned");
+  hipError_t e = awq::launch_lowbit_gemv(X, x_dtype, M, K, codes_t, meta_t, N, bits, group, Y,
+                                         workspace, stream);
+  if (e != hipSuccess) return hip_fail(e, "lowbit gemv launch");
+  return AWQ_OK;
+  AWQ_GUARD_END
+}
+
 awq_status_t awq_quantize_pack(const void* W, awq_dtype_t w_dtype, int64_t N, int64_t K,
                                const float* s, int bits, int group, uint32_t* codes_out,
                                float* scales_out, uint8_t* zeros_out, hipStream_t stream) {

@@ -159,3 +159,45 @@ def test_binding_refuses_cpu_tensors():
     W = torch.zeros(8, 128, dtype=torch.float16)
     with pytest.raises(ValueError):
         awq.awq_quantize_pack(W, torch.ones(128), 4, 128)
+
+
+def _gemv_args(**over):
+    a = dict(X=FAKE, dt=1, M=2, K=256, codes_t=FAKE, meta_t=FAKE, N=300, bits=4, group=128,
+             Y=FAKE, ws=FAKE, ws_bytes=1 << 30, stream=NULL)
+    a.update(over)
+    return tuple(a.values())
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(X=NULL), -1),
+    (dict(M=0), -1),
+    (dict(K=200), -1),                        # K % group != 0
+    (dict(bits=9), -2),
+    (dict(group=64, K=96), -1),
+    (dict(meta_t=ctypes.c_void_p(0x1004)), -2),   # meta_t not 8-byte aligned
+    (dict(ws=NULL), -3),
+    (dict(ws_bytes=16), -3),
+])
+def test_lowbit_gemv_validation(over, status):
+    assert _call("awq_lowbit_gemv", *_gemv_args(**over)) == status
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(codes=NULL), -1),
+    (dict(bits=1), -2),
+    (dict(K=200), -1),
+    (dict(meta_t=ctypes.c_void_p(0x1004)), -2),
+])
+def test_lowbit_repack_validation(over, status):
+    a = dict(codes=FAKE, scales=FAKE, zeros=FAKE, N=8, K=256, bits=4, group=128, codes_t=FAKE,
+             meta_t=FAKE, stream=NULL)
+    a.update(over)
+    assert _call("awq_lowbit_repack", *tuple(a.values())) == status
+
+
+def test_lowbit_gemv_workspace_size():
+    # one fp32 partial per (k-split, activation row, output row)
+    n = awq.awq_lowbit_gemv_workspace_size(4, 4096, 4096)
+    assert n > 0 and n % (4 * 4096 * 4) == 0
+    assert awq.awq_lowbit_gemv_workspace_size(1, 28672, 8192) >= 28672 * 4
+    assert awq.awq_lowbit_gemv_workspace_size(0, 16, 256) == 0

@@ -1,0 +1,146 @@
+"""The low-bit layer on the packed weights (needs a gfx950 GPU): repacked layout
+bit-exact, and Y = Xs W'^T against the oracle's fp64 product within the fp32
+accumulation bound.
+
+Inputs come from the CPU side only: seeded synthetic layers, scales from the
+oracle's statistic, codes from the oracle's quantize_pack.  The GPU result is
+compared per output with |Y_gpu - Y| <= (n + 2) 2^-24 sum_k |x_k w'_k|, where
+n = K + (number of k-splits) bounds the length of any fp32 summation chain
+(every product x w' is exact in fp32 arithmetic up to its own rounding,
+counted in n); W' itself is exact on both sides.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import post_weight_quantization_act_amd as awq
+from datagen import CONFIGS, random_layer, to_numpy
+
+pytestmark = pytest.mark.gpu
+
+F32 = np.float32
+DT = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    awq.library()
+    yield
+    torch.cuda.synchronize()
+
+
+def log_case(**kw):
+    print("case", kw, flush=True)
+
+
+def packed_layer(seed, N, K, T, dtype, bits, group, alpha=0.5):
+    """CPU-built artefact: W, calibration X, s = a^alpha and the oracle's packing."""
+    W, X = random_layer(seed, N, K, T, dtype=dtype, outlier_factor=30.0)
+    Wn, Xn = to_numpy(W).astype(F32), to_numpy(X)
+    s = oracle.scales_for_alpha(oracle.act_stats(Xn), F32(alpha))
+    codes, delta, zero = oracle.quantize_pack(Wn, s, bits, group)
+    return Xn, s, codes, delta, zero
+
+
+def activations(Xn, s, M, dtype):
+    """Decode-step activations divided by s, rounded to the layer dtype."""
+    Xs = (Xn[:M].astype(np.float64) / s[None, :].astype(np.float64)).astype(F32)
+    return torch.from_numpy(Xs).to(DT[dtype])
+
+
+def splits(M, N, K):
+    return awq.awq_lowbit_gemv_workspace_size(M, N, K) // (4 * M * N)
+
+
+def check(Y, Xs_t, codes, delta, zero, bits, group, rows=None):
+    Xs = Xs_t.to(torch.float32).numpy().astype(np.float64)
+    K = Xs.shape[1]
+    N = codes.shape[0]
+    n = K + splits(Xs.shape[0], N, K) + 2
+    if rows is not None:
+        codes, delta, zero = codes[rows], delta[rows], zero[rows]
+        Y = Y[:, rows]
+    ref = oracle.lowbit_matmul(Xs, codes, delta, zero, bits, group)
+    Wd = oracle.dequantize(codes, delta, zero, bits, group, K).astype(np.float64)
+    tol = n * 2.0 ** -24 * (np.abs(Xs) @ np.abs(Wd).T)
+    err = np.abs(Y.astype(np.float64) - ref)
+    assert np.all(err <= tol), (np.argwhere(err > tol)[:5], err.max(), tol.max())
+
+
+CASES = [
+    # dtype, bits, group, M, N, K
+    ("fp16", 4, 128, 1, 300, 1024),
+    ("fp16", 3, 128, 4, 1100, 4096),
+    ("bf16", 3, 64, 8, 513, 2048),
+    ("bf16", 4, 128, 13, 256, 512),      # two activation-row blocks
+    ("fp16", 2, 32, 3, 77, 96),
+    ("fp16", 5, 256, 2, 640, 768),
+    ("fp32", 6, 512, 5, 129, 1536),
+    ("fp16", 7, 32, 1, 1000, 160),
+    ("bf16", 8, 64, 16, 200, 11008 // 172 * 64),
+]
+
+
+@pytest.mark.parametrize("dtype,bits,group,M,N,K", CASES)
+def test_lowbit_gemv_matches_oracle(dtype, bits, group, M, N, K):
+    log_case(test="lowbit_gemv", dtype=dtype, bits=bits, group=group, M=M, N=N, K=K)
+    Xn, s, codes, delta, zero = packed_layer(N + K + bits, N, K, max(M, 16), dtype, bits, group)
+    c_d = torch.from_numpy(codes.view(np.int32)).cuda()
+    d_d = torch.from_numpy(delta).cuda()
+    z_d = torch.from_numpy(zero).cuda()
+    codes_t, meta_t = awq.awq_lowbit_repack(c_d, d_d, z_d, K, bits, group)
+    Xs = activations(Xn, s, M, dtype)
+    Y = awq.awq_lowbit_gemv(Xs.cuda(), codes_t, meta_t, bits, group)
+    torch.cuda.synchronize()
+    # repacked layout, bit for bit
+    ct = codes_t.cpu().numpy().view(np.uint32)
+    exp_ct = codes.reshape(N, K // 32, bits).transpose(1, 0, 2)
+    np.testing.assert_array_equal(ct, exp_ct)
+    mt = meta_t.cpu().numpy()
+    np.testing.assert_array_equal(mt[..., 0], delta.T)
+    np.testing.assert_array_equal(mt[..., 1], zero.T.astype(F32))
+    check(Y.cpu().numpy(), Xs, codes, delta, zero, bits, group)
+
+
+def test_lowbit_gemv_is_reproducible_and_alpha_zero_is_rtn():
+    """Same inputs twice: identical bits.  With s = 1 the layer is the plain
+    round-to-nearest layer: codes from quantize_pack(W, 1)."""
+    log_case(test="lowbit_repro")
+    W, X = random_layer(5, 384, 1024, 4, dtype="fp16")
+    Wn = to_numpy(W).astype(F32)
+    codes, delta, zero = oracle.quantize_pack(Wn, np.ones(1024, F32), 4, 128)
+    codes_t, meta_t = awq.awq_lowbit_repack(torch.from_numpy(codes.view(np.int32)).cuda(),
+                                            torch.from_numpy(delta).cuda(),
+                                            torch.from_numpy(zero).cuda(), 1024, 4, 128)
+    Xd = X.cuda()
+    Y1 = awq.awq_lowbit_gemv(Xd, codes_t, meta_t, 4, 128)
+    Y2 = awq.awq_lowbit_gemv(Xd, codes_t, meta_t, 4, 128)
+    torch.cuda.synchronize()
+    assert torch.equal(Y1, Y2)
+    check(Y1.cpu().numpy(), X, codes, delta, zero, 4, 128)
+    # and it is the layer whose weights fake_quant(W, 1) gives
+    ref = to_numpy(X).astype(np.float64) @ oracle.fake_quant(Wn, np.ones(1024, F32), 4, 128).astype(np.float64).T
+    np.testing.assert_allclose(Y1.cpu().numpy(), ref, rtol=1e-4, atol=1e-4 * np.abs(ref).max())
+
+
+@pytest.mark.parametrize("name,M", [("llama7b-qproj", 1), ("llama7b-qproj", 8),
+                                    ("llama7b-upgate", 4), ("llama7b-down", 2), ("70b-mlp", 1)])
+def test_lowbit_gemv_full_size(name, M):
+    """The five layers' weight shapes at full size (256 calibration tokens for
+    the scales), packed by the oracle, checked on sampled output rows."""
+    spec = CONFIGS[name]
+    N, K, bits, G = spec.N, spec.K, spec.bits, spec.group
+    log_case(test="lowbit_full", name=name, M=M, N=N, K=K, bits=bits)
+    Xn, s, codes, delta, zero = packed_layer(spec.seed, N, K, 256, spec.dtype, bits, G)
+    codes_t, meta_t = awq.awq_lowbit_repack(torch.from_numpy(codes.view(np.int32)).cuda(),
+                                            torch.from_numpy(delta).cuda(),
+                                            torch.from_numpy(zero).cuda(), K, bits, G)
+    Xs = activations(Xn, s, M, spec.dtype)
+    Y = awq.awq_lowbit_gemv(Xs.cuda(), codes_t, meta_t, bits, G)
+    torch.cuda.synchronize()
+    rows = np.concatenate([np.arange(0, 64), np.arange(N // 2, N // 2 + 64), np.arange(N - 64, N)])
+    check(Y.cpu().numpy(), Xs, codes, delta, zero, bits, G, rows=rows)
