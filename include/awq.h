@@ -237,11 +237,14 @@ awq_status_t awq_quantize_pack(const void* W, awq_dtype_t w_dtype, int64_t N, in
  *   meta_t  [K/group][N] pairs of fp32 (delta, z) (8 bytes each).
  * awq_lowbit_gemv: Y [M, N] fp32 = Xs W'^T, Xs [M, K] of x_dtype (the
  *   activations divided by s), W'[n, k] = fp32((c[n,k] - z) * delta) of k's
- *   group: exactly the quantiser's dequantised value.  Products and sums in
- *   fp32; K is split into chunks whose partial sums go to the workspace
- *   (awq_lowbit_gemv_workspace_size(M, N, K) bytes) and are added in a fixed
- *   order, so results are reproducible.  Built for small M (decode, up to a
- *   few tens of rows): the packed weights are read once per 8 rows of Xs.
+ *   group: exactly the quantiser's dequantised value, applied as
+ *   y = sum_g delta_g * sum_{k in g} x_k (c_k - z_g) with the integer
+ *   differences and their products exact and the sums in fp32, added in a fixed
+ *   order, so results are reproducible: K is split over workgroups whose
+ *   partial sums go to the workspace (awq_lowbit_gemv_workspace_size(M, N, K)
+ *   bytes, possibly 0, then the workspace may be NULL) and are added by a
+ *   second kernel in split order.  Xs must be 16-byte aligned.  Built for small M (decode, up to a few
+ *   tens of rows): the packed weights are read once per 8 rows of Xs.
  * ------------------------------------------------------------------------ */
 awq_status_t awq_lowbit_repack(const uint32_t* codes, const float* scales, const uint8_t* zeros,
                                int64_t N, int64_t K, int bits, int group,

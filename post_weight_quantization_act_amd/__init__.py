@@ -274,8 +274,8 @@ def awq_lowbit_gemv(Xs: torch.Tensor, codes_t: torch.Tensor, meta_t: torch.Tenso
     N = codes_t.shape[1]
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=Xs.device)
-    need = awq_lowbit_gemv_workspace_size(M, N, K)
     if workspace is None:
+        need = awq_lowbit_gemv_workspace_size(M, N, K)
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=Xs.device)
     _check(library().awq_lowbit_gemv(Xs.data_ptr(), _dtype(Xs), M, K, codes_t.data_ptr(),
                                      meta_t.data_ptr(), N, bits, group, out.data_ptr(),

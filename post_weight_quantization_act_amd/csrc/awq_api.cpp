@@ -366,12 +366,13 @@ awq_status_t awq_lowbit_gemv(const void* X, awq_dtype_t x_dtype, int64_t M, int6
   if (st != AWQ_OK) return st;
   if (M < 1) return fail(AWQ_ERR_INVALID_ARG, "M must be >= 1");
   if (!X || !codes_t || !meta_t || !Y) return fail(AWQ_ERR_INVALID_ARG, "null pointer");
-  if (!aligned(codes_t, 4) || !aligned(meta_t, 8) || !aligned(Y, 4))
-    return fail(AWQ_ERR_UNSUPPORTED, "codes_t and Y 4-byte, meta_t 8-byte aligned");
+  if (!aligned(X, 16) || !aligned(codes_t, 4) || !aligned(meta_t, 8) || !aligned(Y, 4))
+    return fail(AWQ_ERR_UNSUPPORTED, "X 16-byte, codes_t and Y 4-byte, meta_t 8-byte aligned");
   const size_t need = awq::lowbit_gemv_ws_bytes(M, N, K);
-  if (!workspace || workspace_bytes < need)
+  if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(AWQ_ERR_WORKSPACE, "workspace of %zu bytes is below %zu", workspace_bytes, need);
-  if (!aligned(workspace, 4)) return fail(AWQ_ERR_WORKSPACE, "workspace must be 4-byte aligned");
+  if (need > 0 && !aligned(workspace, 4))
+    return fail(AWQ_ERR_WORKSPACE, "workspace must be 4-byte aligned");
   hipError_t e = awq::launch_lowbit_gemv(X, x_dtype, M, K, codes_t, meta_t, N, bits, group, Y,
                                          workspace, stream);
   if (e != hipSuccess) return hip_fail(e, "lowbit gemv launch");

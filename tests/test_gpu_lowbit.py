@@ -4,10 +4,11 @@ accumulation bound.
 
 Inputs come from the CPU side only: seeded synthetic layers, scales from the
 oracle's statistic, codes from the oracle's quantize_pack.  The GPU result is
-compared per output with |Y_gpu - Y| <= (n + 2) 2^-24 sum_k |x_k w'_k|, where
-n = K + (number of k-splits) bounds the length of any fp32 summation chain
-(every product x w' is exact in fp32 arithmetic up to its own rounding,
-counted in n); W' itself is exact on both sides.
+compared per output with |Y_gpu - Y| <= (K + 2) 2^-24 sum_k |x_k w'_k|: the
+kernel forms y = sum_g delta_g sum_{k in g} x_k (c_k - z_g) with exact
+integer differences and exact products x (c - z), so its error is that of
+fp32 sums with fewer than K + 2 roundings on any path (group sums, one
+product by delta per group, the sums over groups and over k-splits).
 """
 
 import numpy as np
@@ -52,15 +53,10 @@ def activations(Xn, s, M, dtype):
     return torch.from_numpy(Xs).to(DT[dtype])
 
 
-def splits(M, N, K):
-    return awq.awq_lowbit_gemv_workspace_size(M, N, K) // (4 * M * N)
-
-
 def check(Y, Xs_t, codes, delta, zero, bits, group, rows=None):
     Xs = Xs_t.to(torch.float32).numpy().astype(np.float64)
     K = Xs.shape[1]
-    N = codes.shape[0]
-    n = K + splits(Xs.shape[0], N, K) + 2
+    n = K + 2
     if rows is not None:
         codes, delta, zero = codes[rows], delta[rows], zero[rows]
         Y = Y[:, rows]
@@ -144,3 +140,24 @@ def test_lowbit_gemv_full_size(name, M):
     torch.cuda.synchronize()
     rows = np.concatenate([np.arange(0, 64), np.arange(N // 2, N // 2 + 64), np.arange(N - 64, N)])
     check(Y.cpu().numpy(), Xs, codes, delta, zero, bits, G, rows=rows)
+
+
+def test_lowbit_gemv_consecutive_shapes_are_independent():
+    """Calls of different shapes in a row on one stream give the same bits as
+    each shape alone."""
+    log_case(test="lowbit_consecutive")
+    shapes = [(4, 1100, 4096, 3, 128), (1, 300, 1024, 4, 64), (8, 513, 2048, 4, 128),
+              (2, 4096, 512, 2, 32), (16, 100, 11008, 4, 128)]
+    outs, refs = [], []
+    for i, (M, N, K, bits, G) in enumerate(shapes):
+        Xn, s, codes, delta, zero = packed_layer(70 + i, N, K, 16, "fp16", bits, G)
+        codes_t, meta_t = awq.awq_lowbit_repack(torch.from_numpy(codes.view(np.int32)).cuda(),
+                                                torch.from_numpy(delta).cuda(),
+                                                torch.from_numpy(zero).cuda(), K, bits, G)
+        Xs = activations(Xn, s, M, "fp16").cuda()
+        outs.append((Xs, codes_t, meta_t, bits, G, awq.awq_lowbit_gemv(Xs, codes_t, meta_t, bits, G)))
+    torch.cuda.synchronize()
+    for Xs, codes_t, meta_t, bits, G, y in outs:
+        alone = awq.awq_lowbit_gemv(Xs, codes_t, meta_t, bits, G)
+        torch.cuda.synchronize()
+        assert torch.equal(y, alone)
