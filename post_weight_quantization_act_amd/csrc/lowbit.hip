@@ -18,8 +18,8 @@
 // integers c - z and their products with x are exact, the sums are fp32.
 //
 // A workgroup owns 256 output rows (lane = row) and one run of up to 32
-// chunks of 32 columns (a k-split), with the codes of the next 4 chunks in
-// flight while 4 are summed.  The split's activations are staged in LDS and
+// chunks of 32 columns (a k-split), with the codes of the next 2 chunks in
+// flight while 2 are summed.  The split's activations are staged in LDS and
 // read as broadcasts (every lane needs the same ones).  With several splits
 // the partial sums go to the workspace and a second kernel adds them in
 // split order, so the result does not depend on scheduling.  (Letting the
@@ -36,7 +36,7 @@ namespace {
 constexpr int kRows = 256;        // output rows per workgroup, one per lane
 constexpr int kMB = 8;            // activation rows per pass
 constexpr int kMaxChunks = 32;    // chunks of 32 columns per k-split
-constexpr int kUnroll = 4;        // chunks whose codes are loaded together
+constexpr int kUnroll = 2;        // chunks whose codes are loaded together
 constexpr int kTargetGroups = 2048;
 
 struct Split {
