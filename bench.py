@@ -39,6 +39,10 @@ def parse():
     p.add_argument("--flags", type=int, default=0, help="0 weight-delta form, 1 reference-output form")
     p.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--lowbit", action="store_true",
+                   help="instead of the search, time the low-bit decode layer (awq_lowbit_gemv "
+                        "on repacked codes) on the synthetic layers' weight shapes, M = 1, 4, 16 "
+                        "activation rows, against the dense fp16/bf16 product")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 1 GiB fp32 device copy (torch.neg into a second "
                         "buffer) three times: the known-size reference for HBM byte counters")
@@ -58,6 +62,65 @@ def calibrate_copy() -> None:
     torch.cuda.synchronize()
     print(json.dumps({"calibration": "torch.neg fp32", "bytes_read": 4 * n,
                       "bytes_written": 4 * n, "launches": 3}), flush=True)
+
+
+def bench_lowbit(args) -> None:
+    """Decode-shaped low-bit layer: packed-weight bytes per second of one whole
+    awq_lowbit_gemv call (GEMV and, with several k-splits, the reduction),
+    timed with events around `reps` back-to-back calls; the headline case is
+    the 70B MLP layer (28672 x 8192 bf16, INT3) at one activation row."""
+    import torch
+
+    import post_weight_quantization_act_amd as awq
+    from datagen import CONFIGS
+
+    dev = torch.device("cuda", 0)
+    torch.manual_seed(0)
+
+    def timed(fn, reps):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3          # us per call
+
+    cases = []
+    for name in ("llama7b-qproj", "llama7b-upgate", "llama7b-down", "70b-mlp"):
+        spec = CONFIGS[name]
+        N, K, b, G = spec.N, spec.K, spec.bits, spec.group
+        dt = torch.float16 if spec.dtype == "fp16" else torch.bfloat16
+        W = (torch.randn(N, K, device=dev) * 0.02).to(dt)
+        codes, scales, zeros = awq.awq_quantize_pack(W, torch.ones(K, device=dev), b, G)
+        codes_t, meta_t = awq.awq_lowbit_repack(codes, scales, zeros, K, b, G)
+        Wt = W.t().contiguous()
+        for M in (1, 4, 16):
+            X = torch.randn(M, K, device=dev).to(dt)
+            ws = torch.empty(max(1, awq.awq_lowbit_gemv_workspace_size(M, N, K)),
+                             dtype=torch.uint8, device=dev)
+            Y = torch.empty(M, N, device=dev)
+            us = timed(lambda: awq.awq_lowbit_gemv(X, codes_t, meta_t, b, G, out=Y, workspace=ws),
+                       args.steps)
+            dense_us = timed(lambda: X @ Wt, args.steps)
+            nbytes = N * K * b / 8 + N * (K // G) * 8 + M * K * 2 + M * N * 4
+            cases.append({"layer": name, "dtype": spec.dtype, "bits": b, "M": M, "N": N, "K": K,
+                          "us": us, "bytes": nbytes, "gbps": nbytes / (us * 1e-6) / 1e9,
+                          "dense_us": dense_us, "speedup_vs_dense": dense_us / us})
+        del W, Wt, codes, scales, zeros, codes_t, meta_t
+    head = next(c for c in cases if c["layer"] == "70b-mlp" and c["M"] == 1)
+    print(json.dumps({
+        "metric": "low-bit decode layer: packed bytes per second of one call",
+        "value": head["gbps"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "higher_is_better": True, "dtype": head["dtype"],
+        "data": "synthetic",
+        "config": {"workload": "70b MLP weights 28672x8192 bf16, INT3 g128, 1 activation row"},
+        "roofline": {"bound": "hbm", "achieved": head["gbps"], "peak": 8000.0, "unit": "GB/s",
+                     "frac": head["gbps"] / 8000.0, "traffic": None},
+        "cases": cases}), flush=True)
 
 
 def kernel_source_hash() -> str:
@@ -121,6 +184,9 @@ def main():
         sys.exit(2)
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.lowbit:
+        bench_lowbit(args)
         return
     import numpy as np
     import torch
