@@ -75,7 +75,9 @@ typedef enum {
  * candidate GEMM on W_hat subtracts its output from it in the epilogue.
  * fp16 and fp32 layers only: rounding W_hat itself to bf16 perturbs the
  * up-scaled salient channels by more than the 1e-3 loss tolerance, so bf16
- * returns AWQ_ERR_UNSUPPORTED. */
+ * returns AWQ_ERR_UNSUPPORTED.  With fp16 the rounding of W_hat still limits
+ * the loss accuracy at high bit widths (about 1e-3 relative at INT4 on narrow
+ * layers, several 1e-3 at INT8); the default form has no such limit. */
 #define AWQ_SEARCH_REFERENCE_OUTPUT 1u
 
 /* awq_fake_quant output selection. */

@@ -205,11 +205,32 @@ def rounding_bound(Xn, Wn, W_hat, dtype):
     return float(np.mean(2 * np.abs(e) * B + B * B) + 1e-6 * np.mean(e * e))
 
 
+def reference_form_bound(Xn, Wn, W_hat, dtype):
+    """Worst-case loss error of the reference-output form for one candidate.
+
+    That form rounds W_hat itself to the layer dtype (relative error <= u per
+    weight) and accumulates X W_hat^T and the reference output X W^T in fp32,
+    so each output error e = Y - Yhat is off by at most
+    B = u sum |x w_hat| + K 2^-24 (sum |x w_hat| + sum |x w|); the loss by at
+    most mean(2 |e| B + B^2).  For high bit widths this exceeds 1e-3 of the
+    loss: the quantisation error is then not much larger than the rounding of
+    W_hat (the weight-delta form, which rounds D instead, has no such limit)."""
+    X64 = Xn.astype(np.float64)
+    e = X64 @ (Wn.astype(np.float64) - W_hat.astype(np.float64)).T
+    xw_hat = np.abs(X64) @ np.abs(W_hat.astype(np.float64)).T
+    xw = np.abs(X64) @ np.abs(Wn.astype(np.float64)).T
+    K = Xn.shape[1]
+    B = UNIT_ROUNDOFF[dtype] * (1 + 2.0 ** -20) * xw_hat + K * 2.0 ** -24 * (xw_hat + xw)
+    return float(np.mean(2 * np.abs(e) * B + B * B) + 1e-6 * np.mean(e * e))
+
+
 SEARCH_CASES = [
     ("fp16", 4, 128, 300, 384, 520), ("bf16", 3, 128, 129, 256, 77), ("fp32", 4, 128, 64, 512, 256),
     ("fp16", 3, 64, 256, 256, 256), ("fp16", 4, 128, 513, 640, 300),
     # degenerate layers: one output channel and/or one calibration token
     ("bf16", 4, 32, 1, 96, 1), ("fp16", 3, 128, 700, 256, 1), ("bf16", 4, 128, 1, 384, 900),
+    # one 32-column stage (K = 32), 8-bit and 2-bit codes, the widest group
+    ("fp16", 8, 32, 100, 32, 50), ("bf16", 2, 512, 70, 1024, 300), ("fp32", 5, 256, 33, 256, 45),
 ]
 
 
@@ -235,6 +256,11 @@ def test_search_matches_oracle(dtype, bits, group, N, K, T, flags):
         # degenerate layer: too few outputs for operand rounding to average
         # out, so the bar is the arithmetic's own worst-case bound
         tol = np.array([max(1e-3 * ref["losses"][k], rounding_bound(
+            Xn, Wn, oracle.fake_quant(Wn, ref["s_table"][k], bits, group), dtype))
+            for k in range(len(alphas))])
+    elif flags == awq.AWQ_SEARCH_REFERENCE_OUTPUT and dtype != "fp32":
+        # the reference-output form rounds W_hat to fp16: its own bound
+        tol = np.array([max(1e-3 * ref["losses"][k], reference_form_bound(
             Xn, Wn, oracle.fake_quant(Wn, ref["s_table"][k], bits, group), dtype))
             for k in range(len(alphas))])
     check_losses(losses, ref["losses"], best, ref["best"], tol)
