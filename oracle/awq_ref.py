@@ -280,6 +280,62 @@ def quantize_pack(W, s, bits: int, group: int):
 
 
 # ---------------------------------------------------------------------------
+# The mixed-precision ablation that motivates the method.
+# [P2] "Measures": keeping 1% of the weights in FP16 chosen by activation
+# magnitude brings the INT3 model almost back to FP16, choosing them by weight
+# magnitude barely helps.  [P1] section 4: rank the input channels by the
+# activation statistic and keep the top 1% in FP16; section 5, item 4: every
+# other weight is quantised by standard round-to-nearest over groups.  [P4]
+# "AWQ实现要点" / 量化方法: k = int(0.01 * in_features) channels, ranked by
+# mean |x|.
+# ---------------------------------------------------------------------------
+def salient_channels(score: np.ndarray, n_keep: int) -> np.ndarray:
+    """Mask of the n_keep input channels with the largest score (ties: lower index first)."""
+    score = np.asarray(score, dtype=F32)
+    order = np.argsort(-score.astype(F64), kind="stable")
+    keep = np.zeros(score.shape[0], dtype=bool)
+    keep[order[:n_keep]] = True
+    return keep
+
+
+def weight_channel_magnitude(W: np.ndarray) -> np.ndarray:
+    """mean_i |W[i, j]| per input channel: the weight-side ranking statistic
+    (the activation statistic's definition applied to the rows of W)."""
+    return act_stats(W)
+
+
+def fake_quant_keep(W: np.ndarray, keep: np.ndarray, bits: int, group: int) -> np.ndarray:
+    """Round-to-nearest quantisation of W (s = 1) except the kept columns.
+
+    Only the weights being quantised set their group's range: min and max run
+    over the group's non-kept weights.  Kept columns keep their full-precision
+    value.  Same fp32 operation order as quantize_codes / fake_quant."""
+    W = np.asarray(W)
+    _check_quant_args(W, bits, group)
+    N, K = W.shape
+    qmax = F32((1 << bits) - 1)
+    w = W.astype(F32)
+    k2 = np.asarray(keep, dtype=bool)[None, :]
+    g_lo = np.where(k2, F32(np.inf), w).reshape(N, K // group, group)
+    g_hi = np.where(k2, F32(-np.inf), w).reshape(N, K // group, group)
+    mn, mx = g_lo.min(axis=2), g_hi.max(axis=2)
+    with np.errstate(invalid="ignore", over="ignore"):
+        delta = np.maximum((mx - mn) / qmax, DELTA_MIN)     # all-kept group: -inf -> DELTA_MIN
+        zero = np.clip(np.rint(-mn / delta), F32(0), qmax)
+    d_full = np.repeat(delta.astype(F32), group, axis=1)
+    z_full = np.repeat(zero.astype(F32), group, axis=1)
+    c = np.clip(np.rint(w / d_full) + z_full, F32(0), qmax)
+    deq = (c - z_full) * d_full
+    return np.where(k2, w, deq).astype(F32)
+
+
+def salient_keep_loss(W: np.ndarray, X: np.ndarray, keep: np.ndarray, bits: int,
+                      group: int) -> float:
+    """Output error of the layer with the kept channels in full precision and the rest RTN."""
+    return output_loss(W, X, fake_quant_keep(W, keep, bits, group))
+
+
+# ---------------------------------------------------------------------------
 # Using the packed weights: the low-bit linear layer.
 # [P2] "Tiny Chat": the inference kernel dequantises the low-bit weights on
 # the fly and never writes the dequantised copy back to memory.  [P2]

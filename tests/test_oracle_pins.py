@@ -450,3 +450,53 @@ def test_lowbit_matmul_brute_force():
                 mag += abs(term)
             # fp64 accumulation of K products of fp16 x fp32 values (exact in fp64)
             assert abs(Fraction(float(Y[m, i])) - exact) <= K * Fraction(1, 2 ** 53) * mag
+
+
+# ---------------------------------------------------------------------------
+# Mixed-precision ablation: keep the top channels, round the rest to nearest
+# ---------------------------------------------------------------------------
+def test_salient_channels_ranking_and_ties():
+    score = np.array([0.5, 3.0, 1.0, 3.0, 0.1, 2.0], np.float32)
+    np.testing.assert_array_equal(oracle.salient_channels(score, 2), [0, 1, 0, 1, 0, 0])
+    np.testing.assert_array_equal(oracle.salient_channels(score, 3), [0, 1, 0, 1, 0, 1])
+    np.testing.assert_array_equal(oracle.salient_channels(score, 0), np.zeros(6, bool))
+    # a tie at the cut: the lower index wins
+    np.testing.assert_array_equal(oracle.salient_channels(score, 1), [0, 1, 0, 0, 0, 0])
+
+
+def test_keep_excludes_kept_weights_from_the_group_range():
+    """2-bit group of 4: keeping the outlier 10 leaves [-1, 0, 0.5] to set the
+    range (step 0.5, zero-point 2), which then quantises exactly."""
+    W = np.array([[-1.0, 0.0, 0.5, 10.0]], np.float32)
+    out = oracle.fake_quant_keep(W, np.array([0, 0, 0, 1], bool), 2, 4)
+    np.testing.assert_array_equal(out, W)
+    # without keeping it the range is [-1, 10] and the small weights are lost
+    assert not np.array_equal(oracle.fake_quant(W, np.ones(4, np.float32), 2, 4), W)
+    # a group whose every weight is kept stays as it is
+    np.testing.assert_array_equal(oracle.fake_quant_keep(W, np.ones(4, bool), 2, 4), W)
+
+
+def test_keep_nothing_is_rtn_and_keep_everything_is_exact():
+    W, X = random_layer(21, 32, 256, 40, dtype="fp16", outlier_factor=20.0)
+    Wn, Xn = to_numpy(W), to_numpy(X)
+    none = np.zeros(256, bool)
+    np.testing.assert_array_equal(oracle.fake_quant_keep(Wn, none, 4, 128),
+                                  oracle.fake_quant(Wn, np.ones(256, np.float32), 4, 128))
+    assert oracle.salient_keep_loss(Wn, Xn, np.ones(256, bool), 4, 128) == 0.0
+
+
+def test_keeping_salient_activation_channels_beats_weight_magnitude():
+    """[P2] "Measures" (qualitative, parity unpinned for the page's perplexities):
+    on a layer whose 1% largest-activation channels are x10..100 outliers,
+    keeping those channels in full precision cuts the INT3 output error far
+    more than keeping the 1% largest-weight channels."""
+    W, X = random_layer(23, 256, 1024, 256, dtype="fp16", outlier_frac=0.01)
+    Wn, Xn = to_numpy(W), to_numpy(X)
+    n_keep = int(1024 * 0.01)
+    by_act = oracle.salient_channels(oracle.act_stats(Xn), n_keep)
+    by_w = oracle.salient_channels(oracle.weight_channel_magnitude(Wn), n_keep)
+    rtn = oracle.salient_keep_loss(Wn, Xn, np.zeros(1024, bool), 3, 128)
+    act = oracle.salient_keep_loss(Wn, Xn, by_act, 3, 128)
+    wgt = oracle.salient_keep_loss(Wn, Xn, by_w, 3, 128)
+    assert act < 0.5 * rtn
+    assert wgt > 0.8 * rtn
