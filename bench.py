@@ -43,6 +43,11 @@ def parse():
                    help="instead of the search, time the low-bit decode layer (awq_lowbit_gemv "
                         "on repacked codes) on the synthetic layers' weight shapes, M = 1, 4, 16 "
                         "activation rows, against the dense fp16/bf16 product")
+    p.add_argument("--salient", action="store_true",
+                   help="instead of the search, run the mixed-precision ablation on the "
+                        "synthetic layers: output error with the top 1%% channels kept at full "
+                        "precision (ranked by activation, by weight) against round-to-nearest "
+                        "and the AWQ search, and the time of one ablation evaluation")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 1 GiB fp32 device copy (torch.neg into a second "
                         "buffer) three times: the known-size reference for HBM byte counters")
@@ -123,6 +128,63 @@ def bench_lowbit(args) -> None:
         "cases": cases}), flush=True)
 
 
+def bench_salient(args) -> None:
+    """Mixed-precision ablation per synthetic layer: losses of RTN, of keeping
+    int(0.01 K) channels at full precision chosen by activation or by weight
+    magnitude, and of the AWQ search's best alpha; one evaluation (keep mask,
+    masked fake quantisation, candidate GEMM, loss) timed with events."""
+    import numpy as np
+    import torch
+
+    import post_weight_quantization_act_amd as awq
+    from datagen import CONFIGS, make_layer
+
+    dev = torch.device("cuda", 0)
+    out = []
+    for name in ("llama7b-qproj", "llama7b-upgate", "70b-mlp"):
+        spec = CONFIGS[name]
+        W, X = make_layer(spec)
+        Wd, Xd = W.to(dev), X.to(dev)
+        N, K, T = spec.N, spec.K, spec.T
+        n_keep = int(0.01 * K)
+        a = awq.awq_act_stats(Xd)
+        wmag = awq.awq_act_stats(Wd)                  # mean_i |W[i, j]|
+        rtn, _ = awq.awq_salient_keep_loss(Wd, Xd, a, 0, spec.bits, spec.group)
+        by_a, _ = awq.awq_salient_keep_loss(Wd, Xd, a, n_keep, spec.bits, spec.group)
+        by_w, _ = awq.awq_salient_keep_loss(Wd, Xd, wmag, n_keep, spec.bits, spec.group)
+        alphas = (np.arange(spec.n_alpha) / spec.n_alpha).astype(np.float32)
+        res = awq.awq_search_scales(Wd, Xd, a, spec.bits, spec.group, alphas)
+        best = float(res["losses"].min().cpu())
+        for _ in range(args.warmup):
+            awq.awq_salient_keep_loss(Wd, Xd, a, n_keep, spec.bits, spec.group)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            awq.awq_salient_keep_loss(Wd, Xd, a, n_keep, spec.bits, spec.group)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        r = float(rtn.cpu()[0])
+        out.append({"layer": name, "bits": spec.bits, "n_keep": n_keep, "loss_rtn": r,
+                    "loss_keep_by_activation": float(by_a.cpu()[0]),
+                    "loss_keep_by_weight": float(by_w.cpu()[0]), "loss_awq_best": best,
+                    "ratio_keep_by_activation": float(by_a.cpu()[0]) / r,
+                    "ratio_keep_by_weight": float(by_w.cpu()[0]) / r, "ratio_awq": best / r,
+                    "ms_per_evaluation": ms})
+        del W, X, Wd, Xd
+    head = out[0]
+    print(json.dumps({
+        "metric": "mixed-precision ablation evaluations per second (keep mask, masked fake "
+                  "quantisation, candidate GEMM, loss)",
+        "value": 1e3 / head["ms_per_evaluation"], "unit": "evaluations/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "higher_is_better": True, "dtype": "fp16",
+        "data": "synthetic",
+        "config": {"workload": "llama-7b q_proj (W fp16 4096x4096, X 4096 tokens, INT4 g128), "
+                               "1% of input channels kept"},
+        "layers": out}), flush=True)
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for f in sorted((ROOT / "post_weight_quantization_act_amd" / "csrc").glob("*")):
@@ -187,6 +249,9 @@ def main():
         return
     if args.lowbit:
         bench_lowbit(args)
+        return
+    if args.salient:
+        bench_salient(args)
         return
     import numpy as np
     import torch

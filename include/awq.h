@@ -224,6 +224,34 @@ awq_status_t awq_quantize_pack(const void* W, awq_dtype_t w_dtype, int64_t N, in
                                hipStream_t stream);
 
 /* ------------------------------------------------------------------------ *
+ * The mixed-precision ablation that motivates the method ([P2] "Measures":
+ * keeping 1% of the weights in FP16 chosen by activation magnitude recovers
+ * most of the quantisation loss, chosen by weight magnitude it does not;
+ * [P1] section 4: rank the input channels by the activation statistic and
+ * keep the top 1% in FP16; section 5 item 4: round the other weights to
+ * nearest over groups; [P4] "AWQ实现要点": k = int(0.01 * in_features)).
+ *
+ * score: [K] fp32 device, the ranking statistic (awq_act_stats of X for
+ *   "by activation"; awq_act_stats applied to W, i.e. mean_i |W[i, j]|, for
+ *   "by weight").  The n_keep channels with the largest score (ties: lower
+ *   index first) keep their full-precision weights; every other weight is
+ *   quantised round-to-nearest (s = 1, the quantiser of awq_fake_quant),
+ *   with each group's min and max taken over its quantised weights only.
+ * loss_out [1] fp64 device = sum_{t,i} (Y - Y_mix)^2 / (T N), formed like the
+ *   search's default weight-delta form.  keep_out [K] uint8 device (may be
+ *   NULL) = the chosen mask.  fp16/bf16 layers; workspace of
+ *   awq_salient_keep_workspace_size(dtype, N, K, T) bytes, 256-byte aligned;
+ *   it begins with the regions of awq_search_layout(dtype, N, K, T, 1,
+ *   AWQ_SEARCH_WEIGHT_DELTA, 0), and after the call its w_hat region holds
+ *   D = W - W_mix (tiled, in the layer dtype).
+ * ------------------------------------------------------------------------ */
+size_t awq_salient_keep_workspace_size(awq_dtype_t dtype, int64_t N, int64_t K, int64_t T);
+awq_status_t awq_salient_keep_loss(const void* W, const void* X, awq_dtype_t dtype, int64_t N,
+                                   int64_t K, int64_t T, const float* score, int64_t n_keep,
+                                   int bits, int group, double* loss_out, uint8_t* keep_out,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ *
  * Using the packed weights: the low-bit linear layer for decode-shaped
  * inputs ([P2] "Tiny Chat": dequantise on the fly inside the kernel, never
  * write the dequantised weights back, reorder the low-bit weights offline so
@@ -266,7 +294,8 @@ awq_status_t awq_lowbit_gemv(const void* X, awq_dtype_t x_dtype, int64_t M, int6
  * the launch count and the summed elapsed milliseconds.  Kernel names:
  * awq_act_stats_partial, awq_act_stats_finish, awq_scale_table, awq_tile_rows,
  * awq_fake_quant, awq_gemm_ref_output, awq_gemm_sse, awq_loss_argmin,
- * awq_quantize_pack, awq_lowbit_repack, awq_lowbit_gemv, awq_lowbit_reduce.
+ * awq_quantize_pack, awq_keep_mask, awq_lowbit_repack, awq_lowbit_gemv,
+ * awq_lowbit_reduce.
  * awq_profile_reset() drops the records.  Thread-safe.
  * ------------------------------------------------------------------------ */
 awq_status_t awq_profile_enable(int enable);

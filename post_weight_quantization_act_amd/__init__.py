@@ -81,6 +81,9 @@ _SIGS = {
     "awq_search_scales": ([_P, _P, _I32, _I64, _I64, _I64, _P, _I32, _I32, _P, _I32, _U32,
                            _P, _P, _P, _P, _SZ, _P], _I32),
     "awq_quantize_pack": ([_P, _I32, _I64, _I64, _P, _I32, _I32, _P, _P, _P, _P], _I32),
+    "awq_salient_keep_workspace_size": ([_I32, _I64, _I64, _I64], _SZ),
+    "awq_salient_keep_loss": ([_P, _P, _I32, _I64, _I64, _I64, _P, _I64, _I32, _I32, _P, _P, _P,
+                               _SZ, _P], _I32),
     "awq_lowbit_repack": ([_P, _P, _P, _I64, _I64, _I32, _I32, _P, _P, _P], _I32),
     "awq_lowbit_gemv_workspace_size": ([_I64, _I64, _I64], _SZ),
     "awq_lowbit_gemv": ([_P, _I32, _I64, _I64, _P, _P, _I64, _I32, _I32, _P, _P, _SZ, _P], _I32),
@@ -243,6 +246,33 @@ def awq_quantize_pack(W: torch.Tensor, s: torch.Tensor, bits: int, group: int):
                                        codes.data_ptr(), scales.data_ptr(), zeros.data_ptr(),
                                        _stream(W.device)))
     return codes, scales, zeros
+
+
+def awq_salient_keep_workspace_size(dtype: torch.dtype, N: int, K: int, T: int) -> int:
+    return int(library().awq_salient_keep_workspace_size(_DTYPES[dtype], N, K, T))
+
+
+def awq_salient_keep_loss(W: torch.Tensor, X: torch.Tensor, score: torch.Tensor, n_keep: int,
+                          bits: int, group: int, return_workspace: bool = False):
+    """Output MSE with the n_keep top-score channels at full precision and the
+    rest round-to-nearest -> (loss fp64 [1], keep mask uint8 [K]) and, on
+    request, the workspace (its w_hat region holds D = W - W_mix)."""
+    _dev(W, "W")
+    _dev(X, "X")
+    _dev(score, "score")
+    N, K = W.shape
+    T = X.shape[0]
+    if X.dtype != W.dtype or X.shape[1] != K:
+        raise ValueError("W [N, K] and X [T, K] must share K and dtype")
+    loss = torch.empty(1, dtype=torch.float64, device=W.device)
+    keep = torch.empty(K, dtype=torch.uint8, device=W.device)
+    ws = torch.empty(max(1, awq_salient_keep_workspace_size(W.dtype, N, K, T)), dtype=torch.uint8,
+                     device=W.device)
+    _check(library().awq_salient_keep_loss(W.data_ptr(), X.data_ptr(), _dtype(W), N, K, T,
+                                           score.data_ptr(), n_keep, bits, group, loss.data_ptr(),
+                                           keep.data_ptr(), ws.data_ptr(), ws.numel(),
+                                           _stream(W.device)))
+    return (loss, keep, ws) if return_workspace else (loss, keep)
 
 
 def awq_lowbit_repack(codes: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor, K: int,

@@ -124,6 +124,31 @@ std::vector<ProfRec> g_prof;
 std::atomic<bool> g_prof_on{false};
 std::string g_prof_prefix;   // guarded by g_prof_mu
 
+// ---------------------------------------------------------------------------
+// Mixed-precision ablation: keep the top channels, round the rest to nearest.
+// Workspace: the search layout for one candidate (alpha = 0, weight-delta
+// form), then the keep mask [K] uint8, the argmin index and a [K] fp32 copy
+// of the unit scales.
+// ---------------------------------------------------------------------------
+struct KeepLayout {
+  awq_search_layout_t search;
+  size_t keep_offset, best_offset, s_copy_offset, total_bytes;
+};
+
+awq_status_t keep_layout(awq_dtype_t dt, int64_t N, int64_t K, int64_t T, KeepLayout* L) {
+  awq_status_t st = compute_layout(dt, N, K, T, 1, AWQ_SEARCH_WEIGHT_DELTA, 0, &L->search);
+  if (st != AWQ_OK) return st;
+  size_t off = align_up(L->search.total_bytes);
+  L->keep_offset = off;
+  off = align_up(off + (size_t)K);
+  L->best_offset = off;
+  off = align_up(off + 4);
+  L->s_copy_offset = off;
+  off = align_up(off + (size_t)K * 4);
+  L->total_bytes = off;
+  return AWQ_OK;
+}
+
 }  // namespace
 
 namespace awq {
@@ -325,6 +350,71 @@ awq_status_t awq_search_scales(const void* W, const void* X, awq_dtype_t dtype, 
   e = awq::launch_loss_argmin(partials, n_alpha, tiles, 1.0 / ((double)T * (double)N), s_table, K,
                               losses_out, best_idx_out, s_best_out, stream);
   if (e != hipSuccess) return hip_fail(e, "loss/argmin launch");
+  return AWQ_OK;
+  AWQ_GUARD_END
+}
+
+size_t awq_salient_keep_workspace_size(awq_dtype_t dtype, int64_t N, int64_t K, int64_t T) {
+  if (!valid_dtype(dtype) || N < 1 || K < 1 || T < 1) return 0;
+  KeepLayout L;
+  if (keep_layout(dtype, N, K, T, &L) != AWQ_OK) return 0;
+  return L.total_bytes;
+}
+
+awq_status_t awq_salient_keep_loss(const void* W, const void* X, awq_dtype_t dtype, int64_t N,
+                                   int64_t K, int64_t T, const float* score, int64_t n_keep,
+                                   int bits, int group, double* loss_out, uint8_t* keep_out,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  AWQ_GUARD_BEGIN
+  awq_status_t st = check_quant_args(dtype, N, K, bits, group);
+  if (st != AWQ_OK) return st;
+  if (dtype == AWQ_F32) return fail(AWQ_ERR_UNSUPPORTED, "the ablation runs on fp16/bf16 layers");
+  if (T < 1) return fail(AWQ_ERR_INVALID_ARG, "T must be >= 1");
+  if (n_keep < 0 || n_keep > K) return fail(AWQ_ERR_INVALID_ARG, "n_keep=%lld outside [0, K]",
+                                            (long long)n_keep);
+  if (!W || !X || !score || !loss_out) return fail(AWQ_ERR_INVALID_ARG, "null pointer");
+  if (!aligned(W, 16) || !aligned(X, 16) || !aligned(score, 4))
+    return fail(AWQ_ERR_UNSUPPORTED, "W and X must be 16-byte aligned, score 4-byte");
+  if ((uint64_t)awq::padded_rows(T) * (uint64_t)K * 2 > kMaxBufferBytes)
+    return fail(AWQ_ERR_UNSUPPORTED, "X exceeds the 4 GiB operand limit");
+  if (!workspace) return fail(AWQ_ERR_WORKSPACE, "null workspace");
+  if (!aligned(workspace, 256)) return fail(AWQ_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  KeepLayout L;
+  st = keep_layout(dtype, N, K, T, &L);
+  if (st != AWQ_OK) return st;
+  if (workspace_bytes < L.total_bytes)
+    return fail(AWQ_ERR_WORKSPACE, "workspace of %zu bytes is below %zu", workspace_bytes,
+                L.total_bytes);
+  char* ws = static_cast<char*>(workspace);
+  float* s_table = reinterpret_cast<float*>(ws + L.search.s_table_offset);
+  float* rs_table = s_table + K;
+  double* partials = reinterpret_cast<double*>(ws + L.search.partials_offset);
+  void* xt = ws + L.search.x_tiled_offset;
+  void* d = ws + L.search.w_hat_offset;
+  uint8_t* keep = keep_out ? keep_out : reinterpret_cast<uint8_t*>(ws + L.keep_offset);
+  int32_t* best = reinterpret_cast<int32_t*>(ws + L.best_offset);
+  float* s_copy = reinterpret_cast<float*>(ws + L.s_copy_offset);
+
+  hipError_t e = awq::launch_keep_mask(score, K, n_keep, keep, stream);
+  if (e != hipSuccess) return hip_fail(e, "keep mask launch");
+  // unit scales (alpha = 0) and their reciprocals; the statistic only has to be finite
+  awq::AlphaChunk ch;
+  ch.n = 1;
+  ch.v[0] = 0.0f;
+  e = awq::launch_scale_table(score, K, ch, s_table, rs_table, stream);
+  if (e != hipSuccess) return hip_fail(e, "scale table launch");
+  e = awq::launch_tile_rows(X, T, K, xt, stream);
+  if (e != hipSuccess) return hip_fail(e, "tile_rows launch");
+  e = awq::launch_fake_quant(W, dtype, N, K, s_table, rs_table, 1, bits, group, true, true, d,
+                             stream, keep);
+  if (e != hipSuccess) return hip_fail(e, "fake_quant launch");
+  e = awq::launch_gemm(awq::Epi::kSseDelta, dtype, xt, d, true, 1, T, N, K, nullptr, partials, 0,
+                       stream);
+  if (e != hipSuccess) return hip_fail(e, "candidate GEMM launch");
+  const int64_t tiles = (int64_t)L.search.tiles_m * L.search.tiles_n;
+  e = awq::launch_loss_argmin(partials, 1, tiles, 1.0 / ((double)T * (double)N), s_table, K,
+                              loss_out, best, s_copy, stream);
+  if (e != hipSuccess) return hip_fail(e, "loss launch");
   return AWQ_OK;
   AWQ_GUARD_END
 }

@@ -85,9 +85,15 @@ hipError_t launch_scale_table(const float* a, int64_t K, const AlphaChunk& al, f
 // s [n_s, K]; rs (may be null) its elementwise RN(1 / s).  out: n_s consecutive
 // [N, K] row-major matrices, or (tiled = true, fp16/bf16 only) n_s consecutive
 // tiled [padded_rows(N), K] matrices with zero padding rows.
+// keep (tiled only, may be null): columns with keep[j] != 0 stay at full
+// precision and are left out of their group's range.
 hipError_t launch_fake_quant(const void* W, awq_dtype_t dt, int64_t N, int64_t K,
                              const float* s, const float* rs, int n_s, int bits, int group,
-                             bool delta_form, bool tiled, void* out, hipStream_t st);
+                             bool delta_form, bool tiled, void* out, hipStream_t st,
+                             const uint8_t* keep = nullptr);
+// keep[j] = 1 for the n_keep largest scores (ties: lower index first), else 0.
+hipError_t launch_keep_mask(const float* score, int64_t K, int64_t n_keep, uint8_t* keep,
+                            hipStream_t st);
 // Copy a row-major [R, K] fp16/bf16 matrix into the tiled layout (zero padding rows).
 hipError_t launch_tile_rows(const void* src, int64_t R, int64_t K, void* dst, hipStream_t st);
 hipError_t launch_quantize_pack(const void* W, awq_dtype_t dt, int64_t N, int64_t K,

@@ -177,11 +177,13 @@ constexpr int kFqRowSteps = 8;                // rows per wave
 constexpr int kFqRows = kFqRowSteps * (kFqThreads / 64);
 
 // kLanes = G/8 lanes per group, or 0 to take it from lanes_rt.
-template <typename S, typename O, bool kDelta, bool kTiled, int kLanes>
+// kKeep: columns with keep[j] != 0 stay at full precision (output W, or 0 in
+// the delta form) and take no part in their group's min / max.
+template <typename S, typename O, bool kDelta, bool kTiled, int kLanes, bool kKeep = false>
 __global__ __launch_bounds__(kFqThreads) void fake_quant_kernel(
     const S* __restrict__ W, int64_t N, int64_t K, const float* __restrict__ s,
     const float* __restrict__ rs, int n_s, float qmax, int lanes_rt, int64_t out_rows,
-    O* __restrict__ out) {
+    O* __restrict__ out, const uint8_t* __restrict__ keep = nullptr) {
   const int lanes = kLanes ? kLanes : lanes_rt;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -202,6 +204,10 @@ __global__ __launch_bounds__(kFqThreads) void fake_quant_kernel(
       for (int i = 0; i < 8; ++i) w[p][i] = 0.0f;
     }
   }
+
+  bool kept[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) kept[i] = kKeep && col_ok && keep[col + i] != 0;
 
   const float rq = 1.0f / qmax;
   for (int k = 0; k < n_s; ++k) {
@@ -227,12 +233,22 @@ __global__ __launch_bounds__(kFqThreads) void fake_quant_kernel(
       float mn, mx;
 #pragma unroll
       for (int i = 0; i < 8; ++i) wp[i] = w[p][i] * sv[i];
-      mn = wp[0];
-      mx = wp[0];
+      if (kKeep) {
+        mn = kept[0] ? __builtin_inff() : wp[0];
+        mx = kept[0] ? -__builtin_inff() : wp[0];
 #pragma unroll
-      for (int i = 1; i < 8; ++i) {
-        mn = fminf(mn, wp[i]);
-        mx = fmaxf(mx, wp[i]);
+        for (int i = 1; i < 8; ++i) {
+          mn = fminf(mn, kept[i] ? __builtin_inff() : wp[i]);
+          mx = fmaxf(mx, kept[i] ? -__builtin_inff() : wp[i]);
+        }
+      } else {
+        mn = wp[0];
+        mx = wp[0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) {
+          mn = fminf(mn, wp[i]);
+          mx = fmaxf(mx, wp[i]);
+        }
       }
       group_minmax(mn, mx, lanes);
       const GroupQ g = group_params(mn, mx, qmax, rq);
@@ -242,6 +258,7 @@ __global__ __launch_bounds__(kFqThreads) void fake_quant_kernel(
         const float deq = code_minus_z(wp[i], g, qmax) * g.delta;
         const float what = exact_div ? deq / sv[i] : div_rn(deq, sv[i], ys[i]);
         o[i] = kDelta ? (w[p][i] - what) : what;
+        if (kKeep && kept[i]) o[i] = kDelta ? 0.0f : w[p][i];
       }
       const int64_t r = row0 + (int64_t)p * (kFqThreads / 64);
       if (kTiled) {
@@ -355,7 +372,8 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(
 
 template <typename S, typename O, bool kDelta>
 hipError_t fq_dispatch(const void* W, int64_t N, int64_t K, const float* s, const float* rs,
-                       int n_s, int bits, int group, bool tiled, void* out, hipStream_t st) {
+                       int n_s, int bits, int group, bool tiled, const uint8_t* keep, void* out,
+                       hipStream_t st) {
   const int64_t out_rows = tiled ? padded_rows(N) : N;
   dim3 grid((unsigned)((K + kFqCols - 1) / kFqCols), (unsigned)((out_rows + kFqRows - 1) / kFqRows));
   const float qmax = (float)((1 << bits) - 1);
@@ -364,14 +382,19 @@ hipError_t fq_dispatch(const void* W, int64_t N, int64_t K, const float* s, cons
   const int lanes = group / 8;
   ProfScope p("awq_fake_quant", st);
   if (!tiled) {
+    if (keep) return hipErrorInvalidValue;
     fake_quant_kernel<S, O, kDelta, false, 0><<<grid, kFqThreads, 0, st>>>(w, N, K, s, rs, n_s,
                                                                            qmax, lanes, out_rows, o);
     return hipGetLastError();
   }
   // the search's launch: the group width is a compile-time constant
-#define AWQ_FQ_TILED(L)                                                                     \
-  fake_quant_kernel<S, O, kDelta, true, L><<<grid, kFqThreads, 0, st>>>(w, N, K, s, rs, n_s, \
-                                                                        qmax, L, out_rows, o)
+#define AWQ_FQ_TILED(L)                                                                          \
+  if (keep)                                                                                      \
+    fake_quant_kernel<S, O, kDelta, true, L, true><<<grid, kFqThreads, 0, st>>>(                  \
+        w, N, K, s, rs, n_s, qmax, L, out_rows, o, keep);                                         \
+  else                                                                                           \
+    fake_quant_kernel<S, O, kDelta, true, L><<<grid, kFqThreads, 0, st>>>(w, N, K, s, rs, n_s,    \
+                                                                          qmax, L, out_rows, o)
   switch (lanes) {
     case 4: AWQ_FQ_TILED(4); break;
     case 8: AWQ_FQ_TILED(8); break;
@@ -415,22 +438,49 @@ hipError_t launch_scale_table(const float* a, int64_t K, const AlphaChunk& al, f
 
 hipError_t launch_fake_quant(const void* W, awq_dtype_t dt, int64_t N, int64_t K, const float* s,
                              const float* rs, int n_s, int bits, int group, bool delta_form,
-                             bool tiled, void* out, hipStream_t st) {
+                             bool tiled, void* out, hipStream_t st, const uint8_t* keep) {
   switch (dt) {
     case AWQ_F32:
-      if (tiled) return hipErrorInvalidValue;
+      if (tiled || keep) return hipErrorInvalidValue;
       return delta_form
-                 ? fq_dispatch<float, float, true>(W, N, K, s, rs, n_s, bits, group, false, out, st)
-                 : fq_dispatch<float, float, false>(W, N, K, s, rs, n_s, bits, group, false, out, st);
+                 ? fq_dispatch<float, float, true>(W, N, K, s, rs, n_s, bits, group, false, nullptr, out, st)
+                 : fq_dispatch<float, float, false>(W, N, K, s, rs, n_s, bits, group, false, nullptr, out, st);
     case AWQ_F16:
       return delta_form
-                 ? fq_dispatch<_Float16, _Float16, true>(W, N, K, s, rs, n_s, bits, group, tiled, out, st)
-                 : fq_dispatch<_Float16, _Float16, false>(W, N, K, s, rs, n_s, bits, group, tiled, out, st);
+                 ? fq_dispatch<_Float16, _Float16, true>(W, N, K, s, rs, n_s, bits, group, tiled, keep, out, st)
+                 : fq_dispatch<_Float16, _Float16, false>(W, N, K, s, rs, n_s, bits, group, tiled, keep, out, st);
     default:
       return delta_form
-                 ? fq_dispatch<__bf16, __bf16, true>(W, N, K, s, rs, n_s, bits, group, tiled, out, st)
-                 : fq_dispatch<__bf16, __bf16, false>(W, N, K, s, rs, n_s, bits, group, tiled, out, st);
+                 ? fq_dispatch<__bf16, __bf16, true>(W, N, K, s, rs, n_s, bits, group, tiled, keep, out, st)
+                 : fq_dispatch<__bf16, __bf16, false>(W, N, K, s, rs, n_s, bits, group, tiled, keep, out, st);
   }
+}
+
+// keep[j] = 1 for the n_keep channels with the largest score (ties: lower index).
+__global__ __launch_bounds__(256) void keep_mask_kernel(const float* __restrict__ score, int64_t K,
+                                                        int64_t n_keep, uint8_t* __restrict__ keep) {
+  __shared__ float tile[1024];
+  const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const float sj = j < K ? score[j] : 0.0f;
+  int64_t rank = 0;                       // channels ranked before j
+  for (int64_t base = 0; base < K; base += 1024) {
+    const int64_t n = K - base < 1024 ? K - base : 1024;
+    __syncthreads();
+    for (int64_t i = threadIdx.x; i < n; i += blockDim.x) tile[i] = score[base + i];
+    __syncthreads();
+    for (int64_t i = 0; i < n; ++i) {
+      const float si = tile[i];
+      rank += (si > sj || (si == sj && base + i < j)) ? 1 : 0;
+    }
+  }
+  if (j < K) keep[j] = rank < n_keep ? 1 : 0;
+}
+
+hipError_t launch_keep_mask(const float* score, int64_t K, int64_t n_keep, uint8_t* keep,
+                            hipStream_t st) {
+  ProfScope p("awq_keep_mask", st);
+  keep_mask_kernel<<<(unsigned)((K + 255) / 256), 256, 0, st>>>(score, K, n_keep, keep);
+  return hipGetLastError();
 }
 
 hipError_t launch_quantize_pack(const void* W, awq_dtype_t dt, int64_t N, int64_t K,

@@ -202,3 +202,27 @@ def test_lowbit_gemv_workspace_size():
     n = awq.awq_lowbit_gemv_workspace_size(4, 4096, 4096)
     assert n > 0 and n % (4 * 4096 * 4) == 0
     assert awq.awq_lowbit_gemv_workspace_size(1, 4096, 96) == 0
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(W=NULL), -1),
+    (dict(dt=0), -2),                          # fp32 layers are not offered
+    (dict(n_keep=-1), -1),
+    (dict(n_keep=257), -1),
+    (dict(T=0), -1),
+    (dict(ws=NULL), -3),
+    (dict(ws_bytes=1024), -3),
+    (dict(bits=9), -2),
+])
+def test_salient_keep_validation(over, status):
+    a = dict(W=FAKE, X=FAKE, dt=1, N=8, K=256, T=16, score=FAKE, n_keep=2, bits=4, group=128,
+             loss=FAKE, keep=NULL, ws=ctypes.c_void_p(0x10000), ws_bytes=1 << 30, stream=NULL)
+    a.update(over)
+    assert _call("awq_salient_keep_loss", *tuple(a.values())) == status
+
+
+def test_salient_keep_workspace_extends_the_search_layout():
+    n = awq.awq_salient_keep_workspace_size(torch.float16, 4096, 4096, 4096)
+    lay = awq.awq_search_layout(torch.float16, 4096, 4096, 4096, 1, 0, 0)
+    assert n >= lay["total_bytes"] + 4096 + 4 + 4 * 4096
+    assert awq.awq_salient_keep_workspace_size(torch.float16, 0, 4096, 16) == 0
