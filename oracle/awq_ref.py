@@ -336,6 +336,95 @@ def salient_keep_loss(W: np.ndarray, X: np.ndarray, keep: np.ndarray, bits: int,
 
 
 # ---------------------------------------------------------------------------
+# Error feedback after the scaling (AWQ + GPTQ).
+# [P3] section 4: quantise one column at a time and push each column's error
+# onto the weights not yet quantised, spread according to the second-order
+# statistics of the real inputs; the three-weight example.  [P4] GPTQ:
+# column-wise quantisation, each column's error compensated into the later
+# columns with Hessian information, Cholesky preprocessing.  [P2]
+# "Experiment": AWQ's scaling and GPTQ's error compensation are
+# complementary (AWQ + GPTQ).
+# ---------------------------------------------------------------------------
+GPTQ_DAMP = 0.01
+
+
+def gptq_hessian(X: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """H = X'^T X' in fp64, X' = X diag(1/s): the inputs the scaled weights meet."""
+    Xs = np.asarray(X).astype(F64) / np.asarray(s, dtype=F32).astype(F64)[None, :]
+    return Xs.T @ Xs
+
+
+def gptq_inverse_factor(H: np.ndarray, damp: float = GPTQ_DAMP):
+    """Upper-triangular U with U^T U = (H')^-1, where H' is H with every zero
+    diagonal entry (a channel no input reaches) set to 1, plus damp times the
+    mean diagonal on the diagonal.  Returns (U, dead channels)."""
+    H = np.array(H, dtype=F64)
+    dead = np.diag(H) == 0
+    idx = np.nonzero(dead)[0]
+    H[idx, idx] = 1.0
+    H[np.diag_indices_from(H)] += damp * np.mean(np.diag(H))
+    Hinv = np.linalg.inv(H)
+    Hinv = (Hinv + Hinv.T) / 2
+    return np.linalg.cholesky(Hinv).T, dead
+
+
+def gptq_columns(Wp: np.ndarray, U: np.ndarray, quantise_column):
+    """The column loop: quantise column j (quantise_column(j, W) gives its fp64
+    value after quantisation), then move its error onto columns j+1.. with
+    row j of U.  Wp is updated in place (fp64)."""
+    K = Wp.shape[1]
+    out = np.empty_like(Wp)
+    for j in range(K):
+        q = quantise_column(j, Wp)
+        out[:, j] = q
+        err = (Wp[:, j] - q) / U[j, j]
+        Wp[:, j + 1:] -= np.outer(err, U[j, j + 1:])
+    return out
+
+
+def gptq_quantize(W: np.ndarray, X: np.ndarray, s: np.ndarray, bits: int, group: int,
+                  damp: float = GPTQ_DAMP):
+    """Codes, steps and zero-points of W diag(s) with GPTQ error feedback, in
+    quantize_pack's format.  A group's step and zero-point come from its
+    current (already corrected) weights when the loop reaches its first
+    column; each weight is rounded to fp32 and quantised in the order of
+    quantize_codes; dead channels are zeroed.  Returns (codes uint8 [N, K],
+    delta fp32 [N, K/group], zero uint8 [N, K/group])."""
+    W = np.asarray(W)
+    _check_quant_args(W, bits, group)
+    N, K = W.shape
+    s32 = np.asarray(s, dtype=F32)
+    U, dead = gptq_inverse_factor(gptq_hessian(X, s32), damp)
+    Wp = (W.astype(F32) * s32[None, :]).astype(F64)
+    Wp[:, dead] = 0.0
+    qmax = F32((1 << bits) - 1)
+    codes = np.zeros((N, K), dtype=np.uint8)
+    delta = np.zeros((N, K // group), dtype=F32)
+    zero = np.zeros((N, K // group), dtype=F32)
+
+    def quantise_column(j, Wcur):
+        g = j // group
+        if j % group == 0:
+            d, z = _group_params(Wcur[:, j:j + group].astype(F32), bits, group)
+            delta[:, g], zero[:, g] = d[:, 0], z[:, 0]
+        w = Wcur[:, j].astype(F32)
+        c = np.clip(np.rint(w / delta[:, g]) + zero[:, g], F32(0), qmax)
+        codes[:, j] = c.astype(np.uint8)
+        return ((c - zero[:, g]) * delta[:, g]).astype(F64)
+
+    gptq_columns(Wp, U, quantise_column)
+    return codes, delta, zero.astype(np.uint8)
+
+
+def gptq_fake_quant(W, X, s, bits: int, group: int, damp: float = GPTQ_DAMP) -> np.ndarray:
+    """W_hat = ((c - z) * delta) / s in fp32 from gptq_quantize's codes."""
+    codes, delta, zero = gptq_quantize(W, X, s, bits, group, damp)
+    d_full = np.repeat(delta, group, axis=1)
+    z_full = np.repeat(zero.astype(F32), group, axis=1)
+    return ((codes.astype(F32) - z_full) * d_full) / np.asarray(s, dtype=F32)[None, :]
+
+
+# ---------------------------------------------------------------------------
 # Using the packed weights: the low-bit linear layer.
 # [P2] "Tiny Chat": the inference kernel dequantises the low-bit weights on
 # the fly and never writes the dequantised copy back to memory.  [P2]

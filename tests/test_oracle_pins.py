@@ -500,3 +500,88 @@ def test_keeping_salient_activation_channels_beats_weight_magnitude():
     wgt = oracle.salient_keep_loss(Wn, Xn, by_w, 3, 128)
     assert act < 0.5 * rtn
     assert wgt > 0.8 * rtn
+
+
+# ---------------------------------------------------------------------------
+# GPTQ error feedback
+# ---------------------------------------------------------------------------
+def test_gptq_three_weight_example(golden):
+    """[P3] section 4: weights 0.34, 0.33, 0.33 meeting inputs of 1, rounded
+    to a step of 0.25 one at a time with the error carried forward: each
+    weight's value when its turn comes is 0.34, 0.42, 0.25, the results are
+    0.25, 0.50, 0.25 and the output is exactly 1.00, where rounding each on
+    its own gives 0.75.
+
+    The column loop carries the error with row j of U (U^T U = H^-1).  With
+    the calibration inputs (1,0,0), (1,1,0), (1,1,1) -- the last is the
+    page's input -- H^-1 is bidiagonal and the whole error goes to the next
+    weight, which is the page's narration step by step.  With only the
+    all-ones input (H = 1 1^T, lightly damped) the error is spread over all
+    later weights; the output is still exactly 1.00."""
+    g = golden("gptq_three_weights.txt")
+    step = g["step"]
+    rnd = lambda j, W: step * np.rint(W[:, j] / step)
+    # error carried to the next weight only
+    X = np.tril(np.ones((3, 3)))
+    U, dead = oracle.gptq_inverse_factor(X.T @ X, damp=0.0)
+    assert not dead.any()
+    seen = []
+    def q(j, W):
+        seen.append(W[0, j])
+        return rnd(j, W)
+    out = oracle.gptq_columns(np.array([g["w"]], np.float64), U, q)
+    np.testing.assert_allclose(seen, g["carried"], atol=1e-12)
+    np.testing.assert_allclose(out[0], g["expect"], atol=1e-12)
+    assert abs(out[0].sum() - g["sum"]) < 1e-12
+    # the all-ones input alone
+    x = np.ones((1, 3))
+    U1, _ = oracle.gptq_inverse_factor(x.T @ x, damp=1e-6)
+    out1 = oracle.gptq_columns(np.array([g["w"]], np.float64), U1, rnd)
+    assert abs(out1[0].sum() - g["sum"]) < 1e-9
+    assert abs(oracle.round_to_step(g["w"], step).sum() - g["independent_sum"]) < 1e-12
+
+
+def test_gptq_inverse_factor_is_the_cholesky_of_the_inverse():
+    rng = np.random.default_rng(4)
+    X = rng.standard_normal((50, 12))
+    H = X.T @ X
+    U, dead = oracle.gptq_inverse_factor(H, damp=0.0)
+    assert not dead.any()
+    np.testing.assert_allclose(U.T @ U, np.linalg.inv(H), rtol=1e-9, atol=1e-12)
+    assert np.allclose(U, np.triu(U)) and np.all(np.diag(U) > 0)
+
+
+def test_gptq_with_uncorrelated_inputs_is_rtn():
+    """With H diagonal there is nothing to compensate: every off-diagonal of U
+    is zero, so GPTQ's codes are exactly round-to-nearest's."""
+    W, _ = random_layer(12, 16, 256, 1, dtype="fp16")
+    Wn = to_numpy(W).astype(np.float32)
+    X = np.zeros((256, 256))
+    X[np.arange(256), np.arange(256)] = np.linspace(0.5, 2.0, 256)   # orthogonal columns
+    s = np.ones(256, np.float32)
+    c, d, z = oracle.gptq_quantize(Wn, X, s, 4, 128)
+    c_ref, d_ref, z_ref = oracle.quantize_codes(Wn, s, 4, 128)
+    np.testing.assert_array_equal(c, c_ref)
+    np.testing.assert_array_equal(d, d_ref)
+    np.testing.assert_array_equal(z, z_ref)
+
+
+def test_gptq_lowers_the_output_error_and_complements_awq():
+    """[P2] "Experiment" (qualitative, parity unpinned for the page's
+    perplexities): on correlated inputs GPTQ's error feedback lowers the
+    layer's output error below round-to-nearest, and applied after AWQ's
+    scaling it lowers AWQ's error further."""
+    rng = np.random.default_rng(5)
+    W, X = random_layer(13, 64, 256, 512, dtype="fp16", outlier_factor=20.0)
+    Wn, Xn = to_numpy(W).astype(np.float32), to_numpy(X).astype(np.float64)
+    mix = np.eye(256) + 0.3 * rng.standard_normal((256, 256)) / 16     # correlate the channels
+    Xc = (Xn @ mix).astype(np.float32)
+    ones = np.ones(256, np.float32)
+    rtn = oracle.output_loss(Wn, Xc, oracle.fake_quant(Wn, ones, 3, 128))
+    gptq = oracle.output_loss(Wn, Xc, oracle.gptq_fake_quant(Wn, Xc, ones, 3, 128))
+    res = oracle.search(Wn, Xc, 3, 128)
+    s_best = res["s_best"]
+    awq = res["losses"][res["best"]]
+    both = oracle.output_loss(Wn, Xc, oracle.gptq_fake_quant(Wn, Xc, s_best, 3, 128))
+    assert gptq < 0.8 * rtn
+    assert both < awq
