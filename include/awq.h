@@ -286,6 +286,44 @@ awq_status_t awq_lowbit_gemv(const void* X, awq_dtype_t x_dtype, int64_t M, int6
                              hipStream_t stream);
 
 /* ------------------------------------------------------------------------ *
+ * GPTQ error feedback after the scaling (AWQ + GPTQ).  [P3] section 4: the
+ * weights are rounded one column at a time and each column's rounding error
+ * is moved onto the columns not yet rounded, weighted by the second-order
+ * statistics of real inputs; [P4] GPTQ section: Hessian-guided compensation
+ * column by column with a Cholesky factorisation done once; [P2]
+ * "Experiment": AWQ's scaling and GPTQ's compensation are complementary.
+ *
+ * Operates on W' = W diag(s) with inputs X' = X diag(s)^-1 (s [K] fp32
+ * device; s = 1 gives plain GPTQ):
+ *   H = X'^T X' (fp64); channels with H[j][j] = 0 get H[j][j] = 1 and W'[:, j]
+ *   = 0; then damp * mean(diag H) is added to the diagonal (damp >= 0, e.g.
+ *   0.01; with damp = 0 and a singular H the result is undefined);
+ *   U upper triangular with U^T U = H^-1 (fp64);
+ *   for j = 0 .. K-1, every row independently: at the first column of a
+ *   group, its step and zero-point come from the group's current values
+ *   (fp64 rounded to fp32) exactly as in awq_quantize_pack; the current
+ *   value is rounded to fp32 and quantised the same way, q = (c - z) delta;
+ *   e = (w_j - q) / U[j][j] and w_k -= e U[j][k] for k > j (fp64).
+ * Outputs in awq_quantize_pack's format: codes_out uint32 [N, bits*K/32],
+ * scales_out fp32 [N, K/group], zeros_out uint8 [N, K/group] (device).
+ * W and X of dtype; K <= 32768.  Workspace: awq_gptq_workspace_size(N, K, T)
+ * bytes, 256-byte aligned.  After the call the workspace begins with the
+ * factor matrix, fp64 with leading dimension awq_gptq_factor_ld(K) (K rounded
+ * up to 128): its upper triangle (column >= row) over the first K rows and
+ * columns holds U; the rest is scratch.
+ * Arithmetic: H, the factorisation and the error updates run in fp64 (MFMA
+ * and FMA), so codes agree with any exact-arithmetic GPTQ except where a
+ * current value lies within fp64 rounding of a quantisation boundary.
+ * ------------------------------------------------------------------------ */
+size_t awq_gptq_workspace_size(int64_t N, int64_t K, int64_t T);
+int64_t awq_gptq_factor_ld(int64_t K);
+awq_status_t awq_gptq_quantize(const void* W, const void* X, awq_dtype_t dtype, int64_t N,
+                               int64_t K, int64_t T, const float* s, int bits, int group,
+                               double damp, uint32_t* codes_out, float* scales_out,
+                               uint8_t* zeros_out, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/* ------------------------------------------------------------------------ *
  * Kernel timing.  While enabled, every kernel the library launches (or, after
  * awq_profile_select(prefix), every kernel whose name starts with prefix) is
  * bracketed by a pair of HIP events on its stream; each event pair adds a few
@@ -295,7 +333,9 @@ awq_status_t awq_lowbit_gemv(const void* X, awq_dtype_t x_dtype, int64_t M, int6
  * awq_act_stats_partial, awq_act_stats_finish, awq_scale_table, awq_tile_rows,
  * awq_fake_quant, awq_gemm_ref_output, awq_gemm_sse, awq_loss_argmin,
  * awq_quantize_pack, awq_keep_mask, awq_lowbit_repack, awq_lowbit_gemv,
- * awq_lowbit_reduce.
+ * awq_lowbit_reduce.  GPTQ is timed by phase, one event pair around all the
+ * launches of each: awq_gptq_hessian, awq_gptq_prep, awq_gptq_cholesky,
+ * awq_gptq_inverse, awq_gptq_columns, awq_gptq_pack.
  * awq_profile_reset() drops the records.  Thread-safe.
  * ------------------------------------------------------------------------ */
 awq_status_t awq_profile_enable(int enable);

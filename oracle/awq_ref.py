@@ -383,18 +383,25 @@ def gptq_columns(Wp: np.ndarray, U: np.ndarray, quantise_column):
 
 
 def gptq_quantize(W: np.ndarray, X: np.ndarray, s: np.ndarray, bits: int, group: int,
-                  damp: float = GPTQ_DAMP):
+                  damp: float = GPTQ_DAMP, trace: dict | None = None):
     """Codes, steps and zero-points of W diag(s) with GPTQ error feedback, in
     quantize_pack's format.  A group's step and zero-point come from its
     current (already corrected) weights when the loop reaches its first
     column; each weight is rounded to fp32 and quantised in the order of
     quantize_codes; dead channels are zeroed.  Returns (codes uint8 [N, K],
-    delta fp32 [N, K/group], zero uint8 [N, K/group])."""
+    delta fp32 [N, K/group], zero uint8 [N, K/group]).  With trace = {} it
+    also receives "U", "dead" and, per weight, "pre" (its fp64 value when
+    quantised) and "group_vals" (its fp64 value when its group's range was
+    taken)."""
     W = np.asarray(W)
     _check_quant_args(W, bits, group)
     N, K = W.shape
     s32 = np.asarray(s, dtype=F32)
     U, dead = gptq_inverse_factor(gptq_hessian(X, s32), damp)
+    if trace is not None:
+        trace["U"], trace["dead"] = U, dead
+        trace["pre"] = np.empty((N, K))
+        trace["group_vals"] = np.empty((N, K))
     Wp = (W.astype(F32) * s32[None, :]).astype(F64)
     Wp[:, dead] = 0.0
     qmax = F32((1 << bits) - 1)
@@ -404,7 +411,11 @@ def gptq_quantize(W: np.ndarray, X: np.ndarray, s: np.ndarray, bits: int, group:
 
     def quantise_column(j, Wcur):
         g = j // group
+        if trace is not None:
+            trace["pre"][:, j] = Wcur[:, j]
         if j % group == 0:
+            if trace is not None:
+                trace["group_vals"][:, j:j + group] = Wcur[:, j:j + group]
             d, z = _group_params(Wcur[:, j:j + group].astype(F32), bits, group)
             delta[:, g], zero[:, g] = d[:, 0], z[:, 0]
         w = Wcur[:, j].astype(F32)

@@ -21,6 +21,9 @@ __all__ = [
     "AWQ_FQ_WEIGHT_DELTA",
     "awq_version", "awq_act_stats", "awq_act_stats_workspace_size", "awq_scale_table",
     "awq_fake_quant", "awq_search_layout", "awq_search_scales", "awq_quantize_pack",
+    "awq_salient_keep_workspace_size", "awq_salient_keep_loss", "awq_lowbit_repack",
+    "awq_lowbit_gemv_workspace_size", "awq_lowbit_gemv", "awq_gptq_workspace_size",
+    "awq_gptq_factor_ld", "awq_gptq_quantize",
     "awq_profile_enable", "awq_profile_select", "awq_profile_read", "awq_profile_reset",
     "packed_words_per_row",
 ]
@@ -87,6 +90,10 @@ _SIGS = {
     "awq_lowbit_repack": ([_P, _P, _P, _I64, _I64, _I32, _I32, _P, _P, _P], _I32),
     "awq_lowbit_gemv_workspace_size": ([_I64, _I64, _I64], _SZ),
     "awq_lowbit_gemv": ([_P, _I32, _I64, _I64, _P, _P, _I64, _I32, _I32, _P, _P, _SZ, _P], _I32),
+    "awq_gptq_workspace_size": ([_I64, _I64, _I64], _SZ),
+    "awq_gptq_factor_ld": ([_I64], _I64),
+    "awq_gptq_quantize": ([_P, _P, _I32, _I64, _I64, _I64, _P, _I32, _I32, _D, _P, _P, _P, _P, _SZ,
+                           _P], _I32),
     "awq_profile_enable": ([_I32], _I32),
     "awq_profile_select": ([ctypes.c_char_p], _I32),
     "awq_profile_read": ([ctypes.c_char_p, ctypes.POINTER(_I64), ctypes.POINTER(_D)], _I32),
@@ -273,6 +280,41 @@ def awq_salient_keep_loss(W: torch.Tensor, X: torch.Tensor, score: torch.Tensor,
                                            keep.data_ptr(), ws.data_ptr(), ws.numel(),
                                            _stream(W.device)))
     return (loss, keep, ws) if return_workspace else (loss, keep)
+
+
+def awq_gptq_workspace_size(N: int, K: int, T: int) -> int:
+    return int(library().awq_gptq_workspace_size(N, K, T))
+
+
+def awq_gptq_factor_ld(K: int) -> int:
+    return int(library().awq_gptq_factor_ld(K))
+
+
+def awq_gptq_quantize(W: torch.Tensor, X: torch.Tensor, s: torch.Tensor, bits: int, group: int,
+                      damp: float = 0.01, return_workspace: bool = False,
+                      workspace: torch.Tensor | None = None):
+    """GPTQ with error feedback on W diag(s) -> (codes int32 [N, bits*K/32],
+    scales fp32 [N, K/group], zeros uint8 [N, K/group]) and, on request, the
+    workspace (it begins with the fp64 factor matrix holding U)."""
+    _dev(W, "W")
+    _dev(X, "X")
+    _dev(s, "s")
+    N, K = W.shape
+    T = X.shape[0]
+    if X.dtype != W.dtype or X.shape[1] != K:
+        raise ValueError("W [N, K] and X [T, K] must share K and dtype")
+    codes = torch.empty((N, bits * K // 32), dtype=torch.int32, device=W.device)
+    scales = torch.empty((N, K // group), dtype=torch.float32, device=W.device)
+    zeros = torch.empty((N, K // group), dtype=torch.uint8, device=W.device)
+    if workspace is None:
+        workspace = torch.empty(max(1, awq_gptq_workspace_size(N, K, T)), dtype=torch.uint8,
+                                device=W.device)
+    _check(library().awq_gptq_quantize(W.data_ptr(), X.data_ptr(), _dtype(W), N, K, T,
+                                       s.data_ptr(), bits, group, float(damp), codes.data_ptr(),
+                                       scales.data_ptr(), zeros.data_ptr(), workspace.data_ptr(),
+                                       workspace.numel(), _stream(W.device)))
+    out = (codes, scales, zeros)
+    return out + (workspace,) if return_workspace else out
 
 
 def awq_lowbit_repack(codes: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor, K: int,

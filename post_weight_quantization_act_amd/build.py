@@ -29,8 +29,11 @@ COMMON = [
 PER_FILE = {
     "quant.hip": ["-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
                   "-fno-gpu-flush-denormals-to-zero", "-fno-honor-nans"],
+    # Same quantiser rules; the fp64 updates ask for their FMAs explicitly.
+    "gptq.hip": ["-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
+                 "-fno-gpu-flush-denormals-to-zero"],
 }
-SOURCES = ["act_stats.hip", "quant.hip", "gemm_sse.hip", "lowbit.hip", "awq_api.cpp"]
+SOURCES = ["act_stats.hip", "quant.hip", "gemm_sse.hip", "lowbit.hip", "gptq.hip", "awq_api.cpp"]
 
 
 def hipcc() -> str:

@@ -36,6 +36,7 @@ awq_status_t hip_fail(hipError_t e, const char* what) {
 
 constexpr uint64_t kMaxBufferBytes = 0xFFFFFF00ull;  // byte offsets inside kernels are 32-bit
 constexpr int kMaxAlpha = 4096;
+constexpr int64_t kGptqMaxK = 32768;   // the fp64 factor matrix is K^2 * 8 bytes
 
 int esize(awq_dtype_t dt) { return dt == AWQ_F32 ? 4 : 2; }
 
@@ -415,6 +416,46 @@ awq_status_t awq_salient_keep_loss(const void* W, const void* X, awq_dtype_t dty
   e = awq::launch_loss_argmin(partials, 1, tiles, 1.0 / ((double)T * (double)N), s_table, K,
                               loss_out, best, s_copy, stream);
   if (e != hipSuccess) return hip_fail(e, "loss launch");
+  return AWQ_OK;
+  AWQ_GUARD_END
+}
+
+// ---------------------------------------------------------------------------
+// GPTQ error feedback after the scaling.
+// ---------------------------------------------------------------------------
+size_t awq_gptq_workspace_size(int64_t N, int64_t K, int64_t T) {
+  if (N < 1 || K < 1 || T < 1) return 0;
+  return awq::gptq_layout(N, K, T).bytes;
+}
+
+int64_t awq_gptq_factor_ld(int64_t K) { return K < 1 ? 0 : awq::gptq_layout(1, K, 1).Kp; }
+
+awq_status_t awq_gptq_quantize(const void* W, const void* X, awq_dtype_t dtype, int64_t N,
+                               int64_t K, int64_t T, const float* s, int bits, int group,
+                               double damp, uint32_t* codes_out, float* scales_out,
+                               uint8_t* zeros_out, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+  AWQ_GUARD_BEGIN
+  awq_status_t st = check_quant_args(dtype, N, K, bits, group);
+  if (st != AWQ_OK) return st;
+  if (T < 1) return fail(AWQ_ERR_INVALID_ARG, "T must be >= 1");
+  if (K > kGptqMaxK) return fail(AWQ_ERR_UNSUPPORTED, "K=%lld above %lld", (long long)K,
+                                 (long long)kGptqMaxK);
+  if (!(damp >= 0.0) || !std::isfinite(damp))
+    return fail(AWQ_ERR_INVALID_ARG, "damp must be finite and >= 0");
+  if (!W || !X || !s || !codes_out || !scales_out || !zeros_out)
+    return fail(AWQ_ERR_INVALID_ARG, "null pointer");
+  if (!aligned(W, esize(dtype)) || !aligned(X, esize(dtype)) || !aligned(s, 4) ||
+      !aligned(codes_out, 4) || !aligned(scales_out, 4))
+    return fail(AWQ_ERR_UNSUPPORTED, "W, X element-aligned; s, codes, scales 4-byte aligned");
+  if (!workspace) return fail(AWQ_ERR_WORKSPACE, "null workspace");
+  if (!aligned(workspace, 256)) return fail(AWQ_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  const size_t need = awq::gptq_layout(N, K, T).bytes;
+  if (workspace_bytes < need)
+    return fail(AWQ_ERR_WORKSPACE, "workspace of %zu bytes is below %zu", workspace_bytes, need);
+  hipError_t e = awq::launch_gptq(W, X, dtype, N, K, T, s, bits, group, damp, codes_out,
+                                  scales_out, zeros_out, workspace, stream);
+  if (e != hipSuccess) return hip_fail(e, "gptq launch");
   return AWQ_OK;
   AWQ_GUARD_END
 }

@@ -109,6 +109,23 @@ hipError_t launch_lowbit_gemv(const void* X, awq_dtype_t dt, int64_t M, int64_t 
                               const uint32_t* codes_t, const void* meta_t, int64_t N, int bits,
                               int group, float* Y, void* ws, hipStream_t st);
 
+// gptq.hip: GPTQ error feedback after the scaling (all fp64 but the quantiser)
+struct GptqLayout {
+  int64_t Kp;          // K rounded up to 128: leading dimension of the factor matrix
+  int chunk_rows;      // calibration rows per Hessian chunk (a multiple of 16)
+  size_t h_off;        // fp64 [Kp][Kp]: reversed H -> L -> L^-1 -> U (upper triangle)
+  size_t xc_off;       // fp64 [chunk_rows][Kp]: one chunk of reversed X diag(s)^-1
+  size_t wc_off;       // fp64 [N][K]: current scaled weights
+  size_t err_off;      // fp64 [N][64]: one block's scaled errors
+  size_t codes_off;    // uint8 [N][K]: codes before packing
+  size_t dead_off;     // uint8 [K]: channels no calibration input reaches
+  size_t bytes;
+};
+GptqLayout gptq_layout(int64_t N, int64_t K, int64_t T);
+hipError_t launch_gptq(const void* W, const void* X, awq_dtype_t dt, int64_t N, int64_t K,
+                       int64_t T, const float* s, int bits, int group, double damp,
+                       uint32_t* codes, float* scales, uint8_t* zeros, void* ws, hipStream_t st);
+
 // gemm_sse.hip
 enum class Epi { kStore = 0, kSseRef = 1, kSseDelta = 2 };
 struct GemmTiles {

@@ -226,3 +226,37 @@ def test_salient_keep_workspace_extends_the_search_layout():
     lay = awq.awq_search_layout(torch.float16, 4096, 4096, 4096, 1, 0, 0)
     assert n >= lay["total_bytes"] + 4096 + 4 + 4 * 4096
     assert awq.awq_salient_keep_workspace_size(torch.float16, 0, 4096, 16) == 0
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(W=NULL), -1),
+    (dict(T=0), -1),
+    (dict(bits=1), -2),
+    (dict(group=48), -2),
+    (dict(K=200), -1),                         # K % group != 0
+    (dict(K=32768 + 128), -2),                 # factor matrix limit
+    (dict(damp=-0.5), -1),
+    (dict(damp=float("nan")), -1),
+    (dict(ws=NULL), -3),
+    (dict(ws_bytes=1024), -3),
+    (dict(ws=ctypes.c_void_p(0x10010)), -3),   # workspace not 256-byte aligned
+    (dict(s=ctypes.c_void_p(0x1002)), -2),     # s not 4-byte aligned
+])
+def test_gptq_validation(over, status):
+    a = dict(W=FAKE, X=FAKE, dt=1, N=8, K=256, T=16, s=FAKE, bits=4, group=128, damp=0.01,
+             codes=FAKE, scales=FAKE, zeros=FAKE, ws=ctypes.c_void_p(0x10000),
+             ws_bytes=1 << 40, stream=NULL)
+    a.update(over)
+    assert _call("awq_gptq_quantize", *tuple(a.values())) == status
+
+
+def test_gptq_workspace_layout():
+    # the factor matrix (K rounded up to 128, fp64) comes first and the scaled
+    # weights (fp64 [N, K]) are among the rest
+    assert awq.awq_gptq_factor_ld(4096) == 4096
+    assert awq.awq_gptq_factor_ld(96) == 128
+    assert awq.awq_gptq_factor_ld(640) == 640
+    n = awq.awq_gptq_workspace_size(4096, 4096, 4096)
+    assert n >= 4096 * 4096 * 8 * 2 + 4096 * 4096
+    assert awq.awq_gptq_workspace_size(0, 4096, 16) == 0
+    assert awq.awq_gptq_workspace_size(8, 96, 1) >= 128 * 128 * 8
