@@ -48,6 +48,10 @@ def parse():
                         "synthetic layers: output error with the top 1%% channels kept at full "
                         "precision (ranked by activation, by weight) against round-to-nearest "
                         "and the AWQ search, and the time of one ablation evaluation")
+    p.add_argument("--gptq", action="store_true",
+                   help="instead of the search, time GPTQ error feedback after the scaling "
+                        "(awq_gptq_quantize with the AWQ scales of alpha = 0.5) on the synthetic "
+                        "layers, phase by phase")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 1 GiB fp32 device copy (torch.neg into a second "
                         "buffer) three times: the known-size reference for HBM byte counters")
@@ -185,6 +189,106 @@ def bench_salient(args) -> None:
         "layers": out}), flush=True)
 
 
+GPTQ_PHASES = ("awq_gptq_hessian", "awq_gptq_prep", "awq_gptq_cholesky", "awq_gptq_inverse",
+               "awq_gptq_columns", "awq_gptq_pack")
+
+
+def gptq_cpu_baseline(spec, W, X, s) -> dict:
+    """The oracle's GPTQ as it is: H and the factor once, the column loop on 64
+    rows; the layer's time is the factor time plus the loop time scaled to
+    every row (rows are independent given U)."""
+    import numpy as np
+
+    import oracle
+    from datagen import to_numpy
+
+    Wn, Xn = to_numpy(W).astype(np.float32), to_numpy(X)
+    t0 = time.perf_counter()
+    oracle.gptq_inverse_factor(oracle.gptq_hessian(Xn, s))
+    t_factor = time.perf_counter() - t0
+    rows = 64
+    t0 = time.perf_counter()
+    oracle.gptq_quantize(Wn[:rows], Xn, s, spec.bits, spec.group)   # refactors, then the loop
+    t_loop = max(time.perf_counter() - t0 - t_factor, 1e-6)
+    layer_s = t_factor + t_loop * spec.N / rows
+    return {"value": 1.0 / layer_s, "unit": "layers/s", "cores": len(os.sched_getaffinity(0)),
+            "kind": "oracle",
+            "sample": f"H and the factorisation once ({t_factor:.2f} s), the column loop on "
+                      f"{rows} of {spec.N} rows ({t_loop:.2f} s) scaled to all rows: "
+                      f"{layer_s:.1f} s per layer"}
+
+
+def bench_gptq(args) -> None:
+    """GPTQ with error feedback on the AWQ-scaled weights: one awq_gptq_quantize
+    call per step (Hessian of the scaled calibration inputs, damping, Cholesky,
+    triangular inverse, the column loop, packing), timed with events; then one
+    more call with an event pair around each phase."""
+    import numpy as np
+    import torch
+
+    import post_weight_quantization_act_amd as awq
+    from datagen import CONFIGS, make_layer
+
+    dev = torch.device("cuda", 0)
+    out = []
+    for name in ("llama7b-qproj", "llama7b-upgate", "70b-mlp"):
+        spec = CONFIGS[name]
+        W, X = make_layer(spec)
+        Wd, Xd = W.to(dev), X.to(dev)
+        N, K, T = spec.N, spec.K, spec.T
+        a = awq.awq_act_stats(Xd)
+        s = torch.pow(torch.clamp(a, min=1e-8).double(), 0.5).float()
+        ws = torch.empty(awq.awq_gptq_workspace_size(N, K, T), dtype=torch.uint8, device=dev)
+        run = lambda: awq.awq_gptq_quantize(Wd, Xd, s, spec.bits, spec.group, 0.01, workspace=ws)
+        steps = max(1, args.steps // 10) if name == "llama7b-qproj" else 2
+        for _ in range(max(1, min(args.warmup, 3))):
+            run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        awq.awq_profile_reset()
+        awq.awq_profile_select("awq_gptq")
+        awq.awq_profile_enable(True)
+        run()
+        torch.cuda.synchronize()
+        awq.awq_profile_enable(False)
+        phases = {p[len("awq_gptq_"):]: awq.awq_profile_read(p)[1] for p in GPTQ_PHASES}
+        awq.awq_profile_reset()
+        Tpad = -(-T // 16) * 16
+        flops_h = float(T) * K * (K + 1)             # the distinct entries of X'^T X'
+        rec = {"layer": name, "N": N, "K": K, "T": T, "bits": spec.bits, "ms_per_layer": ms,
+               "phases_ms": phases,
+               "hessian_tflops": flops_h / (phases["hessian"] * 1e-3) / 1e12,
+               "cholesky_inverse_tflops": (2.0 * K ** 3 / 3) /
+                                          ((phases["cholesky"] + phases["inverse"]) * 1e-3) / 1e12,
+               "update_tflops": float(N) * K * K / (phases["columns"] * 1e-3) / 1e12}
+        if name == "llama7b-qproj" and not args.no_cpu_baseline:
+            rec["cpu_baseline"] = gptq_cpu_baseline(spec, W, X, s.cpu().numpy())
+        out.append(rec)
+        del W, X, Wd, Xd, ws
+        torch.cuda.empty_cache()
+    head = out[0]
+    line = {
+        "metric": "GPTQ with error feedback after the AWQ scaling: layers per second",
+        "value": 1e3 / head["ms_per_layer"], "unit": "layers/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "higher_is_better": True, "dtype": "f64",
+        "data": "synthetic",
+        "config": {"workload": "llama-7b q_proj (W fp16 4096x4096, X 4096 tokens, INT4 g128), "
+                               "AWQ scales of alpha 0.5, damping 0.01"},
+        "roofline": {"bound": "mfma", "achieved": head["hessian_tflops"], "peak": 78.6,
+                     "unit": "TFLOP/s", "frac": head["hessian_tflops"] / 78.6, "traffic": None,
+                     "kernel": "Hessian X'^T X' (fp64 MFMA), phase time"},
+        "layers": out}
+    if "cpu_baseline" in head:
+        line["cpu_baseline"] = head["cpu_baseline"]
+    print(json.dumps(line), flush=True)
+
+
 def kernel_source_hash() -> str:
     """Hash of the candidate GEMM's source, the kernel the traffic figure belongs to."""
     h = hashlib.sha256()
@@ -252,6 +356,9 @@ def main():
         return
     if args.salient:
         bench_salient(args)
+        return
+    if args.gptq:
+        bench_gptq(args)
         return
     import numpy as np
     import torch

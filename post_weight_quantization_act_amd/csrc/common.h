@@ -32,6 +32,20 @@ template <> __device__ __forceinline__ float from_f32<float>(float x) { return x
 template <> __device__ __forceinline__ _Float16 from_f32<_Float16>(float x) { return (_Float16)x; }
 template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return (__bf16)x; }
 
+// RN(a/b) from y = RN(1/b) in 5 fp32 operations (Markstein: after the first
+// correction q is within an ulp of a/b, so the residual a - b q is exact and
+// the second correction rounds correctly).  Needs the intermediate values
+// normal, which holds for the quantiser's quotients (b = delta >= 1e-10, and
+// a quotient small enough to be at risk only ever feeds rint).  Callers must
+// be compiled without contraction so that a * y is one rounding.
+__device__ __forceinline__ float div_rn(float a, float b, float y) {
+  float q = a * y;
+  float r = fmaf(-b, q, a);
+  q = fmaf(r, y, q);
+  r = fmaf(-b, q, a);
+  return fmaf(r, y, q);
+}
+
 // ---- tiled operand layout of the MFMA GEMM --------------------------------------
 // fp16/bf16 GEMM operands are stored tile by tile so that every global -> LDS
 // transfer of the GEMM is a contiguous 1 KB block holding whole 128-byte lines:
@@ -116,7 +130,7 @@ struct GptqLayout {
   size_t h_off;        // fp64 [Kp][Kp]: reversed H -> L -> L^-1 -> U (upper triangle)
   size_t xc_off;       // fp64 [chunk_rows][Kp]: one chunk of reversed X diag(s)^-1
   size_t wc_off;       // fp64 [N][K]: current scaled weights
-  size_t err_off;      // fp64 [N][64]: one block's scaled errors
+  size_t err_off;      // fp64 [N][512]: one super-block's scaled errors
   size_t codes_off;    // uint8 [N][K]: codes before packing
   size_t dead_off;     // uint8 [K]: channels no calibration input reaches
   size_t bytes;

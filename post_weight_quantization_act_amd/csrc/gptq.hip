@@ -21,8 +21,10 @@
 // damping, a right-looking blocked Cholesky (64-wide panels), a bottom-up
 // recursive inverse of L (every level two batched GEMMs), one in-place
 // reversal that turns L^-1 into U, then the column loop in blocks of 64
-// columns (one kernel, lane = weight row) with the block's error pushed to the
-// later columns by one MFMA GEMM per block.
+// columns (one kernel, lane = weight row).  Errors are pushed on lazily, as
+// GPTQ's batched updates do: each block's errors go at once to the rest of
+// its 512-column super-block (a shallow GEMM), and every super-block's errors
+// go to the columns beyond it in one deep GEMM.
 //
 // Every dense contraction runs on the fp64 MFMA (v_mfma_f64_16x16x4f64):
 // a 64x64 or 128x128 tile per 256-thread workgroup, 2x2 waves, k staged
@@ -47,6 +49,11 @@ constexpr int kKS = 16;            // k depth of one LDS stage
 constexpr int kPad = 16;           // LDS row padding (doubles): rows 128 B off the banks
 constexpr int kThreads = 256;
 constexpr float kDeltaMin = 1e-10f;
+// Columns whose errors are pushed on lazily: inside a super-block of kSuper
+// columns every 64-column block updates the rest of the super-block at once;
+// the columns beyond it are updated once per super-block, by one deep GEMM.
+// A multiple of every group size, so a group never straddles two.
+constexpr int kSuper = 512;
 
 // Tile jobs of the fp64 GEMM.  C(m, n) = alpha sum_k A(m, k) B(n, k) + beta C(m, n).
 enum Map : int {
@@ -319,27 +326,30 @@ __global__ __launch_bounds__(kThreads) void damp_kernel(double* __restrict__ H, 
 // One wave; lane r owns row r of the 64x64 block (lower part read only).  The
 // factor L_pp itself is never needed again (the panel below is solved with
 // its inverse, the later updates use the solved panel), so the block is
-// overwritten with L_pp^-1 (zeros above the diagonal).
+// overwritten with L_pp^-1 (zeros above the diagonal).  Both halves are
+// right-looking, so the dependent chain per column is short and the updates
+// of the later entries are independent FMAs.
 __global__ __launch_bounds__(64) void chol_diag_kernel(double* __restrict__ H, int64_t ld, int p) {
   __shared__ double col[kNb];
+  __shared__ double rdiag[kNb];
   __shared__ double Ls[kNb][kNb + 1];
   const int r = threadIdx.x;
   double* blk = H + (int64_t)p * kNb * ld + (int64_t)p * kNb;
   double a[kNb];
 #pragma unroll
   for (int k = 0; k < kNb; ++k) a[k] = k <= r ? blk[(int64_t)r * ld + k] : 0.0;
-  // right-looking: column j is scaled, then every later column updated
+  // factorisation: column j is scaled by 1 / L_jj, then every later column updated
 #pragma unroll
   for (int j = 0; j < kNb; ++j) {
-    if (r == j) col[j] = sqrt(a[j]);
-    __syncthreads();
-    const double d = col[j];
+    if (r == j) {
+      const double d = sqrt(a[j]);
+      a[j] = d;
+      rdiag[j] = 1.0 / d;
+    }
     __syncthreads();
     if (r > j) {
-      a[j] = a[j] / d;
+      a[j] *= rdiag[j];
       col[r] = a[j];
-    } else if (r == j) {
-      a[j] = d;
     }
     __syncthreads();
     if (r > j) {
@@ -352,18 +362,17 @@ __global__ __launch_bounds__(64) void chol_diag_kernel(double* __restrict__ H, i
 #pragma unroll
   for (int k = 0; k < kNb; ++k) Ls[r][k] = k <= r ? a[k] : 0.0;
   __syncthreads();
-  // inverse: lane c solves L x = e_c by forward substitution
+  // inverse: lane c solves L x = e_c, each x_i pushed into the later rows at once
   const int c = r;
-  double x[kNb];
+  double acc[kNb], x[kNb];
+#pragma unroll
+  for (int i = 0; i < kNb; ++i) acc[i] = 0.0;
 #pragma unroll
   for (int i = 0; i < kNb; ++i) {
-    double s = 0.0;
+    x[i] = ((i == c ? 1.0 : 0.0) - acc[i]) * rdiag[i];
 #pragma unroll
-    for (int k = 0; k < i; ++k) s = fma(Ls[i][k], x[k], s);
-    const double lii = Ls[i][i];
-    x[i] = i < c ? 0.0 : (i == c ? 1.0 / lii : -s / lii);
+    for (int m = i + 1; m < kNb; ++m) acc[m] = fma(Ls[m][i], x[i], acc[m]);
   }
-  // write column c of the inverse
 #pragma unroll
   for (int i = 0; i < kNb; ++i) blk[(int64_t)i * ld + c] = x[i];
 }
@@ -401,36 +410,41 @@ __global__ void scaled_weights_kernel(const S* __restrict__ W, const float* __re
 }
 
 // ---- the column loop over one block of 64 columns --------------------------------
-// Lane = weight row.  The block's 64 current values live in registers; the
-// row of U used at column j is wave-uniform (scalar loads).  A group's step
-// and zero-point come from its current values when the loop reaches its first
-// column: inside the block for groups of at most 64 columns, else from this
-// block's registers and the later columns in Wc (which already carry every
-// earlier block's error).  Quantiser in IEEE fp32, one rounding per operation:
+// Lane = weight row.  The block's 64 current values live in registers and the
+// block's 64 x 64 piece of U is staged in LDS once (every lane reads the same
+// U entries: broadcasts), so the only latency left per column is the
+// quantiser's short dependent chain.  A group's step and zero-point come from
+// its current values when the loop reaches its first column: inside the block
+// for groups of at most 64 columns, else from this block's registers and the
+// later columns in Wc (which already carry every earlier error).  Quantiser
+// in IEEE fp32, one rounding per operation, quotients correctly rounded
+// (div_rn with the reciprocal taken once per group):
 //   delta = max((mx - mn) / qmax, 1e-10), z = clamp(rint(-mn / delta)),
 //   c = clamp(rint(w / delta) + z), q = (c - z) * delta,
-// with w, mn, mx the fp64 current values rounded to fp32.
+// with w, mn, mx the fp64 current values rounded to fp32.  The fp64 error
+// (w - q) / U[j][j] is formed with the reciprocal of U[j][j].
 struct BlockState {
   double w[64];            // current values of the block's columns
-  float delta, z, qmax;
+  float delta, rdelta, z, qmax, rq;
   uint64_t pack8;          // codes of the current 8 columns
   d2 epair;                // errors of the current 2 columns
   bool valid;
-  int ncols, c0;
-  int64_t row, K, ng, ldu;
+  int ncols, c0, gw;        // gw: the group width
+  int64_t row, K, ng;
   const double* wr;        // this row's block in Wc
-  const double* Ub;        // U[c0][c0]
+  const double (*us)[64];  // the block of U in LDS
   float* scales;
   uint8_t* zeros;
   uint8_t* codes8;
-  double* err;
+  double* err;             // this row-block's errors, row stride lde
+  int64_t lde;
 };
 
 // Column J of the block (J a compile-time index, so w stays in registers).
 template <int G, int J>
 __device__ __forceinline__ void column_step(BlockState& b) {
   if (J < b.ncols) {
-    const bool gstart = G <= 64 ? (J % G == 0) : (J == 0 && b.c0 % G == 0);
+    const bool gstart = G <= 64 ? (J % G == 0) : (J == 0 && b.c0 % b.gw == 0);
     if (gstart) {
       double mn = b.w[J], mx = b.w[J];
       constexpr int in_regs = G <= 64 ? G : 64 - J;
@@ -440,27 +454,31 @@ __device__ __forceinline__ void column_step(BlockState& b) {
         mx = fmax(mx, b.w[J + k]);
       }
       if (G > 64 && b.valid) {
-        for (int k = 64; k < G; ++k) {
+#pragma unroll 8
+        for (int k = 64; k < b.gw; ++k) {
           const double v = b.wr[k];
           mn = fmin(mn, v);
           mx = fmax(mx, v);
         }
       }
       const float mn32 = (float)mn, mx32 = (float)mx;
-      b.delta = fmaxf((mx32 - mn32) / b.qmax, kDeltaMin);
-      b.z = fminf(fmaxf(__builtin_rintf(-mn32 / b.delta), 0.0f), b.qmax);
+      b.delta = fmaxf(div_rn(mx32 - mn32, b.qmax, b.rq), kDeltaMin);
+      b.rdelta = 1.0f / b.delta;
+      b.z = fminf(fmaxf(__builtin_rintf(div_rn(-mn32, b.delta, b.rdelta)), 0.0f), b.qmax);
       if (b.valid) {
-        const int64_t gi = b.row * b.ng + (b.c0 + J) / G;
+        const int64_t gi = b.row * b.ng + (b.c0 + J) / b.gw;
         b.scales[gi] = b.delta;
         b.zeros[gi] = (uint8_t)b.z;
       }
     }
+    const double* u = b.us[J];
+    const double ru = 1.0 / u[J];
     const float w32 = (float)b.w[J];
-    const float c = fminf(fmaxf(__builtin_rintf(w32 / b.delta) + b.z, 0.0f), b.qmax);
+    const float c = fminf(fmaxf(__builtin_rintf(div_rn(w32, b.delta, b.rdelta)) + b.z, 0.0f),
+                          b.qmax);
     const float q = (c - b.z) * b.delta;
     b.pack8 |= (uint64_t)(uint32_t)c << (8 * (J % 8));
-    const double* u = b.Ub + (int64_t)J * b.ldu;
-    const double e = (b.w[J] - (double)q) / u[J];
+    const double e = (b.w[J] - (double)q) * ru;
     if (J % 2 == 0) b.epair.x = e; else b.epair.y = e;
 #pragma unroll
     for (int k = J + 1; k < 64; ++k) b.w[k] = fma(-e, u[k], b.w[k]);
@@ -468,7 +486,7 @@ __device__ __forceinline__ void column_step(BlockState& b) {
       *(uint64_t*)(b.codes8 + b.row * b.K + b.c0 + J - 7) = b.pack8;
       b.pack8 = 0;
     }
-    if (J % 2 == 1 && b.valid) *(d2*)(b.err + b.row * 64 + J - 1) = b.epair;
+    if (J % 2 == 1 && b.valid) *(d2*)(b.err + b.row * b.lde + J - 1) = b.epair;
   }
 }
 
@@ -484,26 +502,40 @@ struct Columns<G, 64> {
   static __device__ __forceinline__ void run(BlockState&) {}
 };
 
+// G: the group width when it is 32 or 64 (groups start inside the block);
+// 128 stands for every width of at least 128 (groups start at block starts).
 template <int G>
 __global__ __launch_bounds__(64) void gptq_block_kernel(
     const double* __restrict__ Wc, int64_t N, int64_t K, const double* __restrict__ U,
-    int64_t ldu, int c0, int bits, float* __restrict__ scales, uint8_t* __restrict__ zeros,
-    uint8_t* __restrict__ codes8, double* __restrict__ err) {
+    int64_t ldu, int c0, int bits, int group, float* __restrict__ scales,
+    uint8_t* __restrict__ zeros,
+    uint8_t* __restrict__ codes8, double* __restrict__ err, int64_t lde) {
+  __shared__ __attribute__((aligned(16))) double us[64][64];
+  // U[c0 + r][c0 + l] -> us[r][l]: one coalesced 512-byte row per load
+  {
+    const int l = threadIdx.x;
+    const double* src = U + (int64_t)c0 * ldu + c0 + l;
+#pragma unroll 16
+    for (int r = 0; r < 64; ++r) us[r][l] = src[(int64_t)r * ldu];
+  }
+  __syncthreads();
   BlockState b;
+  b.us = us;
   b.row = (int64_t)blockIdx.x * 64 + threadIdx.x;
   b.valid = b.row < N;
   b.ncols = K - c0 < 64 ? (int)(K - c0) : 64;
   b.c0 = c0;
   b.K = K;
-  b.ng = K / G;
-  b.ldu = ldu;
+  b.gw = group;
+  b.ng = K / group;
   b.qmax = (float)((1 << bits) - 1);
+  b.rq = 1.0f / b.qmax;
   b.wr = Wc + b.row * K + c0;
-  b.Ub = U + (int64_t)c0 * ldu + c0;
   b.scales = scales;
   b.zeros = zeros;
   b.codes8 = codes8;
   b.err = err;
+  b.lde = lde;
 #pragma unroll
   for (int j = 0; j < 64; j += 2) {
     d2 v = d2{0.0, 0.0};
@@ -513,11 +545,12 @@ __global__ __launch_bounds__(64) void gptq_block_kernel(
   }
   b.delta = 1.0f;
   b.z = 0.0f;
-  if (G > 64 && c0 % G != 0 && b.valid) {
-    const int64_t gi = b.row * b.ng + c0 / G;
+  if (G > 64 && c0 % group != 0 && b.valid) {
+    const int64_t gi = b.row * b.ng + c0 / group;
     b.delta = scales[gi];
     b.z = (float)zeros[gi];
   }
+  b.rdelta = 1.0f / b.delta;
   b.pack8 = 0;
   b.epair = d2{0.0, 0.0};
   Columns<G, 0>::run(b);
@@ -576,7 +609,7 @@ GptqLayout gptq_layout(int64_t N, int64_t K, int64_t T) {
   L.wc_off = off;
   off += al((size_t)N * K * 8);
   L.err_off = off;
-  off += al((size_t)N * 64 * 8);
+  off += al((size_t)N * kSuper * 8);
   L.codes_off = off;
   off += al((size_t)N * K);
   L.dead_off = off;
@@ -704,46 +737,54 @@ hipError_t launch_gptq(const void* W, const void* X, awq_dtype_t dt, int64_t N, 
     hipLaunchKernelGGL(reverse_kernel, dim3(grid_for((K * K + 1) / 2)), dim3(256), 0, st, H, K, Kp);
     RET_IF(hipGetLastError());
   }
-  // 5. the column loop, 64 columns per step, then the step's error onto the rest
+  // 5. the column loop, 64 columns per step; each step's errors go to the rest
+  //    of its super-block at once and to the columns beyond once per super-block
   {
     ProfScope ps("awq_gptq_columns", st);
     const int gb = (int)((N + 63) / 64);
-    for (int64_t c0 = 0; c0 < K; c0 += 64) {
-      switch (group) {
-        case 32:
-          hipLaunchKernelGGL(gptq_block_kernel<32>, dim3(gb), dim3(64), 0, st, Wc, N, K, H, Kp,
-                             (int)c0, bits, scales, zeros, C8, E);
-          break;
-        case 64:
-          hipLaunchKernelGGL(gptq_block_kernel<64>, dim3(gb), dim3(64), 0, st, Wc, N, K, H, Kp,
-                             (int)c0, bits, scales, zeros, C8, E);
-          break;
-        case 128:
-          hipLaunchKernelGGL(gptq_block_kernel<128>, dim3(gb), dim3(64), 0, st, Wc, N, K, H, Kp,
-                             (int)c0, bits, scales, zeros, C8, E);
-          break;
-        case 256:
-          hipLaunchKernelGGL(gptq_block_kernel<256>, dim3(gb), dim3(64), 0, st, Wc, N, K, H, Kp,
-                             (int)c0, bits, scales, zeros, C8, E);
-          break;
-        default:
-          hipLaunchKernelGGL(gptq_block_kernel<512>, dim3(gb), dim3(64), 0, st, Wc, N, K, H, Kp,
-                             (int)c0, bits, scales, zeros, C8, E);
-          break;
+    for (int64_t s0 = 0; s0 < K; s0 += kSuper) {
+      const int64_t s1 = std::min<int64_t>(s0 + kSuper, K);
+      for (int64_t c0 = s0; c0 < s1; c0 += 64) {
+        double* eb = E + (c0 - s0);
+#define AWQ_GPTQ_BLOCK(G)                                                                   \
+  hipLaunchKernelGGL(gptq_block_kernel<G>, dim3(gb), dim3(64), 0, st, Wc, N, K, H, Kp, (int)c0, \
+                     bits, group, scales, zeros, C8, eb, (int64_t)kSuper)
+        switch (group) {
+          case 32: AWQ_GPTQ_BLOCK(32); break;
+          case 64: AWQ_GPTQ_BLOCK(64); break;
+          default: AWQ_GPTQ_BLOCK(128); break;
+        }
+#undef AWQ_GPTQ_BLOCK
+        RET_IF(hipGetLastError());
+        const int64_t rest = s1 - c0 - 64;
+        if (rest <= 0) continue;
+        GArgs g{};
+        g.a = eb;
+        g.lda = kSuper;
+        g.b = H + c0 * Kp + c0 + 64;
+        g.ldb = Kp;
+        g.c = Wc + c0 + 64;
+        g.ldc = K;
+        g.M = N;
+        g.Nn = rest;
+        g.depth = 64;
+        g.alpha = -1.0;
+        g.beta = 1.0;
+        const dim3 grid((unsigned)((rest + 63) / 64), (unsigned)((N + 63) / 64));
+        RET_IF((gemm64<64, true, false, kRect>(grid, g, st)));
       }
-      RET_IF(hipGetLastError());
-      const int64_t rest = K - c0 - 64;
+      const int64_t rest = K - s1;
       if (rest <= 0) break;
       GArgs g{};
       g.a = E;
-      g.lda = 64;
-      g.b = H + c0 * Kp + c0 + 64;
+      g.lda = kSuper;
+      g.b = H + s0 * Kp + s1;
       g.ldb = Kp;
-      g.c = Wc + c0 + 64;
+      g.c = Wc + s1;
       g.ldc = K;
       g.M = N;
       g.Nn = rest;
-      g.depth = 64;
+      g.depth = (int)(s1 - s0);
       g.alpha = -1.0;
       g.beta = 1.0;
       const dim3 grid((unsigned)((rest + 127) / 128), (unsigned)((N + 127) / 128));

@@ -74,14 +74,7 @@ __device__ __forceinline__ void group_minmax(float& mn, float& mx, int lanes) {
   }
 }
 
-// RN(a/b) from y = RN(1/b): see the file header.
-__device__ __forceinline__ float div_rn(float a, float b, float y) {
-  float q = a * y;
-  float r = fmaf(-b, q, a);
-  q = fmaf(r, y, q);
-  r = fmaf(-b, q, a);
-  return fmaf(r, y, q);
-}
+// div_rn (common.h): RN(a/b) from y = RN(1/b), see the file header.
 
 struct GroupQ {
   float delta, rdelta, z;   // step, RN(1 / step), zero-point
