@@ -323,58 +323,145 @@ __global__ __launch_bounds__(kThreads) void damp_kernel(double* __restrict__ H, 
 }
 
 // ---- Cholesky of one diagonal block and its inverse --------------------------
-// One wave; lane r owns row r of the 64x64 block (lower part read only).  The
-// factor L_pp itself is never needed again (the panel below is solved with
-// its inverse, the later updates use the solved panel), so the block is
-// overwritten with L_pp^-1 (zeros above the diagonal).  Both halves are
-// right-looking, so the dependent chain per column is short and the updates
-// of the later entries are independent FMAs.
+// One wave; lane r owns row r of the 64x64 block in registers (lower part
+// read only).  The factor L_pp itself is never needed again (the panel below
+// is solved with its inverse, the later updates use the solved panel), so the
+// block is overwritten with L_pp^-1 (zeros above the diagonal).
+//
+// Both halves go four columns per step, the steps unrolled by template
+// recursion so every register index is static (a rolled loop would move the
+// row to scratch memory).  Factorisation step JB: every lane gathers the 4x4
+// diagonal block by readlane and factors it redundantly (1/sqrt from the
+// hardware estimate and two Newton steps), the rows below solve their four
+// entries against it, the four columns are published in LDS (row-major L, one
+// 32-byte write per lane) and every row updates its later entries with four
+// FMAs each.  Inverse step IB: lane c solves the 4x4 block for x_IB..x_IB+3
+// of column c of L^-1 and pushes them into the later rows.
+__device__ __forceinline__ double readlane64(double v, int lane) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane((int)b, lane);
+  const int hi = __builtin_amdgcn_readlane((int)(b >> 32), lane);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+
+// 1/sqrt(x) for x > 0 to a few ulps: the hardware estimate, then two Newton
+// steps y <- y + y (1/2 - (x/2) y^2), each doubling the correct bits.
+__device__ __forceinline__ double rsqrt64(double x) {
+  double y = __builtin_amdgcn_rsq(x);
+  const double h = 0.5 * x;
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const double e = fma(-h * y, y, 0.5);
+    y = fma(y, e, y);
+  }
+  return y;
+}
+
+struct CholRow {
+  double a[kNb];
+};
+typedef double LRow[kNb + 2];
+
+template <int JB>
+__device__ __forceinline__ void chol_step(CholRow& st, int r, LRow* Lr, double* rdiag) {
+  if constexpr (JB < kNb) {
+    double* a = st.a;
+    double b[4][4], l[4][4], rr[4], x[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+#pragma unroll
+      for (int q = 0; q <= p; ++q) b[p][q] = readlane64(a[JB + q], JB + p);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      double d = b[q][q];
+#pragma unroll
+      for (int s = 0; s < q; ++s) d = fma(-l[q][s], l[q][s], d);
+      rr[q] = rsqrt64(d);
+      l[q][q] = d * rr[q];
+#pragma unroll
+      for (int p = q + 1; p < 4; ++p) {
+        double v = b[p][q];
+#pragma unroll
+        for (int s = 0; s < q; ++s) v = fma(-l[p][s], l[q][s], v);
+        l[p][q] = v * rr[q];
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      double v = a[JB + q];
+#pragma unroll
+      for (int s = 0; s < q; ++s) v = fma(-x[s], l[q][s], v);
+      x[q] = v * rr[q];
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      double inblk = 0.0;
+#pragma unroll
+      for (int p = q; p < 4; ++p) inblk = r == JB + p ? l[p][q] : inblk;
+      a[JB + q] = r >= JB + 4 ? x[q] : inblk;
+    }
+    *(d2*)&Lr[r][JB] = d2{a[JB], a[JB + 1]};
+    *(d2*)&Lr[r][JB + 2] = d2{a[JB + 2], a[JB + 3]};
+    if (r == 0) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) rdiag[JB + q] = rr[q];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = JB + 4; k < kNb; ++k) {
+      const d2 u0 = *(const d2*)&Lr[k][JB], u1 = *(const d2*)&Lr[k][JB + 2];
+      double v = a[k];
+      v = fma(-a[JB], u0.x, v);
+      v = fma(-a[JB + 1], u0.y, v);
+      v = fma(-a[JB + 2], u1.x, v);
+      v = fma(-a[JB + 3], u1.y, v);
+      a[k] = v;
+    }
+    chol_step<JB + 4>(st, r, Lr, rdiag);
+  }
+}
+
+template <int IB>
+__device__ __forceinline__ void inv_step(CholRow& st, int c, const LRow* Lr, const double* rdiag,
+                                         double* blk, int64_t ld) {
+  if constexpr (IB < kNb) {
+    double* a = st.a;
+    double x[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      double v = (IB + q == c ? 1.0 : 0.0) - a[IB + q];
+#pragma unroll
+      for (int s = 0; s < q; ++s) v = fma(-Lr[IB + q][IB + s], x[s], v);
+      x[q] = v * rdiag[IB + q];
+      blk[(int64_t)(IB + q) * ld + c] = x[q];
+    }
+#pragma unroll
+    for (int m = IB + 4; m < kNb; ++m) {
+      const d2 u0 = *(const d2*)&Lr[m][IB], u1 = *(const d2*)&Lr[m][IB + 2];
+      double v = a[m];
+      v = fma(u0.x, x[0], v);
+      v = fma(u0.y, x[1], v);
+      v = fma(u1.x, x[2], v);
+      v = fma(u1.y, x[3], v);
+      a[m] = v;
+    }
+    inv_step<IB + 4>(st, c, Lr, rdiag, blk, ld);
+  }
+}
+
 __global__ __launch_bounds__(64) void chol_diag_kernel(double* __restrict__ H, int64_t ld, int p) {
-  __shared__ double col[kNb];
+  __shared__ __attribute__((aligned(16))) LRow Lr[kNb];
   __shared__ double rdiag[kNb];
-  __shared__ double Ls[kNb][kNb + 1];
   const int r = threadIdx.x;
   double* blk = H + (int64_t)p * kNb * ld + (int64_t)p * kNb;
-  double a[kNb];
+  CholRow st;
 #pragma unroll
-  for (int k = 0; k < kNb; ++k) a[k] = k <= r ? blk[(int64_t)r * ld + k] : 0.0;
-  // factorisation: column j is scaled by 1 / L_jj, then every later column updated
-#pragma unroll
-  for (int j = 0; j < kNb; ++j) {
-    if (r == j) {
-      const double d = sqrt(a[j]);
-      a[j] = d;
-      rdiag[j] = 1.0 / d;
-    }
-    __syncthreads();
-    if (r > j) {
-      a[j] *= rdiag[j];
-      col[r] = a[j];
-    }
-    __syncthreads();
-    if (r > j) {
-#pragma unroll
-      for (int k = j + 1; k < kNb; ++k)
-        if (k <= r) a[k] = fma(-a[j], col[k], a[k]);
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int k = 0; k < kNb; ++k) Ls[r][k] = k <= r ? a[k] : 0.0;
+  for (int k = 0; k < kNb; ++k) st.a[k] = k <= r ? blk[(int64_t)r * ld + k] : 0.0;
+  chol_step<0>(st, r, Lr, rdiag);
   __syncthreads();
-  // inverse: lane c solves L x = e_c, each x_i pushed into the later rows at once
-  const int c = r;
-  double acc[kNb], x[kNb];
 #pragma unroll
-  for (int i = 0; i < kNb; ++i) acc[i] = 0.0;
-#pragma unroll
-  for (int i = 0; i < kNb; ++i) {
-    x[i] = ((i == c ? 1.0 : 0.0) - acc[i]) * rdiag[i];
-#pragma unroll
-    for (int m = i + 1; m < kNb; ++m) acc[m] = fma(Ls[m][i], x[i], acc[m]);
-  }
-#pragma unroll
-  for (int i = 0; i < kNb; ++i) blk[(int64_t)i * ld + c] = x[i];
+  for (int i = 0; i < kNb; ++i) st.a[i] = 0.0;
+  inv_step<0>(st, r, Lr, rdiag, blk, ld);
 }
 
 // U[a][b] = Linv[K-1-a][K-1-b]: swap every entry of the leading K x K block
@@ -410,150 +497,149 @@ __global__ void scaled_weights_kernel(const S* __restrict__ W, const float* __re
 }
 
 // ---- the column loop over one block of 64 columns --------------------------------
-// Lane = weight row.  The block's 64 current values live in registers and the
-// block's 64 x 64 piece of U is staged in LDS once (every lane reads the same
-// U entries: broadcasts), so the only latency left per column is the
-// quantiser's short dependent chain.  A group's step and zero-point come from
-// its current values when the loop reaches its first column: inside the block
-// for groups of at most 64 columns, else from this block's registers and the
-// later columns in Wc (which already carry every earlier error).  Quantiser
-// in IEEE fp32, one rounding per operation, quotients correctly rounded
-// (div_rn with the reciprocal taken once per group):
+// Lane = weight row; 64 rows per workgroup (one wave).  The block's piece of
+// U (transposed, so a column of U is a contiguous LDS row) and the rows'
+// current values are staged in LDS.  The 64 columns go in sub-blocks of 16:
+// a sub-block's values sit in registers and are quantised one column at a
+// time, each error pushed into the sub-block's later columns at once; then
+// the sub-block's 16 errors are pushed into the block's later columns (16
+// FMAs per column, a rolled loop).  Loops stay rolled where they can:
+// straight-line code run once per launch spends its time fetching
+// instructions.
+//
+// A group's step and zero-point come from its current values when the loop
+// reaches its first column: from LDS for groups of at most 64 columns, else
+// from LDS and the later columns in Wc (which already carry every earlier
+// error).  Quantiser in IEEE fp32, one rounding per operation, quotients
+// correctly rounded (div_rn with the reciprocal taken once per group):
 //   delta = max((mx - mn) / qmax, 1e-10), z = clamp(rint(-mn / delta)),
 //   c = clamp(rint(w / delta) + z), q = (c - z) * delta,
 // with w, mn, mx the fp64 current values rounded to fp32.  The fp64 error
 // (w - q) / U[j][j] is formed with the reciprocal of U[j][j].
-struct BlockState {
-  double w[64];            // current values of the block's columns
-  float delta, rdelta, z, qmax, rq;
-  uint64_t pack8;          // codes of the current 8 columns
-  d2 epair;                // errors of the current 2 columns
-  bool valid;
-  int ncols, c0, gw;        // gw: the group width
-  int64_t row, K, ng;
-  const double* wr;        // this row's block in Wc
-  const double (*us)[64];  // the block of U in LDS
-  float* scales;
-  uint8_t* zeros;
-  uint8_t* codes8;
-  double* err;             // this row-block's errors, row stride lde
-  int64_t lde;
-};
-
-// Column J of the block (J a compile-time index, so w stays in registers).
-template <int G, int J>
-__device__ __forceinline__ void column_step(BlockState& b) {
-  if (J < b.ncols) {
-    const bool gstart = G <= 64 ? (J % G == 0) : (J == 0 && b.c0 % b.gw == 0);
-    if (gstart) {
-      double mn = b.w[J], mx = b.w[J];
-      constexpr int in_regs = G <= 64 ? G : 64 - J;
-#pragma unroll
-      for (int k = 1; k < in_regs; ++k) {
-        mn = fmin(mn, b.w[J + k]);
-        mx = fmax(mx, b.w[J + k]);
-      }
-      if (G > 64 && b.valid) {
-#pragma unroll 8
-        for (int k = 64; k < b.gw; ++k) {
-          const double v = b.wr[k];
-          mn = fmin(mn, v);
-          mx = fmax(mx, v);
-        }
-      }
-      const float mn32 = (float)mn, mx32 = (float)mx;
-      b.delta = fmaxf(div_rn(mx32 - mn32, b.qmax, b.rq), kDeltaMin);
-      b.rdelta = 1.0f / b.delta;
-      b.z = fminf(fmaxf(__builtin_rintf(div_rn(-mn32, b.delta, b.rdelta)), 0.0f), b.qmax);
-      if (b.valid) {
-        const int64_t gi = b.row * b.ng + (b.c0 + J) / b.gw;
-        b.scales[gi] = b.delta;
-        b.zeros[gi] = (uint8_t)b.z;
-      }
-    }
-    const double* u = b.us[J];
-    const double ru = 1.0 / u[J];
-    const float w32 = (float)b.w[J];
-    const float c = fminf(fmaxf(__builtin_rintf(div_rn(w32, b.delta, b.rdelta)) + b.z, 0.0f),
-                          b.qmax);
-    const float q = (c - b.z) * b.delta;
-    b.pack8 |= (uint64_t)(uint32_t)c << (8 * (J % 8));
-    const double e = (b.w[J] - (double)q) * ru;
-    if (J % 2 == 0) b.epair.x = e; else b.epair.y = e;
-#pragma unroll
-    for (int k = J + 1; k < 64; ++k) b.w[k] = fma(-e, u[k], b.w[k]);
-    if (J % 8 == 7 && b.valid) {
-      *(uint64_t*)(b.codes8 + b.row * b.K + b.c0 + J - 7) = b.pack8;
-      b.pack8 = 0;
-    }
-    if (J % 2 == 1 && b.valid) *(d2*)(b.err + b.row * b.lde + J - 1) = b.epair;
-  }
-}
-
-template <int G, int J>
-struct Columns {
-  static __device__ __forceinline__ void run(BlockState& b) {
-    column_step<G, J>(b);
-    Columns<G, J + 1>::run(b);
-  }
-};
-template <int G>
-struct Columns<G, 64> {
-  static __device__ __forceinline__ void run(BlockState&) {}
-};
+constexpr int kSub = 16;
 
 // G: the group width when it is 32 or 64 (groups start inside the block);
 // 128 stands for every width of at least 128 (groups start at block starts).
 template <int G>
-__global__ __launch_bounds__(64) void gptq_block_kernel(
+__global__ __launch_bounds__(kThreads) void gptq_block_kernel(
     const double* __restrict__ Wc, int64_t N, int64_t K, const double* __restrict__ U,
     int64_t ldu, int c0, int bits, int group, float* __restrict__ scales,
-    uint8_t* __restrict__ zeros,
-    uint8_t* __restrict__ codes8, double* __restrict__ err, int64_t lde) {
-  __shared__ __attribute__((aligned(16))) double us[64][64];
-  // U[c0 + r][c0 + l] -> us[r][l]: one coalesced 512-byte row per load
+    uint8_t* __restrict__ zeros, uint8_t* __restrict__ codes8, double* __restrict__ err,
+    int64_t lde) {
+  __shared__ __attribute__((aligned(16))) double ut[64][66];   // ut[k][j] = U[c0 + j][c0 + k]
+  __shared__ double wl[64][64];                                // wl[k][r]: current values of row r
+  __shared__ double es[kSub][64];                              // a sub-block's errors
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int64_t r0 = (int64_t)blockIdx.x * 64;
+  const int ncols = K - c0 < 64 ? (int)(K - c0) : 64;
+  const int64_t ng = K / group;
+  const float qmax = (float)((1 << bits) - 1), rq = 1.0f / qmax;
   {
-    const int l = threadIdx.x;
-    const double* src = U + (int64_t)c0 * ldu + c0 + l;
-#pragma unroll 16
-    for (int r = 0; r < 64; ++r) us[r][l] = src[(int64_t)r * ldu];
+    // thread t stages 16 entries of U's block and 16 current values of row
+    // t / 4, all loads in flight at once
+    const int j = t >> 2, k0 = (t & 3) * 16;
+    const double* us = U + (int64_t)(c0 + j) * ldu + c0 + k0;
+    const int64_t rr = r0 + j;
+    const bool vr = rr < N;
+    const double* ws = Wc + rr * K + c0 + k0;
+    d2 u[8], w[8];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      u[v] = *(const d2*)(us + 2 * v);
+      w[v] = vr && k0 + 2 * v < ncols ? *(const d2*)(ws + 2 * v) : d2{0.0, 0.0};
+    }
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      ut[k0 + 2 * v][j] = u[v].x;
+      ut[k0 + 2 * v + 1][j] = u[v].y;
+      wl[k0 + 2 * v][j] = w[v].x;
+      wl[k0 + 2 * v + 1][j] = w[v].y;
+    }
   }
   __syncthreads();
-  BlockState b;
-  b.us = us;
-  b.row = (int64_t)blockIdx.x * 64 + threadIdx.x;
-  b.valid = b.row < N;
-  b.ncols = K - c0 < 64 ? (int)(K - c0) : 64;
-  b.c0 = c0;
-  b.K = K;
-  b.gw = group;
-  b.ng = K / group;
-  b.qmax = (float)((1 << bits) - 1);
-  b.rq = 1.0f / b.qmax;
-  b.wr = Wc + b.row * K + c0;
-  b.scales = scales;
-  b.zeros = zeros;
-  b.codes8 = codes8;
-  b.err = err;
-  b.lde = lde;
+  const int64_t row = r0 + lane;
+  const bool valid = row < N;
+  const double* wr = Wc + row * K + c0;
+  float delta = 1.0f, z = 0.0f;
+  if (G > 64 && c0 % group != 0 && valid) {
+    const int64_t gi = row * ng + c0 / group;
+    delta = scales[gi];
+    z = (float)zeros[gi];
+  }
+  float rdelta = 1.0f / delta;
+#pragma unroll 1
+  for (int s0 = 0; s0 < ncols; s0 += kSub) {
+    if (wave == 0) {
+      const bool gstart = G <= 64 ? (s0 % G == 0) : (s0 == 0 && c0 % group == 0);
+      if (gstart) {
+        const int gend = G <= 64 ? s0 + G : 64;
+        double mn = wl[s0][lane], mx = mn;
+#pragma unroll 4
+        for (int k = s0 + 1; k < gend; ++k) {
+          const double v = wl[k][lane];
+          mn = fmin(mn, v);
+          mx = fmax(mx, v);
+        }
+        if (G > 64 && valid) {
+#pragma unroll 8
+          for (int k = 64; k < group; ++k) {
+            const double v = wr[k];
+            mn = fmin(mn, v);
+            mx = fmax(mx, v);
+          }
+        }
+        const float mn32 = (float)mn, mx32 = (float)mx;
+        delta = fmaxf(div_rn(mx32 - mn32, qmax, rq), kDeltaMin);
+        rdelta = 1.0f / delta;
+        z = fminf(fmaxf(__builtin_rintf(div_rn(-mn32, delta, rdelta)), 0.0f), qmax);
+        if (valid) {
+          const int64_t gi = row * ng + (c0 + s0) / group;
+          scales[gi] = delta;
+          zeros[gi] = (uint8_t)z;
+        }
+      }
+      double w[kSub], e[kSub];
 #pragma unroll
-  for (int j = 0; j < 64; j += 2) {
-    d2 v = d2{0.0, 0.0};
-    if (b.valid && j < b.ncols) v = *(const d2*)(b.wr + j);
-    b.w[j] = v.x;
-    b.w[j + 1] = v.y;
+      for (int jj = 0; jj < kSub; ++jj) w[jj] = wl[s0 + jj][lane];
+      uint64_t pk[2] = {0, 0};
+#pragma unroll
+      for (int jj = 0; jj < kSub; ++jj) {
+        const double ru = 1.0 / ut[s0 + jj][s0 + jj];
+        const float w32 = (float)w[jj];
+        const float c =
+            fminf(fmaxf(__builtin_rintf(div_rn(w32, delta, rdelta)) + z, 0.0f), qmax);
+        const float q = (c - z) * delta;
+        pk[jj / 8] |= (uint64_t)(uint32_t)c << (8 * (jj % 8));
+        e[jj] = (w[jj] - (double)q) * ru;
+        es[jj][lane] = e[jj];
+#pragma unroll
+        for (int j2 = jj + 1; j2 < kSub; ++j2) w[j2] = fma(-e[jj], ut[s0 + j2][s0 + jj], w[j2]);
+      }
+      if (valid) {
+        uint64_t* cp = (uint64_t*)(codes8 + row * K + c0 + s0);
+        cp[0] = pk[0];
+        cp[1] = pk[1];
+        double* ep = err + row * lde + s0;
+#pragma unroll
+        for (int jj = 0; jj < kSub; jj += 2) *(d2*)(ep + jj) = d2{e[jj], e[jj + 1]};
+      }
+    }
+    __syncthreads();
+    // the sub-block's errors into the block's later columns, columns split
+    // between the four waves
+    double e[kSub];
+#pragma unroll
+    for (int jj = 0; jj < kSub; ++jj) e[jj] = es[jj][lane];
+#pragma unroll 2
+    for (int k = s0 + kSub + wave; k < ncols; k += 4) {
+      double v = wl[k][lane];
+      const double* uk = &ut[k][s0];
+#pragma unroll
+      for (int jj = 0; jj < kSub; ++jj) v = fma(-e[jj], uk[jj], v);
+      wl[k][lane] = v;
+    }
+    __syncthreads();
   }
-  b.delta = 1.0f;
-  b.z = 0.0f;
-  if (G > 64 && c0 % group != 0 && b.valid) {
-    const int64_t gi = b.row * b.ng + c0 / group;
-    b.delta = scales[gi];
-    b.z = (float)zeros[gi];
-  }
-  b.rdelta = 1.0f / b.delta;
-  b.pack8 = 0;
-  b.epair = d2{0.0, 0.0};
-  Columns<G, 0>::run(b);
 }
 
 // Pack uint8 codes [N][K] into each row's little-endian bitstream.
@@ -747,7 +833,8 @@ hipError_t launch_gptq(const void* W, const void* X, awq_dtype_t dt, int64_t N, 
       for (int64_t c0 = s0; c0 < s1; c0 += 64) {
         double* eb = E + (c0 - s0);
 #define AWQ_GPTQ_BLOCK(G)                                                                   \
-  hipLaunchKernelGGL(gptq_block_kernel<G>, dim3(gb), dim3(64), 0, st, Wc, N, K, H, Kp, (int)c0, \
+  hipLaunchKernelGGL(gptq_block_kernel<G>, dim3(gb), dim3(kThreads), 0, st, Wc, N, K, H, Kp,     \
+                     (int)c0,                                                                 \
                      bits, group, scales, zeros, C8, eb, (int64_t)kSuper)
         switch (group) {
           case 32: AWQ_GPTQ_BLOCK(32); break;
