@@ -52,6 +52,8 @@ def parse():
                    help="instead of the search, time GPTQ error feedback after the scaling "
                         "(awq_gptq_quantize with the AWQ scales of alpha = 0.5) on the synthetic "
                         "layers, phase by phase")
+    p.add_argument("--gptq-layers", default="llama7b-qproj,llama7b-upgate,70b-mlp",
+                   help="comma-separated synthetic layers for --gptq (the first is the headline)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 1 GiB fp32 device copy (torch.neg into a second "
                         "buffer) three times: the known-size reference for HBM byte counters")
@@ -231,7 +233,8 @@ def bench_gptq(args) -> None:
 
     dev = torch.device("cuda", 0)
     out = []
-    for name in ("llama7b-qproj", "llama7b-upgate", "70b-mlp"):
+    layers = args.gptq_layers.split(",")
+    for name in layers:
         spec = CONFIGS[name]
         W, X = make_layer(spec)
         Wd, Xd = W.to(dev), X.to(dev)
@@ -240,7 +243,7 @@ def bench_gptq(args) -> None:
         s = torch.pow(torch.clamp(a, min=1e-8).double(), 0.5).float()
         ws = torch.empty(awq.awq_gptq_workspace_size(N, K, T), dtype=torch.uint8, device=dev)
         run = lambda: awq.awq_gptq_quantize(Wd, Xd, s, spec.bits, spec.group, 0.01, workspace=ws)
-        steps = max(1, args.steps // 10) if name == "llama7b-qproj" else 2
+        steps = max(1, args.steps // 10) if name == layers[0] else 2
         for _ in range(max(1, min(args.warmup, 3))):
             run()
         torch.cuda.synchronize()
@@ -267,7 +270,7 @@ def bench_gptq(args) -> None:
                "cholesky_inverse_tflops": (2.0 * K ** 3 / 3) /
                                           ((phases["cholesky"] + phases["inverse"]) * 1e-3) / 1e12,
                "update_tflops": float(N) * K * K / (phases["columns"] * 1e-3) / 1e12}
-        if name == "llama7b-qproj" and not args.no_cpu_baseline:
+        if name == layers[0] and not args.no_cpu_baseline:
             rec["cpu_baseline"] = gptq_cpu_baseline(spec, W, X, s.cpu().numpy())
         out.append(rec)
         del W, X, Wd, Xd, ws
@@ -278,8 +281,8 @@ def bench_gptq(args) -> None:
         "value": 1e3 / head["ms_per_layer"], "unit": "layers/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "higher_is_better": True, "dtype": "f64",
         "data": "synthetic",
-        "config": {"workload": "llama-7b q_proj (W fp16 4096x4096, X 4096 tokens, INT4 g128), "
-                               "AWQ scales of alpha 0.5, damping 0.01"},
+        "config": {"workload": CONFIGS[head["layer"]].name + ", AWQ scales of alpha 0.5, "
+                               "damping 0.01"},
         "roofline": {"bound": "mfma", "achieved": head["hessian_tflops"], "peak": 78.6,
                      "unit": "TFLOP/s", "frac": head["hessian_tflops"] / 78.6, "traffic": None,
                      "kernel": "Hessian X'^T X' (fp64 MFMA), phase time"},
