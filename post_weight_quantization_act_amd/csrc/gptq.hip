@@ -156,7 +156,7 @@ __device__ __forceinline__ Job make_job(const GArgs& g) {
 }
 
 template <int TILE, bool A_KC, bool B_KC, int MAP, bool C_T>
-__global__ __launch_bounds__(kThreads) void gemm64_kernel(GArgs g) {
+__global__ __launch_bounds__(kThreads, 2) void gemm64_kernel(GArgs g) {
   constexpr int WT = TILE / 2;          // wave tile
   constexpr int F = WT / 16;            // 16x16 blocks per wave side
   constexpr int LS = TILE + kPad;       // LDS row stride (doubles)
