@@ -462,6 +462,74 @@ def lowbit_matmul(Xs: np.ndarray, codes: np.ndarray, scales: np.ndarray, zeros: 
 
 
 # ---------------------------------------------------------------------------
+# SmoothQuant: 8-bit weights and activations.
+# [P3] section 5: to run the product itself in INT8, divide every activation
+# channel by a factor and multiply the matching weights by it (the product
+# is unchanged), with the factor balancing the two sides,
+# s_j = sqrt(max|X_j| / max|W_j|); then both have moderate ranges and both
+# are quantised to INT8.  The readings (symmetric, 127 levels each side,
+# weights per output channel, activations per token) are listed in the
+# design notes.
+# ---------------------------------------------------------------------------
+INT8_MAX = F32(127)
+
+
+def channel_absmax(A: np.ndarray) -> np.ndarray:
+    """max over rows of |A[:, j]| for A [R, K], exact in fp32."""
+    return np.max(np.abs(np.asarray(A).astype(F32)), axis=0)
+
+
+def smooth_scales(X: np.ndarray, W: np.ndarray) -> np.ndarray:
+    """s_j = sqrt(max_t |X[t, j]| / max_i |W[i, j]|) in fp32 (a correctly rounded
+    division, then a correctly rounded square root); s_j = 1 when either
+    maximum is 0 (a channel that carries nothing needs no migration)."""
+    ax, aw = channel_absmax(X), channel_absmax(W)
+    ok = (ax > 0) & (aw > 0)
+    s = np.ones(ax.shape, dtype=F32)
+    s[ok] = np.sqrt(ax[ok] / aw[ok])
+    return s
+
+
+def quantize_rows_int8(A: np.ndarray):
+    """Symmetric per-row INT8: step = max_k |A[r, k]| / 127 (fp32), 1 for an
+    all-zero row; q = clip(rint(A / step), -127, 127).  Returns (q int8 [R, K],
+    step fp32 [R])."""
+    A = np.asarray(A, dtype=F32)
+    amax = np.max(np.abs(A), axis=1)
+    step = np.where(amax > 0, amax / INT8_MAX, F32(1)).astype(F32)
+    q = np.clip(np.rint(A / step[:, None]), -INT8_MAX, INT8_MAX)
+    return q.astype(np.int8), step
+
+
+def w8a8_operands(W: np.ndarray, X: np.ndarray, s: np.ndarray):
+    """The smoothed operands, quantised: X' = X / s per channel (fp32 division)
+    per token, W' = W * s per channel (fp32 product) per output channel.
+    Returns (qx, step_x, qw, step_w)."""
+    s = np.asarray(s, dtype=F32)
+    Xs = np.asarray(X).astype(F32) / s[None, :]
+    Ws = np.asarray(W).astype(F32) * s[None, :]
+    qx, sx = quantize_rows_int8(Xs)
+    qw, sw = quantize_rows_int8(Ws)
+    return qx, sx, qw, sw
+
+
+def w8a8_matmul(qx, sx, qw, sw) -> np.ndarray:
+    """Y[t, n] = fp32(fp32(fp32(acc) * sx[t]) * sw[n]) with acc = sum_k qx[t, k] qw[n, k]
+    exact (int64): the INT8 product and its rescaling to real units."""
+    acc = np.asarray(qx).astype(np.int64) @ np.asarray(qw).astype(np.int64).T
+    y = acc.astype(F32) * np.asarray(sx, dtype=F32)[:, None]
+    return y * np.asarray(sw, dtype=F32)[None, :]
+
+
+def w8a8_loss(W: np.ndarray, X: np.ndarray, s: np.ndarray) -> float:
+    """mean over t, n of (Y - Y8)^2 with Y = X W^T in fp64 and Y8 the W8A8 output."""
+    qx, sx, qw, sw = w8a8_operands(W, X, s)
+    Y = reference_output(W, X)
+    e = Y - w8a8_matmul(qx, sx, qw, sw).astype(F64)
+    return float(np.sum(e * e) / F64(e.size))
+
+
+# ---------------------------------------------------------------------------
 # Helpers that exist only to pin the pages' worked examples.
 # ---------------------------------------------------------------------------
 def fake_quant_sym(w, bits: int) -> np.ndarray:

@@ -585,3 +585,76 @@ def test_gptq_lowers_the_output_error_and_complements_awq():
     both = oracle.output_loss(Wn, Xc, oracle.gptq_fake_quant(Wn, Xc, s_best, 3, 128))
     assert gptq < 0.8 * rtn
     assert both < awq
+
+
+# ---------------------------------------------------------------------------
+# SmoothQuant (W8A8)
+# ---------------------------------------------------------------------------
+def test_smoothing_balances_every_channel():
+    """[P3] section 5: with s_j = sqrt(max|X_j| / max|W_j|) the smoothed
+    activations and weights reach the same maximum in every channel,
+    sqrt(max|X_j| max|W_j|) (two outlier channels, as in the page's toy)."""
+    rng = np.random.default_rng(6)
+    X = rng.standard_normal((64, 8)).astype(F32)
+    X[:, 2] *= 60
+    X[:, 6] *= 90                                         # two outlier channels
+    W = (0.02 * rng.standard_normal((16, 8))).astype(F32)
+    s = oracle.smooth_scales(X, W)
+    ax, aw = np.abs(X).max(0).astype(np.float64), np.abs(W).max(0).astype(np.float64)
+    np.testing.assert_allclose(s, np.sqrt(ax / aw), rtol=2 ** -23)
+    xm = np.abs(X / s).max(0).astype(np.float64)
+    wm = np.abs(W * s).max(0).astype(np.float64)
+    np.testing.assert_allclose(xm, np.sqrt(ax * aw), rtol=3 * 2 ** -24)
+    np.testing.assert_allclose(wm, np.sqrt(ax * aw), rtol=3 * 2 ** -24)
+    assert xm.max() / xm.min() < (ax.max() / ax.min()) ** 0.6   # the outliers' share shrinks
+    # the product is unchanged: (X diag(s)^-1)(diag(s) W^T) = X W^T
+    Xd, Wd, sd = X.astype(np.float64), W.astype(np.float64), s.astype(np.float64)
+    np.testing.assert_allclose((Xd / sd) @ (Wd * sd).T, Xd @ Wd.T, rtol=1e-12, atol=1e-12)
+
+
+def test_smoothing_leaves_empty_channels_alone():
+    X = np.ones((4, 3), F32)
+    X[:, 1] = 0
+    W = np.ones((2, 3), F32)
+    W[:, 2] = 0
+    np.testing.assert_array_equal(oracle.smooth_scales(X, W), np.ones(3, F32))
+
+
+def test_int8_rows_by_hand():
+    """Symmetric 127-level rows: a row whose largest magnitude is 127 has step 1
+    and rounds half to even; scaling by 2^-7 changes only the step; an
+    all-zero row gets step 1 and zero codes."""
+    row = np.array([[-127, 0.5, 1.5, 2.5, -3.5, 126.5, 127]], F32)
+    q, st = oracle.quantize_rows_int8(row)
+    np.testing.assert_array_equal(q, [[-127, 0, 2, 2, -4, 126, 127]])
+    assert st[0] == 1
+    q2, st2 = oracle.quantize_rows_int8(row * F32(2 ** -7))
+    np.testing.assert_array_equal(q2, q)
+    assert st2[0] == F32(2 ** -7)
+    q0, st0 = oracle.quantize_rows_int8(np.zeros((1, 5), F32))
+    assert st0[0] == 1 and not q0.any()
+
+
+def test_w8a8_matmul_brute_force():
+    rng = np.random.default_rng(7)
+    qx = rng.integers(-127, 128, (3, 40)).astype(np.int8)
+    qw = rng.integers(-127, 128, (5, 40)).astype(np.int8)
+    sx = rng.uniform(0.01, 1, 3).astype(F32)
+    sw = rng.uniform(0.01, 1, 5).astype(F32)
+    Y = oracle.w8a8_matmul(qx, sx, qw, sw)
+    for t in range(3):
+        for n in range(5):
+            acc = sum(int(a) * int(b) for a, b in zip(qx[t], qw[n]))
+            assert Y[t, n] == F32(F32(F32(acc) * sx[t]) * sw[n])
+
+
+def test_smoothing_cuts_the_w8a8_error():
+    """[P3] section 5 (qualitative; the page's speed and memory figures are
+    parity unpinned): with 1% activation outlier channels one scale per token
+    crushes the other channels, and migrating the difficulty to the weights
+    cuts the W8A8 output error several times over."""
+    W, X = random_layer(3, 256, 512, 512, dtype="fp16", outlier_factor=50.0)
+    Wn, Xn = to_numpy(W).astype(F32), to_numpy(X).astype(F32)
+    plain = oracle.w8a8_loss(Wn, Xn, np.ones(512, F32))
+    smooth = oracle.w8a8_loss(Wn, Xn, oracle.smooth_scales(Xn, Wn))
+    assert smooth < 0.25 * plain
