@@ -324,6 +324,41 @@ awq_status_t awq_gptq_quantize(const void* W, const void* X, awq_dtype_t dtype, 
                                hipStream_t stream);
 
 /* ------------------------------------------------------------------------ *
+ * SmoothQuant: 8-bit weights and activations ([P3] section 5: divide every
+ * activation channel by a factor and multiply the matching weights by it,
+ * s_j = sqrt(max|X_j| / max|W_j|), so both sides have moderate ranges and
+ * the product can run in INT8).
+ *
+ * awq_smooth_scales: absmax_out [2K] fp32 device = max_t |X[t, j]| then
+ *   max_i |W[i, j]|; s_out [K] = fp32 sqrt(fp32 division), 1 where either
+ *   maximum is 0.  Exact (maxima) and correctly rounded, so bit-identical
+ *   to any IEEE evaluation.
+ * awq_quantize_rows_int8: A [R, K] (dtype; K a multiple of 64), smoothed per
+ *   channel by s [K] (multiply != 0: A * s, as for weights; else A / s, as
+ *   for activations; s NULL: no smoothing), then symmetric per row:
+ *   step_out[r] = max_k |v[r, k]| / 127 (1 for an all-zero row),
+ *   q_out[r, k] = clamp(rint(v / step), -127, 127), int8 row-major [R, K].
+ * awq_w8a8_loss: the W8A8 layer's output error: activations quantised per
+ *   token (A / s), weights per output channel (W * s) as above, their exact
+ *   int32 product rescaled to y = fp32(fp32(fp32(acc) * step_x[t]) *
+ *   step_w[n]) (the int8 MFMA GEMM), loss_out [1] fp64 device = mean over T N
+ *   outputs of (Y - y)^2 with Y = X W^T from the fp16/bf16 MFMA GEMM (fp32
+ *   accumulation).  y_out (device fp32 [T, N], may be NULL) receives y.
+ *   fp16/bf16; K a multiple of 64; workspace of awq_w8a8_workspace_size(N, K,
+ *   T) bytes, 256-byte aligned.
+ * ------------------------------------------------------------------------ */
+awq_status_t awq_smooth_scales(const void* X, const void* W, awq_dtype_t dtype, int64_t T,
+                               int64_t N, int64_t K, float* absmax_out, float* s_out,
+                               hipStream_t stream);
+awq_status_t awq_quantize_rows_int8(const void* A, awq_dtype_t dtype, int64_t R, int64_t K,
+                                    const float* s, int multiply, int8_t* q_out,
+                                    float* step_out, hipStream_t stream);
+size_t awq_w8a8_workspace_size(int64_t N, int64_t K, int64_t T);
+awq_status_t awq_w8a8_loss(const void* W, const void* X, awq_dtype_t dtype, int64_t N,
+                           int64_t K, int64_t T, const float* s, double* loss_out, float* y_out,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ *
  * Kernel timing.  While enabled, every kernel the library launches (or, after
  * awq_profile_select(prefix), every kernel whose name starts with prefix) is
  * bracketed by a pair of HIP events on its stream; each event pair adds a few
@@ -335,7 +370,8 @@ awq_status_t awq_gptq_quantize(const void* W, const void* X, awq_dtype_t dtype, 
  * awq_quantize_pack, awq_keep_mask, awq_lowbit_repack, awq_lowbit_gemv,
  * awq_lowbit_reduce.  GPTQ is timed by phase, one event pair around all the
  * launches of each: awq_gptq_hessian, awq_gptq_prep, awq_gptq_cholesky,
- * awq_gptq_inverse, awq_gptq_columns, awq_gptq_pack.
+ * awq_gptq_inverse, awq_gptq_columns, awq_gptq_pack.  SmoothQuant: awq_smooth_scales,
+ * awq_quant_rows_int8, awq_gemm_w8a8.
  * awq_profile_reset() drops the records.  Thread-safe.
  * ------------------------------------------------------------------------ */
 awq_status_t awq_profile_enable(int enable);

@@ -23,7 +23,8 @@ __all__ = [
     "awq_fake_quant", "awq_search_layout", "awq_search_scales", "awq_quantize_pack",
     "awq_salient_keep_workspace_size", "awq_salient_keep_loss", "awq_lowbit_repack",
     "awq_lowbit_gemv_workspace_size", "awq_lowbit_gemv", "awq_gptq_workspace_size",
-    "awq_gptq_factor_ld", "awq_gptq_quantize",
+    "awq_gptq_factor_ld", "awq_gptq_quantize", "awq_smooth_scales", "awq_quantize_rows_int8",
+    "awq_w8a8_workspace_size", "awq_w8a8_loss",
     "awq_profile_enable", "awq_profile_select", "awq_profile_read", "awq_profile_reset",
     "packed_words_per_row",
 ]
@@ -94,6 +95,10 @@ _SIGS = {
     "awq_gptq_factor_ld": ([_I64], _I64),
     "awq_gptq_quantize": ([_P, _P, _I32, _I64, _I64, _I64, _P, _I32, _I32, _D, _P, _P, _P, _P, _SZ,
                            _P], _I32),
+    "awq_smooth_scales": ([_P, _P, _I32, _I64, _I64, _I64, _P, _P, _P], _I32),
+    "awq_quantize_rows_int8": ([_P, _I32, _I64, _I64, _P, _I32, _P, _P, _P], _I32),
+    "awq_w8a8_workspace_size": ([_I64, _I64, _I64], _SZ),
+    "awq_w8a8_loss": ([_P, _P, _I32, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P], _I32),
     "awq_profile_enable": ([_I32], _I32),
     "awq_profile_select": ([ctypes.c_char_p], _I32),
     "awq_profile_read": ([ctypes.c_char_p, ctypes.POINTER(_I64), ctypes.POINTER(_D)], _I32),
@@ -315,6 +320,65 @@ def awq_gptq_quantize(W: torch.Tensor, X: torch.Tensor, s: torch.Tensor, bits: i
                                        workspace.numel(), _stream(W.device)))
     out = (codes, scales, zeros)
     return out + (workspace,) if return_workspace else out
+
+
+def awq_smooth_scales(X: torch.Tensor, W: torch.Tensor):
+    """SmoothQuant scales -> (s fp32 [K], absmax fp32 [2, K]: max|X_j| and max|W_j|)."""
+    _dev(X, "X")
+    _dev(W, "W")
+    T, K = X.shape
+    N = W.shape[0]
+    if W.dtype != X.dtype or W.shape[1] != K:
+        raise ValueError("W [N, K] and X [T, K] must share K and dtype")
+    s = torch.empty(K, dtype=torch.float32, device=X.device)
+    absmax = torch.empty((2, K), dtype=torch.float32, device=X.device)
+    _check(library().awq_smooth_scales(X.data_ptr(), W.data_ptr(), _dtype(X), T, N, K,
+                                       absmax.data_ptr(), s.data_ptr(), _stream(X.device)))
+    return s, absmax
+
+
+def awq_quantize_rows_int8(A: torch.Tensor, s: torch.Tensor | None = None, multiply: bool = False):
+    """Symmetric per-row INT8 of A smoothed by s -> (q int8 [R, K], step fp32 [R])."""
+    _dev(A, "A")
+    R, K = A.shape
+    q = torch.empty((R, K), dtype=torch.int8, device=A.device)
+    step = torch.empty(R, dtype=torch.float32, device=A.device)
+    sp = 0
+    if s is not None:
+        _dev(s, "s")
+        sp = s.data_ptr()
+    _check(library().awq_quantize_rows_int8(A.data_ptr(), _dtype(A), R, K, sp, int(multiply),
+                                            q.data_ptr(), step.data_ptr(), _stream(A.device)))
+    return q, step
+
+
+def awq_w8a8_workspace_size(N: int, K: int, T: int) -> int:
+    return int(library().awq_w8a8_workspace_size(N, K, T))
+
+
+def awq_w8a8_loss(W: torch.Tensor, X: torch.Tensor, s: torch.Tensor | None = None,
+                  return_output: bool = False, workspace: torch.Tensor | None = None):
+    """Output MSE of the W8A8 layer (smoothed by s, or not) -> loss fp64 [1]
+    and, on request, the W8A8 output fp32 [T, N]."""
+    _dev(W, "W")
+    _dev(X, "X")
+    N, K = W.shape
+    T = X.shape[0]
+    if X.dtype != W.dtype or X.shape[1] != K:
+        raise ValueError("W [N, K] and X [T, K] must share K and dtype")
+    loss = torch.empty(1, dtype=torch.float64, device=W.device)
+    y = torch.empty((T, N), dtype=torch.float32, device=W.device) if return_output else None
+    if workspace is None:
+        workspace = torch.empty(max(1, awq_w8a8_workspace_size(N, K, T)), dtype=torch.uint8,
+                                device=W.device)
+    sp = 0
+    if s is not None:
+        _dev(s, "s")
+        sp = s.data_ptr()
+    _check(library().awq_w8a8_loss(W.data_ptr(), X.data_ptr(), _dtype(W), N, K, T, sp,
+                                   loss.data_ptr(), y.data_ptr() if y is not None else 0,
+                                   workspace.data_ptr(), workspace.numel(), _stream(W.device)))
+    return (loss, y) if return_output else loss
 
 
 def awq_lowbit_repack(codes: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor, K: int,

@@ -32,8 +32,11 @@ PER_FILE = {
     # Same quantiser rules; the fp64 updates ask for their FMAs explicitly.
     "gptq.hip": ["-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
                  "-fno-gpu-flush-denormals-to-zero"],
+    "w8a8.hip": ["-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
+                 "-fno-gpu-flush-denormals-to-zero"],
 }
-SOURCES = ["act_stats.hip", "quant.hip", "gemm_sse.hip", "lowbit.hip", "gptq.hip", "awq_api.cpp"]
+SOURCES = ["act_stats.hip", "quant.hip", "gemm_sse.hip", "lowbit.hip", "gptq.hip", "w8a8.hip",
+           "awq_api.cpp"]
 
 
 def hipcc() -> str:

@@ -461,6 +461,142 @@ awq_status_t awq_gptq_quantize(const void* W, const void* X, awq_dtype_t dtype, 
 }
 
 // ---------------------------------------------------------------------------
+// SmoothQuant W8A8.
+// ---------------------------------------------------------------------------
+namespace {
+
+struct W8a8Layout {
+  size_t xq, wq, sx, sw, xt, yref, partials, scratch, bytes;
+  int tiles_m, tiles_n;
+};
+
+W8a8Layout w8a8_layout(int64_t N, int64_t K, int64_t T) {
+  W8a8Layout L;
+  const int64_t Tp = awq::padded_rows(T), Np = awq::padded_rows(N);
+  const awq::GemmTiles gt = awq::gemm_tiles(AWQ_F16);
+  L.tiles_m = (int)((T + gt.tile_m - 1) / gt.tile_m);
+  L.tiles_n = (int)((N + gt.tile_n - 1) / gt.tile_n);
+  size_t off = 0;
+  L.xq = off;
+  off = align_up(off + (size_t)Tp * K);
+  L.wq = off;
+  off = align_up(off + (size_t)Np * K);
+  L.sx = off;
+  off = align_up(off + (size_t)Tp * 4);
+  L.sw = off;
+  off = align_up(off + (size_t)Np * 4);
+  L.xt = off;
+  off = align_up(off + (size_t)Tp * K * 2);
+  L.yref = off;
+  off = align_up(off + (size_t)T * N * 4);
+  L.partials = off;
+  off = align_up(off + (size_t)L.tiles_m * L.tiles_n * 8);
+  L.scratch = off;                                  // argmin scratch: 2K floats and an index
+  off = align_up(off + (size_t)K * 8 + 4);
+  L.bytes = off;
+  return L;
+}
+
+awq_status_t check_w8a8(awq_dtype_t dt, int64_t R, int64_t K) {
+  if (!valid_dtype(dt)) return fail(AWQ_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
+  if (R < 1 || K < 1) return fail(AWQ_ERR_INVALID_ARG, "sizes must be >= 1");
+  if (K % 64 != 0) return fail(AWQ_ERR_UNSUPPORTED, "K=%lld is not a multiple of 64", (long long)K);
+  if (R > INT32_MAX) return fail(AWQ_ERR_UNSUPPORTED, "too many rows");
+  return AWQ_OK;
+}
+
+}  // namespace
+
+awq_status_t awq_smooth_scales(const void* X, const void* W, awq_dtype_t dtype, int64_t T,
+                               int64_t N, int64_t K, float* absmax_out, float* s_out,
+                               hipStream_t stream) {
+  AWQ_GUARD_BEGIN
+  awq_status_t st = check_w8a8(dtype, T, K);
+  if (st != AWQ_OK) return st;
+  if (N < 1 || N > INT32_MAX) return fail(AWQ_ERR_INVALID_ARG, "N must be >= 1");
+  if (!X || !W || !absmax_out || !s_out) return fail(AWQ_ERR_INVALID_ARG, "null pointer");
+  if (!aligned(absmax_out, 4) || !aligned(s_out, 4))
+    return fail(AWQ_ERR_UNSUPPORTED, "absmax and s must be 4-byte aligned");
+  hipError_t e = awq::launch_smooth_scales(X, W, dtype, T, N, K, absmax_out, s_out, stream);
+  if (e != hipSuccess) return hip_fail(e, "smooth scales launch");
+  return AWQ_OK;
+  AWQ_GUARD_END
+}
+
+awq_status_t awq_quantize_rows_int8(const void* A, awq_dtype_t dtype, int64_t R, int64_t K,
+                                    const float* s, int multiply, int8_t* q_out,
+                                    float* step_out, hipStream_t stream) {
+  AWQ_GUARD_BEGIN
+  awq_status_t st = check_w8a8(dtype, R, K);
+  if (st != AWQ_OK) return st;
+  if (!A || !q_out || !step_out) return fail(AWQ_ERR_INVALID_ARG, "null pointer");
+  if (!aligned(A, 16) || !aligned(q_out, 16) || !aligned(step_out, 4) || (s && !aligned(s, 4)))
+    return fail(AWQ_ERR_UNSUPPORTED, "A and q 16-byte aligned, s and steps 4-byte");
+  hipError_t e = awq::launch_quant_rows_int8(A, dtype, R, R, K, s, multiply != 0, false, q_out,
+                                             step_out, stream);
+  if (e != hipSuccess) return hip_fail(e, "int8 row quantiser launch");
+  return AWQ_OK;
+  AWQ_GUARD_END
+}
+
+size_t awq_w8a8_workspace_size(int64_t N, int64_t K, int64_t T) {
+  if (N < 1 || K < 1 || T < 1) return 0;
+  return w8a8_layout(N, K, T).bytes;
+}
+
+awq_status_t awq_w8a8_loss(const void* W, const void* X, awq_dtype_t dtype, int64_t N,
+                           int64_t K, int64_t T, const float* s, double* loss_out, float* y_out,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  AWQ_GUARD_BEGIN
+  awq_status_t st = check_w8a8(dtype, T, K);
+  if (st != AWQ_OK) return st;
+  if (dtype == AWQ_F32) return fail(AWQ_ERR_UNSUPPORTED, "W8A8 runs on fp16/bf16 layers");
+  if (N < 1 || N > INT32_MAX) return fail(AWQ_ERR_INVALID_ARG, "N must be >= 1");
+  if (!W || !X || !loss_out) return fail(AWQ_ERR_INVALID_ARG, "null pointer");
+  if (!aligned(W, 16) || !aligned(X, 16) || (s && !aligned(s, 4)) || (y_out && !aligned(y_out, 4)))
+    return fail(AWQ_ERR_UNSUPPORTED, "W and X must be 16-byte aligned, s and Y 4-byte");
+  if ((uint64_t)awq::padded_rows(T) * (uint64_t)K * 2 > kMaxBufferBytes ||
+      (uint64_t)awq::padded_rows(N) * (uint64_t)K * 2 > kMaxBufferBytes)
+    return fail(AWQ_ERR_UNSUPPORTED, "an operand exceeds the 4 GiB limit");
+  if (!workspace) return fail(AWQ_ERR_WORKSPACE, "null workspace");
+  if (!aligned(workspace, 256)) return fail(AWQ_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  const W8a8Layout L = w8a8_layout(N, K, T);
+  if (workspace_bytes < L.bytes)
+    return fail(AWQ_ERR_WORKSPACE, "workspace of %zu bytes is below %zu", workspace_bytes, L.bytes);
+  char* ws = static_cast<char*>(workspace);
+  int8_t* xq = reinterpret_cast<int8_t*>(ws + L.xq);
+  int8_t* wq = reinterpret_cast<int8_t*>(ws + L.wq);
+  float* sx = reinterpret_cast<float*>(ws + L.sx);
+  float* sw = reinterpret_cast<float*>(ws + L.sw);
+  float* yref = reinterpret_cast<float*>(ws + L.yref);
+  double* partials = reinterpret_cast<double*>(ws + L.partials);
+  float* scratch = reinterpret_cast<float*>(ws + L.scratch);
+  hipError_t e = awq::launch_quant_rows_int8(X, dtype, T, awq::padded_rows(T), K, s, false, true,
+                                             xq, sx, stream);
+  if (e != hipSuccess) return hip_fail(e, "int8 row quantiser launch");
+  e = awq::launch_quant_rows_int8(W, dtype, N, awq::padded_rows(N), K, s, true, true, wq, sw,
+                                  stream);
+  if (e != hipSuccess) return hip_fail(e, "int8 row quantiser launch");
+  e = awq::launch_tile_rows(X, T, K, ws + L.xt, stream);
+  if (e != hipSuccess) return hip_fail(e, "tile launch");
+  e = awq::launch_gemm(awq::Epi::kStore, dtype, ws + L.xt, W, false, 1, T, N, K, yref, nullptr, 0,
+                       stream);
+  if (e != hipSuccess) return hip_fail(e, "reference GEMM launch");
+  e = awq::launch_gemm_w8a8(awq::Epi::kSseRef, xq, wq, T, N, K, sx, sw, yref, partials, stream);
+  if (e != hipSuccess) return hip_fail(e, "int8 GEMM launch");
+  e = awq::launch_loss_argmin(partials, 1, (int64_t)L.tiles_m * L.tiles_n,
+                              1.0 / ((double)T * (double)N), scratch, K, loss_out,
+                              reinterpret_cast<int32_t*>(scratch + 2 * K), scratch + K, stream);
+  if (e != hipSuccess) return hip_fail(e, "loss launch");
+  if (y_out) {
+    e = awq::launch_gemm_w8a8(awq::Epi::kStore, xq, wq, T, N, K, sx, sw, y_out, nullptr, stream);
+    if (e != hipSuccess) return hip_fail(e, "int8 GEMM launch");
+  }
+  return AWQ_OK;
+  AWQ_GUARD_END
+}
+
+// ---------------------------------------------------------------------------
 // The low-bit layer on the packed weights.
 // ---------------------------------------------------------------------------
 awq_status_t awq_lowbit_repack(const uint32_t* codes, const float* scales, const uint8_t* zeros,

@@ -21,6 +21,10 @@ typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 struct F32T { typedef float storage; static constexpr int size = 4; };
 struct F16T { typedef _Float16 storage; static constexpr int size = 2; };
 struct BF16T { typedef __bf16 storage; static constexpr int size = 2; };
+// Two int8 values stored as one 2-byte element of the tiled layout.
+struct I8Pair {
+  int8_t lo, hi;
+};
 
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(_Float16 x) { return (float)x; }
@@ -140,6 +144,18 @@ hipError_t launch_gptq(const void* W, const void* X, awq_dtype_t dt, int64_t N, 
                        int64_t T, const float* s, int bits, int group, double damp,
                        uint32_t* codes, float* scales, uint8_t* zeros, void* ws, hipStream_t st);
 
+// w8a8.hip: SmoothQuant scales and the INT8 row quantiser
+// absmax [2K]: max|X_j| then max|W_j| (fp32); s [K] = sqrt(max|X_j| / max|W_j|).
+hipError_t launch_smooth_scales(const void* X, const void* W, awq_dtype_t dt, int64_t T,
+                                int64_t N, int64_t K, float* absmax, float* s, hipStream_t st);
+// Rows r < R of A [R, K] (K a multiple of 64): smoothed by s (multiplied or
+// divided; s may be null), symmetric 127-level codes and steps.  tiled: codes
+// in the tiled layout of the MFMA GEMM with Rw (padded) rows, the padding rows
+// zero; else row-major [R, K] (Rw = R).
+hipError_t launch_quant_rows_int8(const void* A, awq_dtype_t dt, int64_t R, int64_t Rw,
+                                  int64_t K, const float* s, bool multiply, bool tiled,
+                                  int8_t* q, float* step, hipStream_t st);
+
 // gemm_sse.hip
 enum class Epi { kStore = 0, kSseRef = 1, kSseDelta = 2 };
 struct GemmTiles {
@@ -156,6 +172,13 @@ GemmTiles gemm_tiles(awq_dtype_t dt);
 hipError_t launch_gemm(Epi epi, awq_dtype_t dt, const void* X, const void* B, bool b_tiled,
                        int nb, int64_t T, int64_t N, int64_t K, float* Y, double* partials,
                        int a0, hipStream_t st);
+// INT8 GEMM on tiled operands (Xq [padded T][K], Wq [padded N][K] int8, K a
+// multiple of 64, in the tiled layout of the 2-byte case with byte pairs as
+// elements): kStore writes Y = fp32(fp32(fp32(acc) sx[t]) sw[n]); kSseRef
+// writes per-tile sums of (Y_ref - that)^2 to partials (Y holds Y_ref).
+hipError_t launch_gemm_w8a8(Epi epi, const void* Xq, const void* Wq, int64_t T, int64_t N,
+                            int64_t K, const float* sx, const float* sw, float* Y,
+                            double* partials, hipStream_t st);
 hipError_t launch_loss_argmin(const double* partials, int n_alpha, int64_t tiles_per_alpha,
                               double inv_count, const float* s_table, int64_t K,
                               double* losses, int32_t* best, float* s_best, hipStream_t st);

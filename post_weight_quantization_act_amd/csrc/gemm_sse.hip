@@ -14,6 +14,8 @@
 // vector-ALU fp32 kernel.  The epilogue never writes C: it either stores the
 // reference output once, or reduces sum((Y - C)^2) / sum(C^2) over the tile
 // into one fp64 partial, so candidate outputs never reach HBM.
+#include <type_traits>
+
 #include "common.h"
 
 namespace awq {
@@ -84,6 +86,27 @@ __device__ __forceinline__ f32x4 mfma16<__bf16>(i32x4 a, i32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
+// INT8 operands travel as pairs of bytes through the same tiles (a 16-byte
+// fragment is 16 int8 along k, and v_mfma_i32_16x16x64_i8 takes lane group g's
+// bytes as k = 16 g .. 16 g + 15, the byte positions of the 16-bit case); the
+// int32 accumulators ride in the fp32 accumulator registers bit for bit.
+template <>
+__device__ __forceinline__ f32x4 mfma16<I8Pair>(i32x4 a, i32x4 b, f32x4 c) {
+  return __builtin_bit_cast(
+      f32x4, __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, __builtin_bit_cast(i32x4, c), 0, 0, 0));
+}
+
+// The epilogue's value of an accumulator: fp32 as is; an INT8 product
+// rescaled to real units, fp32(fp32(fp32(acc) * rs[t]) * cs[n]).
+template <typename S>
+__device__ __forceinline__ float acc_value(float a, const float* rs, const float* cs, int t, int n) {
+  if constexpr (std::is_same<S, I8Pair>::value) {
+    const float v = (float)__builtin_bit_cast(int, a) * rs[t];
+    return v * cs[n];
+  } else {
+    return a;
+  }
+}
 
 // Buffer resource of a raw byte range: loads at offsets >= num_bytes return 0.
 __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t num_bytes) {
@@ -144,7 +167,8 @@ template <typename S, Epi kEpi, bool B_TILED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_mfma_kernel(const S* __restrict__ Xt, const S* __restrict__ B, int nb, int T, int N,
                          int K, float* __restrict__ Y, double* __restrict__ partials, int a0,
-                         int tiles_m, int tiles_n) {
+                         int tiles_m, int tiles_n, const float* __restrict__ rs,
+                         const float* __restrict__ cs) {
   __shared__ __attribute__((aligned(1024))) char smem[kStages * kStageBytes];
   __shared__ double red[kWaves];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -280,7 +304,7 @@ void gemm_mfma_kernel(const S* __restrict__ Xt, const S* __restrict__ B, int nb,
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) {
             const int tt = m0 + wm * WTM + i * 16 + erow + rr;
-            if (tt < T && n < N) Y[(int64_t)tt * N + n] = acc[i][j][rr];
+            if (tt < T && n < N) Y[(int64_t)tt * N + n] = acc_value<S>(acc[i][j][rr], rs, cs, tt, n);
           }
         }
     } else {
@@ -295,7 +319,9 @@ void gemm_mfma_kernel(const S* __restrict__ Xt, const S* __restrict__ B, int nb,
           for (int rr = 0; rr < 4; ++rr) {
             const int tt = m0 + wm * WTM + i * 16 + erow + rr;
             float e;
-            if (kEpi == Epi::kSseRef) e = (tt < T && n < N) ? Y[(int64_t)tt * N + n] - acc[i][j][rr] : 0.0f;
+            if (kEpi == Epi::kSseRef)
+              e = (tt < T && n < N) ? Y[(int64_t)tt * N + n] - acc_value<S>(acc[i][j][rr], rs, cs, tt, n)
+                                    : 0.0f;
             else e = acc[i][j][rr];
             part += e * e;
           }
@@ -511,7 +537,8 @@ int persistent_workgroups() {
 
 template <typename S, Epi kEpi, bool B_TILED>
 hipError_t launch_mfma(const void* X, const void* B, int nb, int64_t T, int64_t N, int64_t K,
-                       float* Y, double* partials, int a0, hipStream_t st) {
+                       float* Y, double* partials, int a0, hipStream_t st,
+                       const float* rs = nullptr, const float* cs = nullptr) {
   const int tiles_m = (int)((T + BM - 1) / BM);
   const int tiles_n = (int)((N + BN - 1) / BN);
   const int total = tiles_m * tiles_n * nb;
@@ -525,7 +552,7 @@ hipError_t launch_mfma(const void* X, const void* B, int nb, int64_t T, int64_t 
   }
   gemm_mfma_kernel<S, kEpi, B_TILED><<<grid, kThreads, 0, st>>>(
       static_cast<const S*>(X), static_cast<const S*>(B), nb, (int)T, (int)N, (int)K, Y, partials,
-      a0, tiles_m, tiles_n);
+      a0, tiles_m, tiles_n, rs, cs);
   return hipGetLastError();
 }
 
@@ -573,6 +600,18 @@ hipError_t launch_gemm(Epi epi, awq_dtype_t dt, const void* X, const void* B, bo
   if (dt == AWQ_F16)
     return dispatch_epi<_Float16>(epi, X, B, b_tiled, nb, T, N, K, Y, partials, a0, st);
   return dispatch_epi<__bf16>(epi, X, B, b_tiled, nb, T, N, K, Y, partials, a0, st);
+}
+
+hipError_t launch_gemm_w8a8(Epi epi, const void* Xq, const void* Wq, int64_t T, int64_t N,
+                            int64_t K, const float* sx, const float* sw, float* Y,
+                            double* partials, hipStream_t st) {
+  ProfScope p("awq_gemm_w8a8", st);
+  const int64_t Kp = K / 2;   // byte pairs: the 2-byte elements of the tiled layout
+  if (epi == Epi::kStore)
+    return launch_mfma<I8Pair, Epi::kStore, true>(Xq, Wq, 1, T, N, Kp, Y, partials, 0, st, sx, sw);
+  if (epi == Epi::kSseRef)
+    return launch_mfma<I8Pair, Epi::kSseRef, true>(Xq, Wq, 1, T, N, Kp, Y, partials, 0, st, sx, sw);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_tile_rows(const void* src, int64_t R, int64_t K, void* dst, hipStream_t st) {

@@ -260,3 +260,50 @@ def test_gptq_workspace_layout():
     assert n >= 4096 * 4096 * 8 * 2 + 4096 * 4096
     assert awq.awq_gptq_workspace_size(0, 4096, 16) == 0
     assert awq.awq_gptq_workspace_size(8, 96, 1) >= 128 * 128 * 8
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(X=NULL), -1),
+    (dict(K=96), -2),                          # K % 64 != 0
+    (dict(T=0), -1),
+    (dict(dt=5), -1),
+    (dict(s=NULL), -1),
+])
+def test_smooth_scales_validation(over, status):
+    a = dict(X=FAKE, W=FAKE, dt=1, T=16, N=8, K=256, absmax=FAKE, s=FAKE, stream=NULL)
+    a.update(over)
+    assert _call("awq_smooth_scales", *tuple(a.values())) == status
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(A=NULL), -1),
+    (dict(K=100), -2),
+    (dict(R=0), -1),
+    (dict(q=ctypes.c_void_p(0x1008)), -2),     # q not 16-byte aligned
+])
+def test_quantize_rows_int8_validation(over, status):
+    a = dict(A=FAKE, dt=1, R=8, K=256, s=NULL, mul=0, q=FAKE, step=FAKE, stream=NULL)
+    a.update(over)
+    assert _call("awq_quantize_rows_int8", *tuple(a.values())) == status
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(W=NULL), -1),
+    (dict(dt=0), -2),                          # fp32 layers are not offered
+    (dict(K=96), -2),
+    (dict(ws=NULL), -3),
+    (dict(ws_bytes=1024), -3),
+    (dict(loss=NULL), -1),
+])
+def test_w8a8_loss_validation(over, status):
+    a = dict(W=FAKE, X=FAKE, dt=1, N=8, K=256, T=16, s=NULL, loss=FAKE, y=NULL,
+             ws=ctypes.c_void_p(0x10000), ws_bytes=1 << 30, stream=NULL)
+    a.update(over)
+    assert _call("awq_w8a8_loss", *tuple(a.values())) == status
+
+
+def test_w8a8_workspace_size():
+    # int8 operands (padded rows), steps, fp16 X tiled, the fp32 reference output
+    n = awq.awq_w8a8_workspace_size(4096, 4096, 4096)
+    assert n >= 2 * 4096 * 4096 + 4096 * 4096 * 2 + 4096 * 4096 * 4
+    assert awq.awq_w8a8_workspace_size(0, 4096, 16) == 0
