@@ -54,6 +54,10 @@ def parse():
                         "layers, phase by phase")
     p.add_argument("--gptq-layers", default="llama7b-qproj,llama7b-upgate,70b-mlp",
                    help="comma-separated synthetic layers for --gptq (the first is the headline)")
+    p.add_argument("--w8a8", action="store_true",
+                   help="instead of the search, run SmoothQuant W8A8 on the synthetic layers: "
+                        "output error with and without the smoothing scales, and the INT8 "
+                        "MFMA GEMM against the fp16/bf16 one of the same shape")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 1 GiB fp32 device copy (torch.neg into a second "
                         "buffer) three times: the known-size reference for HBM byte counters")
@@ -292,6 +296,72 @@ def bench_gptq(args) -> None:
     print(json.dumps(line), flush=True)
 
 
+def bench_w8a8(args) -> None:
+    """SmoothQuant W8A8 per synthetic layer: one awq_w8a8_loss call (both
+    operands quantised, the fp16/bf16 reference GEMM, the INT8 GEMM with the
+    squared-error epilogue, the loss) timed with events, and the two GEMMs
+    timed alone by the library's per-kernel events."""
+    import torch
+
+    import post_weight_quantization_act_amd as awq
+    from datagen import CONFIGS, make_layer
+
+    dev = torch.device("cuda", 0)
+    out = []
+    for name in ("llama7b-qproj", "llama7b-upgate", "70b-mlp"):
+        spec = CONFIGS[name]
+        W, X = make_layer(spec)
+        Wd, Xd = W.to(dev), X.to(dev)
+        N, K, T = spec.N, spec.K, spec.T
+        s, _ = awq.awq_smooth_scales(Xd, Wd)
+        ws = torch.empty(awq.awq_w8a8_workspace_size(N, K, T), dtype=torch.uint8, device=dev)
+        plain = float(awq.awq_w8a8_loss(Wd, Xd, None, workspace=ws).cpu()[0])
+        smooth = float(awq.awq_w8a8_loss(Wd, Xd, s, workspace=ws).cpu()[0])
+        power = float((Xd.float() @ Wd.float().t()).pow(2).mean())
+        reps = max(2, args.steps // 5)
+        for _ in range(max(2, args.warmup // 3)):
+            awq.awq_w8a8_loss(Wd, Xd, s, workspace=ws)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            awq.awq_w8a8_loss(Wd, Xd, s, workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        awq.awq_profile_reset()
+        awq.awq_profile_select("awq_")
+        awq.awq_profile_enable(True)
+        for _ in range(reps):
+            awq.awq_w8a8_loss(Wd, Xd, s, workspace=ws)
+        torch.cuda.synchronize()
+        awq.awq_profile_enable(False)
+        n8, ms8 = awq.awq_profile_read("awq_gemm_w8a8")
+        n16, ms16 = awq.awq_profile_read("awq_gemm_ref_output")
+        nq, msq = awq.awq_profile_read("awq_quant_rows_int8")
+        awq.awq_profile_reset()
+        ops = 2.0 * T * N * K
+        g8, g16 = ms8 / max(n8, 1), ms16 / max(n16, 1)
+        out.append({"layer": name, "N": N, "K": K, "T": T,
+                    "loss_w8a8_plain": plain, "loss_w8a8_smooth": smooth,
+                    "rel_plain": plain / power, "rel_smooth": smooth / power,
+                    "ms_per_call": ms, "int8_gemm_ms": g8, "int8_tops": ops / (g8 * 1e-3) / 1e12,
+                    "fp16_gemm_ms": g16, "fp16_tflops": ops / (g16 * 1e-3) / 1e12,
+                    "int8_speedup": g16 / g8, "quantise_ms": msq / max(nq, 1) * 2})
+        del W, X, Wd, Xd, ws
+        torch.cuda.empty_cache()
+    head = out[0]
+    print(json.dumps({
+        "metric": "W8A8 INT8 GEMM throughput (SmoothQuant operands, squared-error epilogue)",
+        "value": head["int8_tops"], "unit": "TOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "higher_is_better": True, "dtype": "i8", "data": "synthetic",
+        "config": {"workload": CONFIGS[head["layer"]].name + ", W8A8 per token / per output "
+                               "channel"},
+        "roofline": {"bound": "mfma", "achieved": head["int8_tops"], "peak": 5000.0,
+                     "unit": "TOP/s", "frac": head["int8_tops"] / 5000.0, "traffic": None},
+        "layers": out}), flush=True)
+
+
 def kernel_source_hash() -> str:
     """Hash of the candidate GEMM's source, the kernel the traffic figure belongs to."""
     h = hashlib.sha256()
@@ -362,6 +432,9 @@ def main():
         return
     if args.gptq:
         bench_gptq(args)
+        return
+    if args.w8a8:
+        bench_w8a8(args)
         return
     import numpy as np
     import torch
