@@ -14,13 +14,19 @@
  *   and the final integer codes with per-group step and zero-point
  *                                                         (awq_quantize_pack)
  *
+ * and the rows that build on it: the low-bit decode layer on the packed
+ * codes (awq_lowbit_*), the mixed-precision ablation that motivates the
+ * method (awq_salient_keep_loss), GPTQ error feedback after the scaling
+ * (awq_gptq_*) and SmoothQuant W8A8 (awq_smooth_scales,
+ * awq_quantize_rows_int8, awq_w8a8_loss).
+ *
  * Sources (web pages on the method):
  *   [P1] "Как работает quantization-aware scaling в AWQ для защиты важных
  *        весов?" (aivaro.ru Q&A), sections 5, 6 and 9
  *   [P2] "AWQ: Activation-Aware Weight Quantization For On-Device LLM
  *        Compression AND Acceleration" (reading notes), section "Measures"
- *   [P3] "52 · AWQ, GPTQ và SmoothQuant", sections 2 and 3
- *   [P4] "GPTQ与AWQ" (study notes), section "AWQ实现要点"
+ *   [P3] "52 · AWQ, GPTQ và SmoothQuant", sections 2 to 5
+ *   [P4] "GPTQ与AWQ" (study notes), sections "AWQ实现要点" and GPTQ
  *
  * Conventions shared by every entry point
  *   - Every tensor is a dense row-major buffer in device memory, allocated and
