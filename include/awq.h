@@ -377,7 +377,8 @@ awq_status_t awq_w8a8_loss(const void* W, const void* X, awq_dtype_t dtype, int6
  * awq_lowbit_reduce.  GPTQ is timed by phase, one event pair around all the
  * launches of each: awq_gptq_hessian, awq_gptq_prep, awq_gptq_cholesky,
  * awq_gptq_inverse, awq_gptq_columns, awq_gptq_pack.  SmoothQuant: awq_smooth_scales,
- * awq_quant_rows_int8, awq_gemm_w8a8.
+ * awq_quant_rows_int8, awq_gemm_w8a8_sse (the INT8 GEMM with the squared-error
+ * epilogue), awq_gemm_w8a8_store (the INT8 GEMM writing y).
  * awq_profile_reset() drops the records.  Thread-safe.
  * ------------------------------------------------------------------------ */
 awq_status_t awq_profile_enable(int enable);

@@ -605,7 +605,7 @@ hipError_t launch_gemm(Epi epi, awq_dtype_t dt, const void* X, const void* B, bo
 hipError_t launch_gemm_w8a8(Epi epi, const void* Xq, const void* Wq, int64_t T, int64_t N,
                             int64_t K, const float* sx, const float* sw, float* Y,
                             double* partials, hipStream_t st) {
-  ProfScope p("awq_gemm_w8a8", st);
+  ProfScope p(epi == Epi::kStore ? "awq_gemm_w8a8_store" : "awq_gemm_w8a8_sse", st);
   const int64_t Kp = K / 2;   // byte pairs: the 2-byte elements of the tiled layout
   if (epi == Epi::kStore)
     return launch_mfma<I8Pair, Epi::kStore, true>(Xq, Wq, 1, T, N, Kp, Y, partials, 0, st, sx, sw);
