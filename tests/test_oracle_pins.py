@@ -474,6 +474,14 @@ def test_keep_excludes_kept_weights_from_the_group_range():
     assert not np.array_equal(oracle.fake_quant(W, np.ones(4, np.float32), 2, 4), W)
     # a group whose every weight is kept stays as it is
     np.testing.assert_array_equal(oracle.fake_quant_keep(W, np.ones(4, bool), 2, 4), W)
+    # the same with the outlier below the group: [0, 0.5, 1.5] set step 0.5, zero-point 0
+    W2 = np.array([[-10.0, 0.0, 0.5, 1.5]], np.float32)
+    np.testing.assert_array_equal(oracle.fake_quant_keep(W2, np.array([1, 0, 0, 0], bool), 2, 4), W2)
+
+
+def test_weight_channel_magnitude_is_the_mean_of_magnitudes():
+    W = np.array([[1.0, -2.0, 0.0], [3.0, 4.0, -0.5]], np.float32)
+    np.testing.assert_array_equal(oracle.weight_channel_magnitude(W), np.array([2.0, 3.0, 0.25], np.float32))
 
 
 def test_keep_nothing_is_rtn_and_keep_everything_is_exact():
@@ -658,3 +666,49 @@ def test_smoothing_cuts_the_w8a8_error():
     plain = oracle.w8a8_loss(Wn, Xn, np.ones(512, F32))
     smooth = oracle.w8a8_loss(Wn, Xn, oracle.smooth_scales(Xn, Wn))
     assert smooth < 0.25 * plain
+
+
+def test_gptq_damping_and_dead_channels_in_closed_form():
+    """A dead channel's diagonal becomes 1, then damp * mean(diag) is added:
+    H = diag(4, 0), damp 0.5 -> diag(5.25, 2.25), U = diag(5.25, 2.25)^-1/2."""
+    U, dead = oracle.gptq_inverse_factor(np.diag([4.0, 0.0]), damp=0.5)
+    np.testing.assert_array_equal(dead, [False, True])
+    np.testing.assert_allclose(U, np.diag([5.25 ** -0.5, 2.25 ** -0.5]), rtol=1e-15, atol=0)
+
+
+def test_gptq_dead_channel_weights_are_dropped():
+    """A channel no calibration input reaches is quantised as zero: its codes
+    are the group's zero-point whatever its weights were."""
+    rng = np.random.default_rng(8)
+    W = rng.standard_normal((6, 64)).astype(F32)
+    X = rng.standard_normal((100, 64)).astype(F32)
+    X[:, 5] = 0
+    c, d, z = oracle.gptq_quantize(W, X, np.ones(64, F32), 4, 32)
+    np.testing.assert_array_equal(c[:, 5], z[:, 0])
+
+
+def test_gptq_with_prefix_inputs_is_error_diffusion():
+    """With the calibration rows (1,0,...,0), (1,1,0,...), ..., (1,...,1) and no
+    damping, H^-1 is bidiagonal and GPTQ reduces to carrying each rounding
+    error onto the next weight only ([P3] section 4's narration), groups
+    taking their range when the carry reaches their first column.  The carry
+    is recomputed here by that rule, with the quantiser applied one group at
+    a time."""
+    rng = np.random.default_rng(9)
+    K, G, bits = 16, 4, 3
+    W = rng.standard_normal((5, K)).astype(F32)
+    X = np.tril(np.ones((K, K)))
+    codes, delta, zero = oracle.gptq_quantize(W, X, np.ones(K, F32), bits, G, damp=0.0)
+    qmax = F32((1 << bits) - 1)
+    for r in range(W.shape[0]):
+        w = W[r].astype(np.float64).copy()
+        for j in range(K):
+            if j % G == 0:
+                grp = w[j:j + G].astype(F32)[None, :]
+                _, d, z = oracle.quantize_codes(grp, np.ones(G, F32), bits, G)
+                d, z = d[0, 0], F32(z[0, 0])
+                assert d == delta[r, j // G] and z == zero[r, j // G]
+            c = np.clip(np.rint(F32(w[j]) / d) + z, F32(0), qmax)
+            assert c == codes[r, j], (r, j)
+            if j + 1 < K:
+                w[j + 1] += w[j] - np.float64((c - z) * d)
