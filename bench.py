@@ -516,8 +516,9 @@ def main():
 
     ms_per_step = 1e3 * elapsed / args.steps
     value = spec.n_alpha * args.steps / elapsed
-    batch = lay["alpha_batch"]
-    flop_per_launch = 2.0 * T * N * K * batch
+    # the library may split the candidates over several launches (a batch that
+    # does not fit the workspace, or the two overlapped halves of one that does)
+    flop_per_launch = 2.0 * T * N * K * spec.n_alpha * args.steps / max(n_gemm, 1)
     avg_ms = ms_gemm / max(n_gemm, 1)
     achieved = flop_per_launch / (avg_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[spec.dtype]
@@ -526,10 +527,13 @@ def main():
     def avg(ms, n):
         return ms / max(n, 1)
 
+    fq_alphas = spec.n_alpha * 2 / max(n_fq, 1)        # the breakdown ran two steps
+
     detail = {
-        "gemm_sse": {"launches": n_gemm, "avg_ms": avg_ms, "tflops": achieved},
-        "fake_quant": {"avg_ms": avg(ms_fq, n_fq),
-                       "gbps": (N * K * esize + batch * N * K * esize) / (avg(ms_fq, n_fq) * 1e-3) / 1e9},
+        "gemm_sse": {"launches": n_gemm, "per_step": n_gemm / args.steps, "avg_ms": avg_ms,
+                     "tflops": achieved},
+        "fake_quant": {"avg_ms": avg(ms_fq, n_fq), "alphas_per_launch": fq_alphas,
+                       "gbps": (N * K * esize + fq_alphas * N * K * esize) / (avg(ms_fq, n_fq) * 1e-3) / 1e9},
         "act_stats": {"avg_ms": avg(ms_st, 2),
                       "gbps": (T * K * esize) / (avg(ms_st, 2) * 1e-3) / 1e9},
         "quantize_pack": {"avg_ms": avg(ms_pk, n_pk),
@@ -556,7 +560,7 @@ def main():
         "config": {"workload": spec.name, "N_out": N, "K_in": K, "T_tokens": T,
                    "bits": spec.bits, "group": spec.group, "n_alpha": spec.n_alpha,
                    "loss_form": "reference_output" if args.flags else "weight_delta",
-                   "alpha_batch": batch},
+                   "alpha_batch": lay["alpha_batch"]},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": traffic,
                      "kernel": "gemm_mfma_kernel (candidate GEMM + squared-error epilogue)",
