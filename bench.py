@@ -40,9 +40,14 @@ def parse():
     p.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--lowbit", action="store_true",
-                   help="instead of the search, time the low-bit decode layer (awq_lowbit_gemv "
-                        "on repacked codes) on the synthetic layers' weight shapes, M = 1, 4, 16 "
-                        "activation rows, against the dense fp16/bf16 product")
+                   help="instead of the search, time the low-bit layer on repacked codes on the "
+                        "synthetic layers' weight shapes against the dense fp16/bf16 product: "
+                        "awq_lowbit_gemv at M = 1, 4, 16 activation rows, awq_lowbit_gemm at "
+                        "M = 64 .. 4096")
+    p.add_argument("--lowbit-layers", default="llama7b-qproj,llama7b-upgate,llama7b-down,70b-mlp",
+                   help="with --lowbit: comma-separated layer names")
+    p.add_argument("--lowbit-m", default="64,256,1024,4096",
+                   help="with --lowbit: comma-separated activation-row counts for awq_lowbit_gemm")
     p.add_argument("--salient", action="store_true",
                    help="instead of the search, run the mixed-precision ablation on the "
                         "synthetic layers: output error with the top 1%% channels kept at full "
@@ -85,7 +90,9 @@ def bench_lowbit(args) -> None:
     """Decode-shaped low-bit layer: packed-weight bytes per second of one whole
     awq_lowbit_gemv call (GEMV and, with several k-splits, the reduction),
     timed with events around `reps` back-to-back calls; the headline case is
-    the 70B MLP layer (28672 x 8192 bf16, INT3) at one activation row."""
+    the 70B MLP layer (28672 x 8192 bf16, INT3) at one activation row.  The
+    prefill-sized matrix-core form (awq_lowbit_gemm) is timed beside the dense
+    fp16 / bf16 product for 64 to 4096 activation rows."""
     import torch
 
     import post_weight_quantization_act_amd as awq
@@ -106,8 +113,8 @@ def bench_lowbit(args) -> None:
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps * 1e3          # us per call
 
-    cases = []
-    for name in ("llama7b-qproj", "llama7b-upgate", "llama7b-down", "70b-mlp"):
+    cases, prefill = [], []
+    for name in args.lowbit_layers.split(","):
         spec = CONFIGS[name]
         N, K, b, G = spec.N, spec.K, spec.bits, spec.group
         dt = torch.float16 if spec.dtype == "fp16" else torch.bfloat16
@@ -127,17 +134,29 @@ def bench_lowbit(args) -> None:
             cases.append({"layer": name, "dtype": spec.dtype, "bits": b, "M": M, "N": N, "K": K,
                           "us": us, "bytes": nbytes, "gbps": nbytes / (us * 1e-6) / 1e9,
                           "dense_us": dense_us, "speedup_vs_dense": dense_us / us})
+        for M in (int(v) for v in args.lowbit_m.split(",")):
+            X = torch.randn(M, K, device=dev).to(dt)
+            Y = torch.empty(M, N, device=dev)
+            us = timed(lambda: awq.awq_lowbit_gemm(X, codes_t, meta_t, b, G, out=Y), args.steps)
+            dense_us = timed(lambda: X @ Wt, args.steps)
+            flop = 2.0 * M * N * K
+            prefill.append({"layer": name, "dtype": spec.dtype, "bits": b, "M": M, "N": N, "K": K,
+                            "us": us, "tflops": flop / (us * 1e-6) / 1e12,
+                            "mfma_frac": flop / (us * 1e-6) / 2.5e15, "dense_us": dense_us,
+                            "speedup_vs_dense": dense_us / us})
         del W, Wt, codes, scales, zeros, codes_t, meta_t
-    head = next(c for c in cases if c["layer"] == "70b-mlp" and c["M"] == 1)
+    head = next((c for c in cases if c["layer"] == "70b-mlp" and c["M"] == 1), cases[0])
     print(json.dumps({
         "metric": "low-bit decode layer: packed bytes per second of one call",
         "value": head["gbps"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "higher_is_better": True, "dtype": head["dtype"],
         "data": "synthetic",
-        "config": {"workload": "70b MLP weights 28672x8192 bf16, INT3 g128, 1 activation row"},
+        "config": {"workload": f"{head['layer']} weights {head['N']}x{head['K']} {head['dtype']}, "
+                               f"INT{head['bits']} g{CONFIGS[head['layer']].group}, "
+                               f"{head['M']} activation row(s)"},
         "roofline": {"bound": "hbm", "achieved": head["gbps"], "peak": 8000.0, "unit": "GB/s",
                      "frac": head["gbps"] / 8000.0, "traffic": None},
-        "cases": cases}), flush=True)
+        "cases": cases, "prefill_gemm": prefill}), flush=True)
 
 
 def bench_salient(args) -> None:

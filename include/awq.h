@@ -290,6 +290,18 @@ awq_status_t awq_lowbit_gemv(const void* X, awq_dtype_t x_dtype, int64_t M, int6
                              const uint32_t* codes_t, const void* meta_t, int64_t N, int bits,
                              int group, float* Y, void* workspace, size_t workspace_bytes,
                              hipStream_t stream);
+/* awq_lowbit_gemm: the same layer for many activation rows (prefill, M from
+ *   a few tens up): the same Y, the same repacked operands, the same exact
+ *   products x (c - z) with fp32 sums and one product by delta per group and
+ *   output, so the same error bound as awq_lowbit_gemv; the summation order
+ *   differs, so the two need not agree bit for bit.  Runs on the matrix
+ *   cores: each workgroup dequantises a 128-row tile of the packed weights
+ *   into on-chip memory once and uses it for 256 activation rows.  x_dtype
+ *   AWQ_F16 or AWQ_BF16 only (AWQ_ERR_UNSUPPORTED otherwise); Xs 16-byte
+ *   aligned; M <= 8388480, K <= 4194304; no workspace.  Results are reproducible. */
+awq_status_t awq_lowbit_gemm(const void* X, awq_dtype_t x_dtype, int64_t M, int64_t K,
+                             const uint32_t* codes_t, const void* meta_t, int64_t N, int bits,
+                             int group, float* Y, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ *
  * GPTQ error feedback after the scaling (AWQ + GPTQ).  [P3] section 4: the
@@ -373,7 +385,7 @@ awq_status_t awq_w8a8_loss(const void* W, const void* X, awq_dtype_t dtype, int6
  * the launch count and the summed elapsed milliseconds.  Kernel names:
  * awq_act_stats_partial, awq_act_stats_finish, awq_scale_table, awq_tile_rows,
  * awq_fake_quant, awq_gemm_ref_output, awq_gemm_sse, awq_loss_argmin,
- * awq_quantize_pack, awq_keep_mask, awq_lowbit_repack, awq_lowbit_gemv,
+ * awq_quantize_pack, awq_keep_mask, awq_lowbit_repack, awq_lowbit_gemv, awq_lowbit_gemm,
  * awq_lowbit_reduce.  GPTQ is timed by phase, one event pair around all the
  * launches of each: awq_gptq_hessian, awq_gptq_prep, awq_gptq_cholesky,
  * awq_gptq_inverse, awq_gptq_columns, awq_gptq_pack.  SmoothQuant: awq_smooth_scales,

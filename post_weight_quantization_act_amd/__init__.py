@@ -22,7 +22,8 @@ __all__ = [
     "awq_version", "awq_act_stats", "awq_act_stats_workspace_size", "awq_scale_table",
     "awq_fake_quant", "awq_search_layout", "awq_search_scales", "awq_quantize_pack",
     "awq_salient_keep_workspace_size", "awq_salient_keep_loss", "awq_lowbit_repack",
-    "awq_lowbit_gemv_workspace_size", "awq_lowbit_gemv", "awq_gptq_workspace_size",
+    "awq_lowbit_gemv_workspace_size", "awq_lowbit_gemv", "awq_lowbit_gemm",
+    "awq_gptq_workspace_size",
     "awq_gptq_factor_ld", "awq_gptq_quantize", "awq_smooth_scales", "awq_quantize_rows_int8",
     "awq_w8a8_workspace_size", "awq_w8a8_loss",
     "awq_profile_enable", "awq_profile_select", "awq_profile_read", "awq_profile_reset",
@@ -91,6 +92,7 @@ _SIGS = {
     "awq_lowbit_repack": ([_P, _P, _P, _I64, _I64, _I32, _I32, _P, _P, _P], _I32),
     "awq_lowbit_gemv_workspace_size": ([_I64, _I64, _I64], _SZ),
     "awq_lowbit_gemv": ([_P, _I32, _I64, _I64, _P, _P, _I64, _I32, _I32, _P, _P, _SZ, _P], _I32),
+    "awq_lowbit_gemm": ([_P, _I32, _I64, _I64, _P, _P, _I64, _I32, _I32, _P, _P], _I32),
     "awq_gptq_workspace_size": ([_I64, _I64, _I64], _SZ),
     "awq_gptq_factor_ld": ([_I64], _I64),
     "awq_gptq_quantize": ([_P, _P, _I32, _I64, _I64, _I64, _P, _I32, _I32, _D, _P, _P, _P, _P, _SZ,
@@ -416,6 +418,23 @@ def awq_lowbit_gemv(Xs: torch.Tensor, codes_t: torch.Tensor, meta_t: torch.Tenso
     _check(library().awq_lowbit_gemv(Xs.data_ptr(), _dtype(Xs), M, K, codes_t.data_ptr(),
                                      meta_t.data_ptr(), N, bits, group, out.data_ptr(),
                                      workspace.data_ptr(), workspace.numel(),
+                                     _stream(Xs.device)))
+    return out
+
+
+def awq_lowbit_gemm(Xs: torch.Tensor, codes_t: torch.Tensor, meta_t: torch.Tensor, bits: int,
+                    group: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Y [M, N] fp32 = Xs [M, K] (fp16 / bf16) times the dequantised packed
+    weights (repacked layout), on the matrix cores; for many activation rows."""
+    _dev(Xs, "Xs")
+    _dev(codes_t, "codes_t")
+    _dev(meta_t, "meta_t")
+    M, K = Xs.shape
+    N = codes_t.shape[1]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=Xs.device)
+    _check(library().awq_lowbit_gemm(Xs.data_ptr(), _dtype(Xs), M, K, codes_t.data_ptr(),
+                                     meta_t.data_ptr(), N, bits, group, out.data_ptr(),
                                      _stream(Xs.device)))
     return out
 

@@ -37,6 +37,8 @@ awq_status_t hip_fail(hipError_t e, const char* what) {
 constexpr uint64_t kMaxBufferBytes = 0xFFFFFF00ull;  // byte offsets inside kernels are 32-bit
 constexpr int kMaxAlpha = 4096;
 constexpr int64_t kGptqMaxK = 32768;   // the fp64 factor matrix is K^2 * 8 bytes
+constexpr int64_t kLowbitGemmMaxM = 65535ll * 128;  // activation-row tiles on grid y
+constexpr int64_t kLowbitGemmMaxK = 1ll << 22;       // a 256-row activation tile in 32-bit offsets
 
 int esize(awq_dtype_t dt) { return dt == AWQ_F32 ? 4 : 2; }
 
@@ -643,6 +645,29 @@ awq_status_t awq_lowbit_gemv(const void* X, awq_dtype_t x_dtype, int64_t M, int6
   hipError_t e = awq::launch_lowbit_gemv(X, x_dtype, M, K, codes_t, meta_t, N, bits, group, Y,
                                          workspace, stream);
   if (e != hipSuccess) return hip_fail(e, "lowbit gemv launch");
+  return AWQ_OK;
+  AWQ_GUARD_END
+}
+
+awq_status_t awq_lowbit_gemm(const void* X, awq_dtype_t x_dtype, int64_t M, int64_t K,
+                             const uint32_t* codes_t, const void* meta_t, int64_t N, int bits,
+                             int group, float* Y, hipStream_t stream) {
+  AWQ_GUARD_BEGIN
+  awq_status_t st = check_quant_args(x_dtype, N, K, bits, group);
+  if (st != AWQ_OK) return st;
+  if (x_dtype != AWQ_F16 && x_dtype != AWQ_BF16)
+    return fail(AWQ_ERR_UNSUPPORTED, "lowbit gemm takes fp16 or bf16 activations");
+  if (M < 1) return fail(AWQ_ERR_INVALID_ARG, "M must be >= 1");
+  if (M > kLowbitGemmMaxM)
+    return fail(AWQ_ERR_UNSUPPORTED, "M=%lld above %lld", (long long)M, (long long)kLowbitGemmMaxM);
+  if (K > kLowbitGemmMaxK)
+    return fail(AWQ_ERR_UNSUPPORTED, "K=%lld above %lld", (long long)K, (long long)kLowbitGemmMaxK);
+  if (!X || !codes_t || !meta_t || !Y) return fail(AWQ_ERR_INVALID_ARG, "null pointer");
+  if (!aligned(X, 16) || !aligned(codes_t, 4) || !aligned(meta_t, 8) || !aligned(Y, 4))
+    return fail(AWQ_ERR_UNSUPPORTED, "X 16-byte, codes_t and Y 4-byte, meta_t 8-byte aligned");
+  hipError_t e = awq::launch_lowbit_gemm(X, x_dtype, M, K, codes_t, meta_t, N, bits, group, Y,
+                                         stream);
+  if (e != hipSuccess) return hip_fail(e, "lowbit gemm launch");
   return AWQ_OK;
   AWQ_GUARD_END
 }

@@ -126,6 +126,10 @@ size_t lowbit_gemv_ws_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_lowbit_gemv(const void* X, awq_dtype_t dt, int64_t M, int64_t K,
                               const uint32_t* codes_t, const void* meta_t, int64_t N, int bits,
                               int group, float* Y, void* ws, hipStream_t st);
+// fp16/bf16 activations only; K a multiple of the group, group >= 32.
+hipError_t launch_lowbit_gemm(const void* X, awq_dtype_t dt, int64_t M, int64_t K,
+                              const uint32_t* codes_t, const void* meta_t, int64_t N, int bits,
+                              int group, float* Y, hipStream_t st);
 
 // gptq.hip: GPTQ error feedback after the scaling (all fp64 but the quantiser)
 struct GptqLayout {

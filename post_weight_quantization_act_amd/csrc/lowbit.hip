@@ -313,6 +313,414 @@ hipError_t gemv_bits(int bits, const void* X, int64_t M, int64_t K, const uint32
   }
 }
 
+// ---- prefill-sized GEMM on the matrix cores ------------------------------------
+// Y [M, N] = Xs W'^T for many activation rows: a 256 x 128 output tile per
+// workgroup of 8 waves, one workgroup per CU.  Each wave owns a 64 x 64 block
+// (2 x 2 v_mfma_f32_32x32x16 on fp16 / bf16).  K advances 32 per stage.  The
+// weights are not dequantised to W' but to the exact integers c - z (the
+// GEMV's pairs), so the MFMA sums exact products x (c - z) in fp32; at the end
+// of each group the group's sums are scaled by its delta (one product per
+// group and output) and added to the running totals, as in the GEMV, and the
+// next group's first MFMAs start from zero.  The dequantised weights never
+// leave LDS, and each 128-row weight tile serves 256 activation rows.
+//
+// The waves run ping-pong: group 0 (waves 0-3, tile rows 0-127) and group 1
+// (waves 4-7, rows 128-255) hold one wave on each SIMD.  Each stage has two
+// halves separated by a barrier: in one, group 0 issues its MFMAs, with its
+// share of the unpacking two stages ahead between them, while group 1 reads
+// its fragments, issues its transfers and applies the group-end scaling of its
+// previous stage; in the other the roles swap.  Each SIMD's matrix pipe is
+// thus fed by its two waves in turn, and one wave's memory work runs while the
+// other's MFMAs execute.
+//
+// Everything a stage needs arrives by wave-wide global -> LDS transfers
+// (buffer_load_dwordx4 ... lds, 1 KB each), issued in the wave's working
+// half: two per wave of the activation tile (16 KB, each lane fetching the
+// chunk that the swizzle puts at its LDS position) four stages ahead into a
+// ring of five slots, and, six stages ahead into rings of eight, one more per
+// wave from as many waves as needed: the stage's packed codes (128 rows x bits
+// words, contiguous in the repacked layout) and the (delta, z) pairs of the
+// stage's group.  Before every barrier each wave lets only its last two stages
+// of transfers stay in flight.  The unpacked B tiles live in a ring of three.
+// Rows of 64 bytes; 16-byte chunk c of row r sits at c ^ ((r >> 1) & 3) (no
+// bank conflicts for the fragment reads).  The LDS traffic of a stage (about
+// 100 KB: fragment reads, transfers, unpacking) is what bounds this kernel.
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kGM = 256;                         // activation rows per tile
+constexpr int kGN = 128;                         // output rows per tile
+constexpr int kGWaves = 8;
+constexpr int kGThreads = 64 * kGWaves;
+constexpr int kXRing = 5, kXAhead = 4;           // activation slots, stages ahead
+constexpr int kCRing = 8, kCAhead = 6;           // code and (delta, z) slots, stages ahead
+constexpr int kBRing = 3;                        // unpacked weight slots (two stages ahead)
+constexpr int kXSlot = kGM * 64;                 // 16 KB
+constexpr int kBSlot = kGN * 64;                 // 8 KB
+constexpr int kPerStage = 3;                     // transfers per stage of a wave with a third one
+
+__device__ __forceinline__ int g_off(int r, int c) { return r * 64 + 16 * (c ^ ((r >> 1) & 3)); }
+
+// Buffer resource of a raw byte range: loads at offsets >= num_bytes return 0.
+__device__ __forceinline__ i32x4 byte_range(const void* base, uint32_t num_bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  return i32x4{(int)(uint32_t)b, (int)(uint32_t)(b >> 32), (int)num_bytes, 0x00020000};
+}
+
+// 16 bytes per lane from rsrc + voff into LDS at lds_addr + 16 * lane.  Inline
+// asm, so that the compiler does not wait for every transfer before each LDS
+// read; the kernel waits with explicit counts.
+__device__ __forceinline__ void to_lds16(i32x4 rsrc, uint32_t lds_addr, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(rsrc)
+               : "memory");
+}
+
+// Wait until at most n transfers of this lane are outstanding.
+template <int n>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(n >= 0 && n < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Wait until at most the transfers of the last n stages this wave issued are
+// in flight (three per stage for a wave with a third transfer, else two).
+template <int n>
+__device__ __forceinline__ void stage_wait(bool third) {
+  if (third) vm_wait<n * kPerStage>();
+  else vm_wait<n * (kPerStage - 1)>();
+}
+
+// Barrier that the instruction scheduler may not move anything across; before
+// it, only the wave's last two stages of transfers stay in flight.
+__device__ __forceinline__ void half_barrier(bool third) {
+  stage_wait<2>(third);
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int BITS>
+struct GemmLds {
+  static constexpr int kCodeOps = (BITS + 1) / 2;          // 1 KB transfers of a stage's codes
+  static_assert(kCodeOps + 1 <= kGWaves, "one code or pairs transfer per wave");
+  static constexpr int kCodeSlot = kCodeOps * 1024;
+  static constexpr int kX = 0;
+  static constexpr int kB = kX + kXRing * kXSlot;
+  static constexpr int kC = kB + kBRing * kBSlot;
+  static constexpr int kMeta = kC + kCRing * kCodeSlot;     // (delta, z) slots of 1 KB, by stage
+  static constexpr int kBytes = kMeta + kCRing * 1024;
+  static_assert(kBytes <= 160 * 1024, "LDS of one CU");
+};
+
+template <typename S>
+__device__ __forceinline__ f32x16 mfma32(i32x4 a, i32x4 b, f32x16 c);
+template <>
+__device__ __forceinline__ f32x16 mfma32<_Float16>(i32x4 a, i32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, a),
+                                                __builtin_bit_cast(half8, b), c, 0, 0, 0);
+}
+template <>
+__device__ __forceinline__ f32x16 mfma32<__bf16>(i32x4 a, i32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Code t of 8 consecutive ones held in bits [t BITS, t BITS + BITS) of hi:lo.
+template <int BITS, int T>
+__device__ __forceinline__ uint32_t code_of(uint32_t lo, uint32_t hi) {
+  constexpr int b = T * BITS;
+  constexpr uint32_t mask = (1u << BITS) - 1u;
+  if constexpr (b + BITS <= 32) return (lo >> b) & mask;
+  else if constexpr (b >= 32) return (hi >> (b - 32)) & mask;
+  else return __builtin_amdgcn_alignbit(hi, lo, b) & mask;
+}
+
+// Pair P (codes 2P, 2P + 1) of 8 codes as two S values (c - z), exact.
+template <typename S, int BITS, int P>
+__device__ __forceinline__ uint32_t pair_of(uint32_t lo, uint32_t hi, half2v negz, int z) {
+  const uint32_t c0 = code_of<BITS, 2 * P>(lo, hi), c1 = code_of<BITS, 2 * P + 1>(lo, hi);
+  if constexpr (std::is_same<S, _Float16>::value) {
+    // 1024 + c is exact in fp16; adding -(1024 + z) is exact
+    const uint32_t v = c0 | (c1 << 16) | 0x64006400u;
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, v) + negz);
+  } else {
+    // small integers are exact in fp32 and their upper halves are exact bf16
+    const float f0 = (float)((int)c0 - z), f1 = (float)((int)c1 - z);
+    return __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+  }
+}
+
+template <typename S, int BITS>
+__global__ __launch_bounds__(kGThreads, 1) void lowbit_gemm_kernel(
+    const S* __restrict__ X, int64_t M, int64_t K, const uint32_t* __restrict__ codes_t,
+    const float2* __restrict__ meta_t, int64_t N, int lg_cpg, float* __restrict__ Y) {
+  using L = GemmLds<BITS>;
+  __shared__ __attribute__((aligned(1024))) char lds[L::kBytes];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2, w4 = wave & 3;
+  const int wm = grp * 128 + (w4 >> 1) * 64, wn = (w4 & 1) * 64;
+  const int64_t m0 = (int64_t)blockIdx.y * kGM, n0 = (int64_t)blockIdx.x * kGN;
+  const int chunks = (int)(K / 32), cmask = (1 << lg_cpg) - 1;
+  const int64_t rows = M - m0 < kGM ? M - m0 : kGM;
+  const i32x4 rx = byte_range(X + m0 * K, (uint32_t)(rows * K * (int64_t)sizeof(S)));
+  const uint32_t base = (uint32_t)(uintptr_t)lds;
+  const uint32_t lane16 = (uint32_t)lane * 16;
+  // Activation transfers: this lane's row and chunk in each of the wave's two
+  // 16-row slabs, as running offsets of the next stage to be issued.
+  uint32_t xoff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = 16 * (2 * wave + i) + (lane >> 2);
+    const int c = (lane & 3) ^ ((row >> 1) & 3);
+    xoff[i] = (uint32_t)(((int64_t)row * K + 8 * c) * (int64_t)sizeof(S));
+  }
+  // The wave's third transfer of stage s, fixed for the kernel: waves
+  // 0 .. kCodeOps - 1 fetch a kilobyte of the stage's codes, the next wave the
+  // (delta, z) pairs of the stage's group, the others have none.  For unit
+  // u = s >> a_shift: source a_src + u a_step.  32-bit wrap-around of a source
+  // offset can only touch stages past the end, which are never used.
+  const bool third = wave <= L::kCodeOps;
+  i32x4 a_rsrc;
+  uint32_t a_dst, a_dstride, a_src, a_step;
+  int a_shift;
+  if (wave < L::kCodeOps) {
+    a_rsrc = byte_range(codes_t, (uint32_t)((uint64_t)chunks * N * BITS * 4));
+    a_dst = base + L::kC + wave * 1024;
+    a_dstride = L::kCodeSlot;
+    a_src = (uint32_t)((uint64_t)n0 * BITS * 4) + wave * 1024;
+    a_step = (uint32_t)((uint64_t)N * BITS * 4);
+    a_shift = 0;
+  } else {
+    a_rsrc = byte_range(meta_t, (uint32_t)((uint64_t)(K >> (lg_cpg + 5)) * N * 8));
+    a_dst = base + L::kMeta;
+    a_dstride = 1024;
+    a_src = (uint32_t)((uint64_t)n0 * 8);
+    a_step = (uint32_t)((uint64_t)N * 8);
+    a_shift = lg_cpg;
+  }
+  int aux_s = 0, x_slot = 0;
+  auto issue_aux = [&]() {
+    if (third) {
+      const uint32_t u = (uint32_t)(aux_s >> a_shift);
+      to_lds16(a_rsrc, a_dst + (uint32_t)(aux_s & (kCRing - 1)) * a_dstride, a_src + u * a_step + lane16);
+    }
+    ++aux_s;
+  };
+  auto issue_x = [&]() {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      to_lds16(rx, base + L::kX + x_slot * kXSlot + (2 * wave + i) * 1024, xoff[i]);
+      xoff[i] += 32 * (uint32_t)sizeof(S);
+    }
+    x_slot = x_slot == kXRing - 1 ? 0 : x_slot + 1;
+  };
+  // Unpacking, split between the two groups: thread -> B row lr, codes
+  // [8 lq, 8 lq + 8) of the chunk for each of its group's two quarters, which
+  // sit in bits [8 lq BITS, 8 lq BITS + 8 BITS) of the row's words.
+  const int lr = tid & (kGN - 1);
+  const int lq = __builtin_amdgcn_readfirstlane((tid >> 7) & 1) + 2 * grp;
+  const int qbit = 8 * lq * BITS, qw = qbit >> 5, qoff = qbit & 31;
+  const int qw1 = qw + 1 < BITS ? qw + 1 : BITS - 1, qw2 = qw + 2 < BITS ? qw + 2 : BITS - 1;
+  struct Codes {
+    uint32_t w0, w1, w2;
+    int z;
+  };
+  auto dq_load = [&](int s) {
+    const uint32_t* cw =
+        reinterpret_cast<const uint32_t*>(lds + L::kC + (s & (kCRing - 1)) * L::kCodeSlot) + lr * BITS;
+    Codes c;
+    c.w0 = cw[qw];
+    c.w1 = cw[qw1];
+    c.w2 = BITS == 7 ? cw[qw2] : 0u;
+    c.z = (int)reinterpret_cast<const float2*>(lds + L::kMeta + (s & (kCRing - 1)) * 1024)[lr].y;
+    return c;
+  };
+  auto dq_store = [&](int s, const Codes& c) {
+    uint32_t lo, hi;
+    if constexpr (BITS == 2 || BITS == 4) {
+      lo = c.w0 >> qoff;
+      hi = 0u;
+    } else if constexpr (BITS == 7) {
+      lo = __builtin_amdgcn_alignbit(c.w1, c.w0, qoff);
+      hi = __builtin_amdgcn_alignbit(c.w2, c.w1, qoff);
+    } else {
+      lo = __builtin_amdgcn_alignbit(c.w1, c.w0, qoff);
+      hi = c.w1 >> qoff;
+    }
+    const int z = c.z;
+    const _Float16 nzh = (_Float16)(-(1024 + z));
+    const half2v negz = {nzh, nzh};
+    const i32x4 v = {(int)pair_of<S, BITS, 0>(lo, hi, negz, z), (int)pair_of<S, BITS, 1>(lo, hi, negz, z),
+                     (int)pair_of<S, BITS, 2>(lo, hi, negz, z), (int)pair_of<S, BITS, 3>(lo, hi, negz, z)};
+    *reinterpret_cast<i32x4*>(lds + L::kB + (s % kBRing) * kBSlot + g_off(lr, lq)) = v;
+  };
+  auto dequant = [&](int s) { dq_store(s, dq_load(s)); };
+  f32x16 acc[2][2], tot[2][2];
+  const f32x16 zero16 = {};
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      acc[i][j] = zero16;
+      tot[i][j] = zero16;
+    }
+  // fragment rows and 16-byte chunk of this lane: row l % 32, chunk 2 ks + l / 32
+  const int fr = lane & 31, fh = lane >> 5;
+  int a_frag[2], b_frag[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    a_frag[ks] = g_off(wm + fr, 2 * ks + fh);      // + 2048 for the second 32-row block
+    b_frag[ks] = g_off(wn + fr, 2 * ks + fh);
+  }
+  i32x4 fa[2][2], fb[2][2];
+  auto read_frags = [&](int s, int xslot) {
+    const char* A = lds + L::kX + xslot * kXSlot;
+    const char* B = lds + L::kB + (s % kBRing) * kBSlot;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        fa[i][ks] = *reinterpret_cast<const i32x4*>(A + a_frag[ks] + 2048 * i);
+        fb[i][ks] = *reinterpret_cast<const i32x4*>(B + b_frag[ks] + 2048 * i);
+      }
+  };
+  auto mfmas = [&](int s) {
+    if ((s & cmask) == 0) {
+      // a group's first stage: its sums start from zero
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) acc[i][jj] = mfma32<S>(fa[i][0], fb[jj][0], zero16);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) acc[i][jj] = mfma32<S>(fa[i][0], fb[jj][0], acc[i][jj]);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) acc[i][jj] = mfma32<S>(fa[i][1], fb[jj][1], acc[i][jj]);
+  };
+  // The group's sums of stage s times its delta, per output column, when s
+  // ends a group.
+  auto scale = [&](int s) {
+    if (((s + 1) & cmask) != 0) return;
+    const float2* meta = reinterpret_cast<const float2*>(lds + L::kMeta + (s & (kCRing - 1)) * 1024);
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const float d = meta[wn + 32 * jj + fr].x;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) tot[i][jj][e] = fmaf(d, acc[i][jj][e], tot[i][jj][e]);
+    }
+  };
+  // A wave's multiplying half of stage s: its MFMAs, with its share of the
+  // unpacking of stage s + 2 between them (the codes read first, the
+  // conversion after the first MFMAs, the store last).  Its working half: the
+  // fragment reads of stage f and the next stage's transfers first, then the
+  // group-end scaling of stage sc (if any) while those are in flight.  Work on
+  // stages past the end reads and writes only ring slots that are never used
+  // again.
+  auto multiply = [&](int s) {
+    const Codes c = dq_load(s + 2);
+    mfmas(s);
+    dq_store(s + 2, c);
+  };
+  auto work = [&](int f, int fslot, int sc, bool do_scale) {
+    read_frags(f, fslot);
+    issue_aux();
+    issue_x();
+    __builtin_amdgcn_sched_barrier(0);
+    if (do_scale) scale(sc);
+  };
+  // Prologue: codes and pairs of stages 0 .. 5 and activations of stages
+  // 0 .. 3, in the order the loop continues (stage t + 2's third transfer
+  // before stage t's activations).
+  issue_aux();
+  issue_aux();
+#pragma unroll
+  for (int t = 0; t < kXAhead; ++t) {
+    issue_aux();
+    issue_x();
+  }
+  stage_wait<kXAhead>(third);                // codes and pairs of stages 0 and 1
+  __syncthreads();
+  dequant(0);
+  dequant(1);
+  stage_wait<kXAhead - 1>(third);            // activations of stage 0
+  __syncthreads();
+  // Each group runs its own copy of the loop (same barriers in the same
+  // order), so that its registers are allocated for its own schedule.
+  auto run = [&](auto group) {
+    constexpr int G = decltype(group)::value;
+    int xr = 0;                              // activation slot of stage k + 1 (group 0) / k (group 1)
+    if constexpr (G == 0) {
+      read_frags(0, 0);
+      xr = 1;
+      for (int k = 0; k < chunks; ++k) {
+        multiply(k);                         // first half: multiply
+        half_barrier(third);
+        work(k + 1, xr, k, true);            // second half: work
+        xr = xr == kXRing - 1 ? 0 : xr + 1;
+        half_barrier(third);
+      }
+    } else {
+      for (int k = 0; k < chunks; ++k) {
+        work(k, xr, k - 1, k > 0);           // first half: work
+        xr = xr == kXRing - 1 ? 0 : xr + 1;
+        half_barrier(third);
+        multiply(k);                         // second half: multiply
+        half_barrier(third);
+      }
+      scale(chunks - 1);
+    }
+  };
+  if (grp == 0) run(std::integral_constant<int, 0>());
+  else run(std::integral_constant<int, 1>());
+  vm_wait<0>();                              // no transfer may outlive the workgroup
+  // lane l holds column l % 32 and rows 8 (e / 4) + 4 (l / 32) + e % 4 of a block
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int64_t n = n0 + wn + 32 * jj + fr;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t m = m0 + wm + 32 * i + 8 * (e >> 2) + 4 * fh + (e & 3);
+        if (m < M && n < N) Y[m * N + n] = tot[i][jj][e];
+      }
+    }
+}
+
+template <typename S, int BITS>
+hipError_t gemm_launch(const void* X, int64_t M, int64_t K, const uint32_t* codes_t,
+                       const float2* meta_t, int64_t N, int group, float* Y, hipStream_t st) {
+  ProfScope p("awq_lowbit_gemm", st);
+  const dim3 grid((unsigned)((N + kGN - 1) / kGN), (unsigned)((M + kGM - 1) / kGM));
+  const int lg_cpg = __builtin_ctz((unsigned)(group / 32));   // group is a power of two >= 32
+  lowbit_gemm_kernel<S, BITS><<<grid, kGThreads, 0, st>>>(static_cast<const S*>(X), M, K, codes_t,
+                                                          meta_t, N, lg_cpg, Y);
+  return hipGetLastError();
+}
+
+template <typename S>
+hipError_t gemm_bits(int bits, const void* X, int64_t M, int64_t K, const uint32_t* codes_t,
+                     const float2* meta_t, int64_t N, int group, float* Y, hipStream_t st) {
+  switch (bits) {
+    case 2: return gemm_launch<S, 2>(X, M, K, codes_t, meta_t, N, group, Y, st);
+    case 3: return gemm_launch<S, 3>(X, M, K, codes_t, meta_t, N, group, Y, st);
+    case 4: return gemm_launch<S, 4>(X, M, K, codes_t, meta_t, N, group, Y, st);
+    case 5: return gemm_launch<S, 5>(X, M, K, codes_t, meta_t, N, group, Y, st);
+    case 6: return gemm_launch<S, 6>(X, M, K, codes_t, meta_t, N, group, Y, st);
+    case 7: return gemm_launch<S, 7>(X, M, K, codes_t, meta_t, N, group, Y, st);
+    default: return gemm_launch<S, 8>(X, M, K, codes_t, meta_t, N, group, Y, st);
+  }
+}
+
 }  // namespace
 
 size_t lowbit_gemv_ws_bytes(int64_t M, int64_t N, int64_t K) {
@@ -349,6 +757,14 @@ hipError_t launch_lowbit_gemv(const void* X, awq_dtype_t dt, int64_t M, int64_t 
     case AWQ_F16: return gemv_bits<_Float16>(bits, X, M, K, codes_t, meta, N, group, Y, partials, st);
     default: return gemv_bits<__bf16>(bits, X, M, K, codes_t, meta, N, group, Y, partials, st);
   }
+}
+
+hipError_t launch_lowbit_gemm(const void* X, awq_dtype_t dt, int64_t M, int64_t K,
+                              const uint32_t* codes_t, const void* meta_t, int64_t N, int bits,
+                              int group, float* Y, hipStream_t st) {
+  const float2* meta = static_cast<const float2*>(meta_t);
+  if (dt == AWQ_F16) return gemm_bits<_Float16>(bits, X, M, K, codes_t, meta, N, group, Y, st);
+  return gemm_bits<__bf16>(bits, X, M, K, codes_t, meta, N, group, Y, st);
 }
 
 }  // namespace awq

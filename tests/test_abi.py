@@ -183,6 +183,31 @@ def test_lowbit_gemv_validation(over, status):
     assert _call("awq_lowbit_gemv", *_gemv_args(**over)) == status
 
 
+def _gemm_args(**over):
+    a = dict(X=FAKE, dt=1, M=300, K=256, codes_t=FAKE, meta_t=FAKE, N=300, bits=4, group=128,
+             Y=FAKE, stream=NULL)
+    a.update(over)
+    return tuple(a.values())
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(X=NULL), -1),
+    (dict(Y=NULL), -1),
+    (dict(M=0), -1),
+    (dict(M=65535 * 128 + 1), -2),            # beyond the activation-row tiles of one launch
+    (dict(K=(1 << 22) + 128, N=1), -2),       # a 256-row activation tile beyond 32-bit offsets
+    (dict(dt=0), -2),                         # fp32 activations: the GEMV takes them
+    (dict(dt=7), -1),
+    (dict(K=200), -1),
+    (dict(bits=1), -2),
+    (dict(group=16, K=256), -2),
+    (dict(meta_t=ctypes.c_void_p(0x1004)), -2),
+    (dict(X=ctypes.c_void_p(0x1008)), -2),
+])
+def test_lowbit_gemm_validation(over, status):
+    assert _call("awq_lowbit_gemm", *_gemm_args(**over)) == status
+
+
 @pytest.mark.parametrize("over,status", [
     (dict(codes=NULL), -1),
     (dict(bits=1), -2),

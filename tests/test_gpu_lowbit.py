@@ -161,3 +161,72 @@ def test_lowbit_gemv_consecutive_shapes_are_independent():
         alone = awq.awq_lowbit_gemv(Xs, codes_t, meta_t, bits, G)
         torch.cuda.synchronize()
         assert torch.equal(y, alone)
+
+
+# ---- the matrix-core form for many activation rows --------------------------
+
+GEMM_CASES = [
+    # dtype, bits, group, M, N, K
+    ("fp16", 4, 128, 300, 300, 1024),      # ragged activation and output tiles
+    ("bf16", 3, 64, 129, 513, 2048),
+    ("fp16", 2, 32, 1, 77, 96),            # one row, one partial tile each way
+    ("fp16", 8, 512, 200, 256, 512),       # one group per row, widest codes
+    ("bf16", 5, 256, 128, 128, 768),       # exactly one tile
+    ("fp16", 6, 32, 64, 1000, 160),
+    ("bf16", 7, 128, 513, 130, 1024),
+    ("fp16", 4, 128, 1024, 512, 4096),     # several tiles each way
+]
+
+
+@pytest.mark.parametrize("dtype,bits,group,M,N,K", GEMM_CASES)
+def test_lowbit_gemm_matches_oracle(dtype, bits, group, M, N, K):
+    log_case(test="lowbit_gemm", dtype=dtype, bits=bits, group=group, M=M, N=N, K=K)
+    Xn, s, codes, delta, zero = packed_layer(3 * N + K + bits, N, K, max(M, 16), dtype, bits, group)
+    codes_t, meta_t = awq.awq_lowbit_repack(torch.from_numpy(codes.view(np.int32)).cuda(),
+                                            torch.from_numpy(delta).cuda(),
+                                            torch.from_numpy(zero).cuda(), K, bits, group)
+    Xs = activations(Xn, s, M, dtype)
+    Y = awq.awq_lowbit_gemm(Xs.cuda(), codes_t, meta_t, bits, group)
+    torch.cuda.synchronize()
+    check(Y.cpu().numpy(), Xs, codes, delta, zero, bits, group)
+
+
+def test_lowbit_gemm_is_reproducible_and_matches_the_gemv_layer():
+    """Same inputs twice: identical bits; and the GEMV on the same operands is
+    the same layer (both within the bound of the exact product, so within
+    twice the bound of each other)."""
+    log_case(test="lowbit_gemm_repro")
+    M, N, K, bits, G = 40, 700, 2048, 4, 128
+    Xn, s, codes, delta, zero = packed_layer(12, N, K, M, "bf16", bits, G)
+    codes_t, meta_t = awq.awq_lowbit_repack(torch.from_numpy(codes.view(np.int32)).cuda(),
+                                            torch.from_numpy(delta).cuda(),
+                                            torch.from_numpy(zero).cuda(), K, bits, G)
+    Xs = activations(Xn, s, M, "bf16").cuda()
+    Y1 = awq.awq_lowbit_gemm(Xs, codes_t, meta_t, bits, G)
+    Y2 = awq.awq_lowbit_gemm(Xs, codes_t, meta_t, bits, G)
+    Yv = awq.awq_lowbit_gemv(Xs, codes_t, meta_t, bits, G)
+    torch.cuda.synchronize()
+    assert torch.equal(Y1, Y2)
+    Xa = Xs.cpu().to(torch.float32).numpy().astype(np.float64)
+    Wd = oracle.dequantize(codes, delta, zero, bits, G, K).astype(np.float64)
+    tol = 2 * (K + 2) * 2.0 ** -24 * (np.abs(Xa) @ np.abs(Wd).T)
+    assert np.all(np.abs(Y1.cpu().numpy().astype(np.float64) - Yv.cpu().numpy()) <= tol)
+
+
+@pytest.mark.parametrize("name,M", [("llama7b-qproj", 512), ("llama7b-down", 200),
+                                    ("70b-mlp", 256)])
+def test_lowbit_gemm_full_size(name, M):
+    """Full weight shapes with prefill-sized activation blocks, every
+    activation row checked on sampled output rows."""
+    spec = CONFIGS[name]
+    N, K, bits, G = spec.N, spec.K, spec.bits, spec.group
+    log_case(test="lowbit_gemm_full", name=name, M=M, N=N, K=K, bits=bits)
+    Xn, s, codes, delta, zero = packed_layer(spec.seed, N, K, M, spec.dtype, bits, G)
+    codes_t, meta_t = awq.awq_lowbit_repack(torch.from_numpy(codes.view(np.int32)).cuda(),
+                                            torch.from_numpy(delta).cuda(),
+                                            torch.from_numpy(zero).cuda(), K, bits, G)
+    Xs = activations(Xn, s, M, spec.dtype)
+    Y = awq.awq_lowbit_gemm(Xs.cuda(), codes_t, meta_t, bits, G)
+    torch.cuda.synchronize()
+    rows = np.concatenate([np.arange(0, 64), np.arange(N // 2, N // 2 + 64), np.arange(N - 64, N)])
+    check(Y.cpu().numpy(), Xs, codes, delta, zero, bits, G, rows=rows)
