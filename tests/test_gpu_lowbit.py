@@ -175,6 +175,8 @@ GEMM_CASES = [
     ("fp16", 6, 32, 64, 1000, 160),
     ("bf16", 7, 128, 513, 130, 1024),
     ("fp16", 4, 128, 1024, 512, 4096),     # several tiles each way
+    ("bf16", 8, 32, 33, 129, 32),          # a single 32-column stage, widest codes in bf16
+    ("fp16", 5, 64, 257, 64, 64),          # two stages, one row past a 256-row tile, N below a tile
 ]
 
 
