@@ -193,7 +193,7 @@ __global__ __launch_bounds__(kRows) void lowbit_gemv_kernel(
       const int j = c0 + u;
       if (j >= c_end) break;
       const int kl = (j - c_begin) * 32;      // column of the chunk inside the staged block
-      if (kF32) {
+      if constexpr (kF32) {
         // fp32 activations: plain fp32 products of x and the exact (c - z)
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
@@ -203,7 +203,7 @@ __global__ __launch_bounds__(kRows) void lowbit_gemv_kernel(
         }
       } else {
         uint32_t pr[16];
-        if (kHalf) {
+        if constexpr (kHalf) {
           const _Float16 nz = (_Float16)(-(1024.0f + g[u].y));
           const half2v negz = {nz, nz};
 #pragma unroll
