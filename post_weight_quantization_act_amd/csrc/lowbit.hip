@@ -26,6 +26,7 @@
 // last workgroup of a row block add them instead needs a device-scope fence
 // per workgroup to make the partials visible across XCDs, which measured
 // slower than the second launch.)
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -696,6 +697,244 @@ __global__ __launch_bounds__(kGThreads, 1) void lowbit_gemm_kernel(
     }
 }
 
+// ---- small-M layer on the matrix cores --------------------------------------------
+// Up to 64 activation rows.  The GEMV's cost is vector work that grows with
+// the rows (one v_dot2 per pair of codes per row); here every code is unpacked
+// once, in registers, by the lane whose MFMA fragment holds it, and the matrix
+// cores do the multiply-adds for all rows.  Workgroup: 4 waves, each owning 32
+// output rows (the weight side of v_mfma_f32_32x32x16), MB blocks of 32
+// activation rows (rows past M are zero).  The k order inside a 16-deep MFMA
+// step is free as long as both operands agree: lane half h takes codes
+// [16 h, 16 h + 16) of each 32-column chunk (k step t takes 8 of them), so its
+// codes are one run of 16 fields: ceil(bits / 2) words of the repacked layout
+// and one funnel shift.  The activations go through LDS 256 columns at a time
+// (double-buffered, staged through registers a fill ahead; 16-byte chunk c of
+// row m at c ^ (m % 32)).  The codes and (delta, z) pairs of stage s + 2 are
+// loaded while stage s is multiplied.  Same arithmetic as the GEMV: exact
+// products x (c - z) summed in fp32 per group, one product by delta per group
+// and output (or per split end), k-splits summed in order by a second kernel.
+constexpr int kSmRows = 128;                 // output rows per workgroup
+constexpr int kSmStages = 8;                 // 32-column stages per activation fill
+constexpr int kSmCols = kSmStages * 32;      // columns per fill
+constexpr int kSmTarget = 1024;              // workgroups aimed at
+constexpr int kSmMinM = 5;                   // below this the vector kernel is faster
+constexpr int64_t kGemmMaxK = 1ll << 22;     // the large-tile kernel's limits (32-bit tile offsets,
+constexpr int64_t kGemmMaxM = 65535ll * 128; // activation-row tiles on grid y)
+constexpr int kSmMaxM = 64;
+
+// Code T of 16 consecutive ones held in bits [T BITS, T BITS + BITS) of sw.
+template <int BITS, int NW, int T>
+__device__ __forceinline__ uint32_t code_in(const uint32_t (&sw)[NW]) {
+  constexpr int b = T * BITS, w = b >> 5, o = b & 31;
+  constexpr uint32_t mask = (1u << BITS) - 1u;
+  if constexpr (o + BITS <= 32) return (sw[w] >> o) & mask;
+  else return __builtin_amdgcn_alignbit(sw[w + 1], sw[w], o) & mask;
+}
+
+// Codes 2P and 2P + 1 of the run as two S values (c - z), exact.
+template <typename S, int BITS, int NW, int P>
+__device__ __forceinline__ int small_pair(const uint32_t (&sw)[NW], half2v negz, int z) {
+  const uint32_t c0 = code_in<BITS, NW, 2 * P>(sw), c1 = code_in<BITS, NW, 2 * P + 1>(sw);
+  if constexpr (std::is_same<S, _Float16>::value) {
+    const uint32_t v = c0 | (c1 << 16) | 0x64006400u;
+    return (int)__builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, v) + negz);
+  } else {
+    const float f0 = (float)((int)c0 - z), f1 = (float)((int)c1 - z);
+    return (int)__builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+  }
+}
+
+template <typename S, int BITS, int MB>
+__global__ __launch_bounds__(256) void lowbit_small_kernel(
+    const S* __restrict__ X, int64_t M, int64_t K, const uint32_t* __restrict__ codes_t,
+    const float2* __restrict__ meta_t, int64_t N, int lg_cpg, int cps,
+    float* __restrict__ partials, float* __restrict__ Y) {
+  constexpr int NW = (BITS + 1) / 2;          // words holding a lane's 16 codes
+  constexpr int kXRows = 32 * MB;
+  constexpr int kPer = kXRows * 32 / 256;     // 16-byte activation chunks per thread and fill
+  __shared__ __attribute__((aligned(16))) char xs[2][kXRows * kSmCols * 2];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int fr = lane & 31, h = lane >> 5;
+  const int64_t n = (int64_t)blockIdx.x * kSmRows + wave * 32 + fr;
+  const int64_t nc = n < N ? n : N - 1;       // rows past N load row N - 1 (never stored)
+  const int chunks = (int)(K / 32), cmask = (1 << lg_cpg) - 1;
+  const int split = blockIdx.y;
+  const int s0 = split * cps, s1 = min(chunks, s0 + cps);
+  const int nfill = (s1 - s0 + kSmStages - 1) / kSmStages;
+  const int qbit = 16 * h * BITS, qw = qbit >> 5, qoff = qbit & 31;
+
+  i32x4 xr[kPer];
+  auto load_x = [&](int f) {
+    const int64_t col0 = (int64_t)(s0 + kSmStages * f) * 32;
+#pragma unroll
+    for (int p = 0; p < kPer; ++p) {
+      const int idx = tid + 256 * p, row = idx >> 5, c = idx & 31;
+      const int64_t col = col0 + 8 * c;
+      xr[p] = (row < M && col < K) ? *reinterpret_cast<const i32x4*>(X + row * K + col)
+                                   : i32x4{0, 0, 0, 0};
+    }
+  };
+  auto store_x = [&](int buf) {
+#pragma unroll
+    for (int p = 0; p < kPer; ++p) {
+      const int idx = tid + 256 * p, row = idx >> 5, c = idx & 31;
+      *reinterpret_cast<i32x4*>(xs[buf] + row * 512 + 16 * (c ^ (row & 31))) = xr[p];
+    }
+  };
+  uint32_t cw[4][NW];
+  float2 mt[4];
+  auto load_codes = [&](int s, int set) {
+    const int sc = s < s1 ? s : s1 - 1;
+    const uint32_t* cp = codes_t + ((int64_t)sc * N + nc) * BITS + qw;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) cw[set][i] = cp[i];
+    mt[set] = meta_t[(int64_t)(sc >> lg_cpg) * N + nc];
+  };
+  f32x16 acc[MB], tot[MB];
+  const f32x16 zero16 = {};
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+    acc[i] = zero16;
+    tot[i] = zero16;
+  }
+  // one stage: unpack this lane's 16 codes, read the activation fragments,
+  // multiply; scale the group's sums at a group or split end
+  auto stage = [&](int s, int set, const char* xb, int u) {
+    uint32_t sw[NW];
+    if constexpr (BITS % 2 == 1) {
+#pragma unroll
+      for (int i = 0; i + 1 < NW; ++i) sw[i] = __builtin_amdgcn_alignbit(cw[set][i + 1], cw[set][i], qoff);
+      sw[NW - 1] = cw[set][NW - 1] >> qoff;
+    } else {
+#pragma unroll
+      for (int i = 0; i < NW; ++i) sw[i] = cw[set][i];
+    }
+    const int z = (int)mt[set].y;
+    const _Float16 nzh = (_Float16)(-(1024 + z));
+    const half2v negz = {nzh, nzh};
+    const i32x4 fb0 = {small_pair<S, BITS, NW, 0>(sw, negz, z), small_pair<S, BITS, NW, 1>(sw, negz, z),
+                       small_pair<S, BITS, NW, 2>(sw, negz, z), small_pair<S, BITS, NW, 3>(sw, negz, z)};
+    const i32x4 fb1 = {small_pair<S, BITS, NW, 4>(sw, negz, z), small_pair<S, BITS, NW, 5>(sw, negz, z),
+                       small_pair<S, BITS, NW, 6>(sw, negz, z), small_pair<S, BITS, NW, 7>(sw, negz, z)};
+    i32x4 fa[MB][2];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int row = 32 * mb + fr, c = 4 * u + 2 * h + t;
+        fa[mb][t] = *reinterpret_cast<const i32x4*>(xb + row * 512 + 16 * (c ^ fr));
+      }
+    if (s == s0 || (s & cmask) == 0) {
+      // a group's (or the split's) first stage: its sums start from zero
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) acc[mb] = mfma32<S>(fa[mb][0], fb0, zero16);
+    } else {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) acc[mb] = mfma32<S>(fa[mb][0], fb0, acc[mb]);
+    }
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[mb] = mfma32<S>(fa[mb][1], fb1, acc[mb]);
+    if (s == s1 - 1 || ((s + 1) & cmask) == 0) {
+      const float d = mt[set].x;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) tot[mb][e] = fmaf(d, acc[mb][e], tot[mb][e]);
+    }
+  };
+  load_x(0);
+  load_codes(s0, 0);
+  load_codes(s0 + 1, 1);
+  store_x(0);
+  __syncthreads();
+  for (int f = 0; f < nfill; ++f) {
+    const int buf = f & 1;
+    if (f + 1 < nfill) load_x(f + 1);
+#pragma unroll
+    for (int u = 0; u < kSmStages; ++u) {
+      const int s = s0 + kSmStages * f + u;
+      load_codes(s + 2, (u + 2) & 3);
+      if (s < s1) stage(s, u & 3, xs[buf], u);
+    }
+    if (f + 1 < nfill) store_x(buf ^ 1);
+    __syncthreads();
+  }
+  if (n >= N) return;
+  float* dst = gridDim.y == 1 ? Y : partials + (int64_t)split * M * N;
+  // lane l holds column l % 32 and rows 8 (e / 4) + 4 (l / 32) + e % 4 of a block
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int64_t m = 32 * mb + 8 * (e >> 2) + 4 * h + (e & 3);
+      if (m < M) dst[m * N + n] = tot[mb][e];
+    }
+}
+
+// k-splits of the small-M kernel: enough workgroups to fill the chip, at least
+// one activation fill per split, and at most K / (32 M) splits (the partial
+// sums, S M N fp32 written and read back, then stay below the bytes of the
+// weights at 8 bits).
+Split small_split(int64_t M, int64_t N, int64_t K) {
+  const int64_t chunks = K / 32;
+  const int64_t tiles = (N + kSmRows - 1) / kSmRows;
+  int64_t s = (kSmTarget + tiles - 1) / tiles;
+  const int64_t s_fill = chunks / kSmStages > 0 ? chunks / kSmStages : 1;
+  const int64_t s_traffic = K / (32 * M) > 0 ? K / (32 * M) : 1;
+  s = std::min(s, std::min(s_fill, s_traffic));
+  if (s < 1) s = 1;
+  const int64_t cps = (chunks + s - 1) / s;
+  s = (chunks + cps - 1) / cps;
+  return Split{(int)s, (int)cps};
+}
+
+// fp16 / bf16 activations, 5 to 64 rows: the unpacking is paid once per code
+// here, once per code and row block of 8 in the vector kernel, which is the
+// faster one for 1 to 4 rows (less work per code, no MFMA padding).
+bool use_small(awq_dtype_t dt, int64_t M) { return dt != AWQ_F32 && M >= kSmMinM && M <= kSmMaxM; }
+
+template <typename S, int BITS>
+hipError_t small_launch(const void* X, int64_t M, int64_t K, const uint32_t* codes_t,
+                        const float2* meta_t, int64_t N, int group, float* Y, float* partials,
+                        hipStream_t st) {
+  const Split sp = small_split(M, N, K);
+  const int lg_cpg = __builtin_ctz((unsigned)(group / 32));
+  const dim3 grid((unsigned)((N + kSmRows - 1) / kSmRows), (unsigned)sp.s);
+  {
+    ProfScope p("awq_lowbit_gemv", st);
+    if (M <= 32)
+      lowbit_small_kernel<S, BITS, 1><<<grid, 256, 0, st>>>(static_cast<const S*>(X), M, K, codes_t,
+                                                             meta_t, N, lg_cpg, sp.cps, partials, Y);
+    else
+      lowbit_small_kernel<S, BITS, 2><<<grid, 256, 0, st>>>(static_cast<const S*>(X), M, K, codes_t,
+                                                             meta_t, N, lg_cpg, sp.cps, partials, Y);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || sp.s == 1) return e;
+  const int64_t MN = M * N;
+  {
+    ProfScope p("awq_lowbit_reduce", st);
+    lowbit_reduce_kernel<<<(unsigned)((MN + 255) / 256), 256, 0, st>>>(partials, sp.s, MN, Y);
+  }
+  return hipGetLastError();
+}
+
+template <typename S>
+hipError_t small_bits(int bits, const void* X, int64_t M, int64_t K, const uint32_t* codes_t,
+                      const float2* meta_t, int64_t N, int group, float* Y, float* partials,
+                      hipStream_t st) {
+  switch (bits) {
+    case 2: return small_launch<S, 2>(X, M, K, codes_t, meta_t, N, group, Y, partials, st);
+    case 3: return small_launch<S, 3>(X, M, K, codes_t, meta_t, N, group, Y, partials, st);
+    case 4: return small_launch<S, 4>(X, M, K, codes_t, meta_t, N, group, Y, partials, st);
+    case 5: return small_launch<S, 5>(X, M, K, codes_t, meta_t, N, group, Y, partials, st);
+    case 6: return small_launch<S, 6>(X, M, K, codes_t, meta_t, N, group, Y, partials, st);
+    case 7: return small_launch<S, 7>(X, M, K, codes_t, meta_t, N, group, Y, partials, st);
+    default: return small_launch<S, 8>(X, M, K, codes_t, meta_t, N, group, Y, partials, st);
+  }
+}
+
 template <typename S, int BITS>
 hipError_t gemm_launch(const void* X, int64_t M, int64_t K, const uint32_t* codes_t,
                        const float2* meta_t, int64_t N, int group, float* Y, hipStream_t st) {
@@ -724,8 +963,15 @@ hipError_t gemm_bits(int bits, const void* X, int64_t M, int64_t K, const uint32
 }  // namespace
 
 size_t lowbit_gemv_ws_bytes(int64_t M, int64_t N, int64_t K) {
+  // the larger of the two paths' needs: the vector kernel (every dtype) and
+  // the matrix-core kernel (fp16 / bf16 activations, M <= 64)
   const Split sp = choose_split(N, K);
-  return sp.s == 1 ? 0 : (size_t)sp.s * (size_t)M * (size_t)N * sizeof(float);
+  size_t need = sp.s == 1 ? 0 : (size_t)sp.s * (size_t)M * (size_t)N * sizeof(float);
+  if (M >= kSmMinM && M <= kSmMaxM) {
+    const Split ss = small_split(M, N, K);
+    if (ss.s > 1) need = std::max(need, (size_t)ss.s * (size_t)M * (size_t)N * sizeof(float));
+  }
+  return need;
 }
 
 hipError_t launch_lowbit_repack(const uint32_t* codes, const float* scales, const uint8_t* zeros,
@@ -752,6 +998,12 @@ hipError_t launch_lowbit_gemv(const void* X, awq_dtype_t dt, int64_t M, int64_t 
                               int group, float* Y, void* ws, hipStream_t st) {
   const float2* meta = static_cast<const float2*>(meta_t);
   float* partials = static_cast<float*>(ws);
+  if (use_small(dt, M)) {
+    if (dt == AWQ_F16) return small_bits<_Float16>(bits, X, M, K, codes_t, meta, N, group, Y, partials, st);
+    return small_bits<__bf16>(bits, X, M, K, codes_t, meta, N, group, Y, partials, st);
+  }
+  if (dt != AWQ_F32 && M > kSmMaxM && K <= kGemmMaxK && M <= kGemmMaxM)
+    return launch_lowbit_gemm(X, dt, M, K, codes_t, meta_t, N, bits, group, Y, st);
   switch (dt) {
     case AWQ_F32: return gemv_bits<float>(bits, X, M, K, codes_t, meta, N, group, Y, partials, st);
     case AWQ_F16: return gemv_bits<_Float16>(bits, X, M, K, codes_t, meta, N, group, Y, partials, st);

@@ -78,6 +78,16 @@ CASES = [
     ("fp32", 6, 512, 5, 129, 1536),
     ("fp16", 7, 32, 1, 1000, 160),
     ("bf16", 8, 64, 16, 200, 11008 // 172 * 64),
+    # 5 to 64 rows of fp16 / bf16 activations take the matrix-core kernel
+    ("fp16", 4, 128, 5, 300, 1024),      # its smallest row count, ragged N
+    ("bf16", 3, 32, 33, 129, 2048),      # two 32-row activation blocks, one group per stage
+    ("fp16", 8, 512, 64, 256, 1536),     # its largest row count
+    ("fp16", 6, 64, 20, 1000, 320),      # one split of 10 stages: a partial activation fill
+    ("bf16", 7, 128, 48, 77, 4096),      # codes that straddle words at both lane halves
+    ("bf16", 5, 256, 9, 513, 2304),
+    # beyond 64 rows fp16 / bf16 activations take the large-tile kernel
+    ("bf16", 4, 128, 65, 300, 1024),
+    ("fp16", 3, 64, 300, 129, 512),
 ]
 
 
@@ -124,7 +134,8 @@ def test_lowbit_gemv_is_reproducible_and_alpha_zero_is_rtn():
 
 
 @pytest.mark.parametrize("name,M", [("llama7b-qproj", 1), ("llama7b-qproj", 8),
-                                    ("llama7b-upgate", 4), ("llama7b-down", 2), ("70b-mlp", 1)])
+                                    ("llama7b-upgate", 4), ("llama7b-down", 2), ("70b-mlp", 1),
+                                    ("llama7b-down", 32), ("70b-mlp", 64)])
 def test_lowbit_gemv_full_size(name, M):
     """The five layers' weight shapes at full size (256 calibration tokens for
     the scales), packed by the oracle, checked on sampled output rows."""
