@@ -872,18 +872,19 @@ __global__ __launch_bounds__(256) void lowbit_small_kernel(
     }
 }
 
-// k-splits of the small-M kernel: enough workgroups to fill the chip, at least
-// one activation fill per split, and at most K / (32 M) splits (the partial
-// sums, S M N fp32 written and read back, then stay below the bytes of the
-// weights at 8 bits).
+// k-splits of the small-M kernel: the largest power of two that keeps about
+// kSmTarget workgroups, at least one activation fill per split, and the
+// partial sums (S M N fp32, written and read back) under 64 MiB.  A power of
+// two keeps the splits whole numbers of fills where K allows; a sweep of S on
+// the layer shapes puts this within about 10% of the best split everywhere.
 Split small_split(int64_t M, int64_t N, int64_t K) {
   const int64_t chunks = K / 32;
   const int64_t tiles = (N + kSmRows - 1) / kSmRows;
-  int64_t s = (kSmTarget + tiles - 1) / tiles;
-  const int64_t s_fill = chunks / kSmStages > 0 ? chunks / kSmStages : 1;
-  const int64_t s_traffic = K / (32 * M) > 0 ? K / (32 * M) : 1;
-  s = std::min(s, std::min(s_fill, s_traffic));
-  if (s < 1) s = 1;
+  int64_t lim = (kSmTarget + tiles - 1) / tiles;
+  lim = std::min(lim, chunks / kSmStages);
+  lim = std::min(lim, (int64_t)(64ll << 20) / (M * N * 8));
+  int64_t s = 1;
+  while (2 * s <= lim) s *= 2;
   const int64_t cps = (chunks + s - 1) / s;
   s = (chunks + cps - 1) / cps;
   return Split{(int)s, (int)cps};
