@@ -122,7 +122,7 @@ def bench_lowbit(args) -> None:
         codes, scales, zeros = awq.awq_quantize_pack(W, torch.ones(K, device=dev), b, G)
         codes_t, meta_t = awq.awq_lowbit_repack(codes, scales, zeros, K, b, G)
         Wt = W.t().contiguous()
-        for M in (1, 4, 16, 64):
+        for M in (1, 4, 16, 64, 256, 1024):
             X = torch.randn(M, K, device=dev).to(dt)
             ws = torch.empty(max(1, awq.awq_lowbit_gemv_workspace_size(M, N, K)),
                              dtype=torch.uint8, device=dev)

@@ -281,10 +281,11 @@ awq_status_t awq_salient_keep_loss(const void* W, const void* X, awq_dtype_t dty
  *   bytes, possibly 0, then the workspace may be NULL) and are added by a
  *   second kernel in split order.  Xs must be 16-byte aligned.  The kernel follows M and x_dtype:
  *   fp32 activations, or 1 to 4 rows, take a vector kernel (the packed weights read once per 8
- *   rows); 5 to 64 fp16 / bf16 rows take a matrix-core kernel that unpacks every code once for
- *   all rows; more fp16 / bf16 rows take awq_lowbit_gemm's kernel (no workspace used).  All three
- *   sum exact products in fp32 with one product by delta per group, so one error bound covers
- *   them, but their summation orders differ.
+ *   rows); from 5 fp16 / bf16 rows a matrix-core kernel unpacks every code once per tile of up
+ *   to 96 rows; beyond 1024 rows, or from 65 rows once ceil(N/128) * ceil(M/256) >= 200,
+ *   awq_lowbit_gemm's kernel runs (no workspace used).  All three sum exact products in fp32
+ *   with one product by delta per group, so one error bound covers them, but their summation
+ *   orders differ.  The workspace size covers whichever kernel the sizes select for any dtype.
  * ------------------------------------------------------------------------ */
 awq_status_t awq_lowbit_repack(const uint32_t* codes, const float* scales, const uint8_t* zeros,
                                int64_t N, int64_t K, int bits, int group,
@@ -298,8 +299,8 @@ awq_status_t awq_lowbit_gemv(const void* X, awq_dtype_t x_dtype, int64_t M, int6
  *   a few tens up): the same Y, the same repacked operands, the same exact
  *   products x (c - z) with fp32 sums and one product by delta per group and
  *   output, so the same error bound as awq_lowbit_gemv, which itself calls
- *   this kernel beyond 64 fp16 / bf16 rows; at 5 to 64 rows awq_lowbit_gemv's
- *   matrix-core kernel is the faster one.  Runs on the matrix
+ *   this kernel for large fp16 / bf16 inputs; below that awq_lowbit_gemv's
+ *   kernels are the faster ones.  Runs on the matrix
  *   cores: each workgroup dequantises a 128-row tile of the packed weights
  *   into on-chip memory once and uses it for 256 activation rows.  x_dtype
  *   AWQ_F16 or AWQ_BF16 only (AWQ_ERR_UNSUPPORTED otherwise); Xs 16-byte

@@ -714,13 +714,11 @@ __global__ __launch_bounds__(kGThreads, 1) void lowbit_gemm_kernel(
 // products x (c - z) summed in fp32 per group, one product by delta per group
 // and output (or per split end), k-splits summed in order by a second kernel.
 constexpr int kSmRows = 128;                 // output rows per workgroup
-constexpr int kSmStages = 8;                 // 32-column stages per activation fill
-constexpr int kSmCols = kSmStages * 32;      // columns per fill
 constexpr int kSmTarget = 1024;              // workgroups aimed at
 constexpr int kSmMinM = 5;                   // below this the vector kernel is faster
 constexpr int64_t kGemmMaxK = 1ll << 22;     // the large-tile kernel's limits (32-bit tile offsets,
 constexpr int64_t kGemmMaxM = 65535ll * 128; // activation-row tiles on grid y)
-constexpr int kSmMaxM = 64;
+constexpr int kSmMaxM = 1024;
 
 // Code T of 16 consecutive ones held in bits [T BITS, T BITS + BITS) of sw.
 template <int BITS, int NW, int T>
@@ -744,15 +742,19 @@ __device__ __forceinline__ int small_pair(const uint32_t (&sw)[NW], half2v negz,
   }
 }
 
-template <typename S, int BITS, int MB>
-__global__ __launch_bounds__(256) void lowbit_small_kernel(
+// MB blocks of 32 activation rows per workgroup (grid z walks the row tiles),
+// FS 32-column stages per activation fill.
+template <typename S, int BITS, int MB, int FS>
+__global__ __launch_bounds__(256, 2) void lowbit_small_kernel(
     const S* __restrict__ X, int64_t M, int64_t K, const uint32_t* __restrict__ codes_t,
     const float2* __restrict__ meta_t, int64_t N, int lg_cpg, int cps,
     float* __restrict__ partials, float* __restrict__ Y) {
   constexpr int NW = (BITS + 1) / 2;          // words holding a lane's 16 codes
   constexpr int kXRows = 32 * MB;
-  constexpr int kPer = kXRows * 32 / 256;     // 16-byte activation chunks per thread and fill
-  __shared__ __attribute__((aligned(16))) char xs[2][kXRows * kSmCols * 2];
+  constexpr int kCPR = 4 * FS;                // 16-byte chunks per activation row and fill
+  constexpr int kRowB = 16 * kCPR;
+  constexpr int kPer = kXRows * kCPR / 256;   // chunks per thread and fill
+  __shared__ __attribute__((aligned(16))) char xs[2][kXRows * kRowB];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int fr = lane & 31, h = lane >> 5;
@@ -761,25 +763,26 @@ __global__ __launch_bounds__(256) void lowbit_small_kernel(
   const int chunks = (int)(K / 32), cmask = (1 << lg_cpg) - 1;
   const int split = blockIdx.y;
   const int s0 = split * cps, s1 = min(chunks, s0 + cps);
-  const int nfill = (s1 - s0 + kSmStages - 1) / kSmStages;
+  const int nfill = (s1 - s0 + FS - 1) / FS;
+  const int64_t m_base = (int64_t)blockIdx.z * kXRows;
   const int qbit = 16 * h * BITS, qw = qbit >> 5, qoff = qbit & 31;
 
   i32x4 xr[kPer];
   auto load_x = [&](int f) {
-    const int64_t col0 = (int64_t)(s0 + kSmStages * f) * 32;
+    const int64_t col0 = (int64_t)(s0 + FS * f) * 32;
 #pragma unroll
     for (int p = 0; p < kPer; ++p) {
-      const int idx = tid + 256 * p, row = idx >> 5, c = idx & 31;
-      const int64_t col = col0 + 8 * c;
-      xr[p] = (row < M && col < K) ? *reinterpret_cast<const i32x4*>(X + row * K + col)
-                                   : i32x4{0, 0, 0, 0};
+      const int idx = tid + 256 * p, row = idx / kCPR, c = idx % kCPR;
+      const int64_t col = col0 + 8 * c, m = m_base + row;
+      xr[p] = (m < M && col < K) ? *reinterpret_cast<const i32x4*>(X + m * K + col)
+                                 : i32x4{0, 0, 0, 0};
     }
   };
   auto store_x = [&](int buf) {
 #pragma unroll
     for (int p = 0; p < kPer; ++p) {
-      const int idx = tid + 256 * p, row = idx >> 5, c = idx & 31;
-      *reinterpret_cast<i32x4*>(xs[buf] + row * 512 + 16 * (c ^ (row & 31))) = xr[p];
+      const int idx = tid + 256 * p, row = idx / kCPR, c = idx % kCPR;
+      *reinterpret_cast<i32x4*>(xs[buf] + row * kRowB + 16 * (c ^ (row & (kCPR - 1)))) = xr[p];
     }
   };
   uint32_t cw[4][NW];
@@ -823,7 +826,7 @@ __global__ __launch_bounds__(256) void lowbit_small_kernel(
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const int row = 32 * mb + fr, c = 4 * u + 2 * h + t;
-        fa[mb][t] = *reinterpret_cast<const i32x4*>(xb + row * 512 + 16 * (c ^ fr));
+        fa[mb][t] = *reinterpret_cast<const i32x4*>(xb + row * kRowB + 16 * (c ^ (fr & (kCPR - 1))));
       }
     if (s == s0 || (s & cmask) == 0) {
       // a group's (or the split's) first stage: its sums start from zero
@@ -852,8 +855,8 @@ __global__ __launch_bounds__(256) void lowbit_small_kernel(
     const int buf = f & 1;
     if (f + 1 < nfill) load_x(f + 1);
 #pragma unroll
-    for (int u = 0; u < kSmStages; ++u) {
-      const int s = s0 + kSmStages * f + u;
+    for (int u = 0; u < FS; ++u) {
+      const int s = s0 + FS * f + u;
       load_codes(s + 2, (u + 2) & 3);
       if (s < s1) stage(s, u & 3, xs[buf], u);
     }
@@ -867,10 +870,19 @@ __global__ __launch_bounds__(256) void lowbit_small_kernel(
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const int64_t m = 32 * mb + 8 * (e >> 2) + 4 * h + (e & 3);
+      const int64_t m = m_base + 32 * mb + 8 * (e >> 2) + 4 * h + (e & 3);
       if (m < M) dst[m * N + n] = tot[mb][e];
     }
 }
+
+// Activation-row blocks per workgroup and stages per fill, by M: one or two
+// 32-row blocks with 256-column fills up to 64 rows; beyond, three blocks (a
+// 96-row tile per workgroup, grid z over the tiles: four would not fit two
+// waves per SIMD without spilling) with 128-column fills.
+struct SmallShape {
+  int mb, fs;
+};
+SmallShape small_shape(int64_t M) { return M <= 32 ? SmallShape{1, 8} : M <= 64 ? SmallShape{2, 8} : SmallShape{3, 4}; }
 
 // k-splits of the small-M kernel: the largest power of two that keeps about
 // kSmTarget workgroups, at least one activation fill per split, and the
@@ -879,9 +891,10 @@ __global__ __launch_bounds__(256) void lowbit_small_kernel(
 // the layer shapes puts this within about 10% of the best split everywhere.
 Split small_split(int64_t M, int64_t N, int64_t K) {
   const int64_t chunks = K / 32;
-  const int64_t tiles = (N + kSmRows - 1) / kSmRows;
+  const SmallShape sh = small_shape(M);
+  const int64_t tiles = (N + kSmRows - 1) / kSmRows * ((M + 32 * sh.mb - 1) / (32 * sh.mb));
   int64_t lim = (kSmTarget + tiles - 1) / tiles;
-  lim = std::min(lim, chunks / kSmStages);
+  lim = std::min(lim, chunks / sh.fs);
   lim = std::min(lim, (int64_t)(64ll << 20) / (M * N * 8));
   int64_t s = 1;
   while (2 * s <= lim) s *= 2;
@@ -890,26 +903,40 @@ Split small_split(int64_t M, int64_t N, int64_t K) {
   return Split{(int)s, (int)cps};
 }
 
-// fp16 / bf16 activations, 5 to 64 rows: the unpacking is paid once per code
-// here, once per code and row block of 8 in the vector kernel, which is the
-// faster one for 1 to 4 rows (less work per code, no MFMA padding).
-bool use_small(awq_dtype_t dt, int64_t M) { return dt != AWQ_F32 && M >= kSmMinM && M <= kSmMaxM; }
+// fp16 / bf16 activations from 5 rows: the unpacking is paid once per code and
+// row tile here, once per code and row block of 8 in the vector kernel, which
+// is the faster one for 1 to 4 rows (less work per code, no MFMA padding).
+// Beyond 64 rows the large-tile kernel (unpacking amortised over 256 rows)
+// wins once it has enough tiles to fill the chip (measured on the layer
+// shapes: the 70B MLP layer at 256 rows, 224 tiles: 180 us there, 263 us here;
+// the 4096-row layers at 256 rows, 32 tiles: 34 us here, 82 us there).
+constexpr int64_t kGemmFullTiles = 200;
+bool use_small(awq_dtype_t dt, int64_t M, int64_t N) {
+  if (dt == AWQ_F32 || M < kSmMinM || M > kSmMaxM) return false;
+  return M <= 64 || (N + 127) / 128 * ((M + 255) / 256) < kGemmFullTiles;
+}
 
 template <typename S, int BITS>
 hipError_t small_launch(const void* X, int64_t M, int64_t K, const uint32_t* codes_t,
                         const float2* meta_t, int64_t N, int group, float* Y, float* partials,
                         hipStream_t st) {
   const Split sp = small_split(M, N, K);
+  const SmallShape sh = small_shape(M);
   const int lg_cpg = __builtin_ctz((unsigned)(group / 32));
-  const dim3 grid((unsigned)((N + kSmRows - 1) / kSmRows), (unsigned)sp.s);
+  const dim3 grid((unsigned)((N + kSmRows - 1) / kSmRows), (unsigned)sp.s,
+                  (unsigned)((M + 32 * sh.mb - 1) / (32 * sh.mb)));
+  const S* x = static_cast<const S*>(X);
   {
     ProfScope p("awq_lowbit_gemv", st);
-    if (M <= 32)
-      lowbit_small_kernel<S, BITS, 1><<<grid, 256, 0, st>>>(static_cast<const S*>(X), M, K, codes_t,
-                                                             meta_t, N, lg_cpg, sp.cps, partials, Y);
+    if (sh.mb == 1)
+      lowbit_small_kernel<S, BITS, 1, 8><<<grid, 256, 0, st>>>(x, M, K, codes_t, meta_t, N, lg_cpg,
+                                                                sp.cps, partials, Y);
+    else if (sh.mb == 2)
+      lowbit_small_kernel<S, BITS, 2, 8><<<grid, 256, 0, st>>>(x, M, K, codes_t, meta_t, N, lg_cpg,
+                                                                sp.cps, partials, Y);
     else
-      lowbit_small_kernel<S, BITS, 2><<<grid, 256, 0, st>>>(static_cast<const S*>(X), M, K, codes_t,
-                                                             meta_t, N, lg_cpg, sp.cps, partials, Y);
+      lowbit_small_kernel<S, BITS, 3, 4><<<grid, 256, 0, st>>>(x, M, K, codes_t, meta_t, N, lg_cpg,
+                                                                sp.cps, partials, Y);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || sp.s == 1) return e;
@@ -968,7 +995,7 @@ size_t lowbit_gemv_ws_bytes(int64_t M, int64_t N, int64_t K) {
   // the matrix-core kernel (fp16 / bf16 activations, M <= 64)
   const Split sp = choose_split(N, K);
   size_t need = sp.s == 1 ? 0 : (size_t)sp.s * (size_t)M * (size_t)N * sizeof(float);
-  if (M >= kSmMinM && M <= kSmMaxM) {
+  if (use_small(AWQ_F16, M, N)) {
     const Split ss = small_split(M, N, K);
     if (ss.s > 1) need = std::max(need, (size_t)ss.s * (size_t)M * (size_t)N * sizeof(float));
   }
@@ -999,11 +1026,11 @@ hipError_t launch_lowbit_gemv(const void* X, awq_dtype_t dt, int64_t M, int64_t 
                               int group, float* Y, void* ws, hipStream_t st) {
   const float2* meta = static_cast<const float2*>(meta_t);
   float* partials = static_cast<float*>(ws);
-  if (use_small(dt, M)) {
+  if (use_small(dt, M, N)) {
     if (dt == AWQ_F16) return small_bits<_Float16>(bits, X, M, K, codes_t, meta, N, group, Y, partials, st);
     return small_bits<__bf16>(bits, X, M, K, codes_t, meta, N, group, Y, partials, st);
   }
-  if (dt != AWQ_F32 && M > kSmMaxM && K <= kGemmMaxK && M <= kGemmMaxM)
+  if (dt != AWQ_F32 && M > 4 && K <= kGemmMaxK && M <= kGemmMaxM)
     return launch_lowbit_gemm(X, dt, M, K, codes_t, meta_t, N, bits, group, Y, st);
   switch (dt) {
     case AWQ_F32: return gemv_bits<float>(bits, X, M, K, codes_t, meta, N, group, Y, partials, st);

@@ -85,9 +85,14 @@ CASES = [
     ("fp16", 6, 64, 20, 1000, 320),      # one split of 10 stages: a partial activation fill
     ("bf16", 7, 128, 48, 77, 4096),      # codes that straddle words at both lane halves
     ("bf16", 5, 256, 9, 513, 2304),
-    # beyond 64 rows fp16 / bf16 activations take the large-tile kernel
+    # 65 to 1024 rows on layers too narrow to fill the chip with 256-row tiles:
+    # the matrix-core kernel with 96-row tiles
     ("bf16", 4, 128, 65, 300, 1024),
     ("fp16", 3, 64, 300, 129, 512),
+    ("bf16", 2, 32, 1024, 64, 96),
+    # beyond 1024 rows, or once its tiles fill the chip, the large-tile kernel
+    ("fp16", 4, 128, 1100, 130, 256),
+    ("bf16", 4, 128, 100, 25700, 128),   # 201 tiles of 128 x 256
 ]
 
 
@@ -135,7 +140,7 @@ def test_lowbit_gemv_is_reproducible_and_alpha_zero_is_rtn():
 
 @pytest.mark.parametrize("name,M", [("llama7b-qproj", 1), ("llama7b-qproj", 8),
                                     ("llama7b-upgate", 4), ("llama7b-down", 2), ("70b-mlp", 1),
-                                    ("llama7b-down", 32), ("70b-mlp", 64)])
+                                    ("llama7b-down", 32), ("70b-mlp", 64), ("llama7b-qproj", 256)])
 def test_lowbit_gemv_full_size(name, M):
     """The five layers' weight shapes at full size (256 calibration tokens for
     the scales), packed by the oracle, checked on sampled output rows."""
