@@ -124,7 +124,7 @@ def bench_lowbit(args) -> None:
         Wt = W.t().contiguous()
         for M in (1, 4, 16, 64, 256, 1024):
             X = torch.randn(M, K, device=dev).to(dt)
-            ws = torch.empty(max(1, awq.awq_lowbit_gemv_workspace_size(M, N, K)),
+            ws = torch.empty(max(1, awq.awq_lowbit_gemv_workspace_size(dt, M, N, K)),
                              dtype=torch.uint8, device=dev)
             Y = torch.empty(M, N, device=dev)
             us = timed(lambda: awq.awq_lowbit_gemv(X, codes_t, meta_t, b, G, out=Y, workspace=ws),

@@ -277,20 +277,20 @@ awq_status_t awq_salient_keep_loss(const void* W, const void* X, awq_dtype_t dty
  *   y = sum_g delta_g * sum_{k in g} x_k (c_k - z_g) with the integer
  *   differences and their products exact and the sums in fp32, added in a fixed
  *   order, so results are reproducible: K is split over workgroups whose
- *   partial sums go to the workspace (awq_lowbit_gemv_workspace_size(M, N, K)
- *   bytes, possibly 0, then the workspace may be NULL) and are added by a
+ *   partial sums go to the workspace (awq_lowbit_gemv_workspace_size(x_dtype,
+ *   M, N, K) bytes, possibly 0, then the workspace may be NULL) and are added by a
  *   second kernel in split order.  Xs must be 16-byte aligned.  The kernel follows M and x_dtype:
  *   fp32 activations, or 1 to 4 rows, take a vector kernel (the packed weights read once per 8
  *   rows); from 5 fp16 / bf16 rows a matrix-core kernel unpacks every code once per tile of up
  *   to 96 rows; beyond 1024 rows, or from 65 rows once ceil(N/128) * ceil(M/256) >= 200,
  *   awq_lowbit_gemm's kernel runs (no workspace used).  All three sum exact products in fp32
  *   with one product by delta per group, so one error bound covers them, but their summation
- *   orders differ.  The workspace size covers whichever kernel the sizes select for any dtype.
+ *   orders differ.  The workspace size is that of the kernel the dtype and sizes select.
  * ------------------------------------------------------------------------ */
 awq_status_t awq_lowbit_repack(const uint32_t* codes, const float* scales, const uint8_t* zeros,
                                int64_t N, int64_t K, int bits, int group,
                                uint32_t* codes_t, void* meta_t, hipStream_t stream);
-size_t awq_lowbit_gemv_workspace_size(int64_t M, int64_t N, int64_t K);
+size_t awq_lowbit_gemv_workspace_size(awq_dtype_t x_dtype, int64_t M, int64_t N, int64_t K);
 awq_status_t awq_lowbit_gemv(const void* X, awq_dtype_t x_dtype, int64_t M, int64_t K,
                              const uint32_t* codes_t, const void* meta_t, int64_t N, int bits,
                              int group, float* Y, void* workspace, size_t workspace_bytes,

@@ -90,7 +90,7 @@ _SIGS = {
     "awq_salient_keep_loss": ([_P, _P, _I32, _I64, _I64, _I64, _P, _I64, _I32, _I32, _P, _P, _P,
                                _SZ, _P], _I32),
     "awq_lowbit_repack": ([_P, _P, _P, _I64, _I64, _I32, _I32, _P, _P, _P], _I32),
-    "awq_lowbit_gemv_workspace_size": ([_I64, _I64, _I64], _SZ),
+    "awq_lowbit_gemv_workspace_size": ([_I32, _I64, _I64, _I64], _SZ),
     "awq_lowbit_gemv": ([_P, _I32, _I64, _I64, _P, _P, _I64, _I32, _I32, _P, _P, _SZ, _P], _I32),
     "awq_lowbit_gemm": ([_P, _I32, _I64, _I64, _P, _P, _I64, _I32, _I32, _P, _P], _I32),
     "awq_gptq_workspace_size": ([_I64, _I64, _I64], _SZ),
@@ -397,8 +397,8 @@ def awq_lowbit_repack(codes: torch.Tensor, scales: torch.Tensor, zeros: torch.Te
     return codes_t, meta_t
 
 
-def awq_lowbit_gemv_workspace_size(M: int, N: int, K: int) -> int:
-    return int(library().awq_lowbit_gemv_workspace_size(M, N, K))
+def awq_lowbit_gemv_workspace_size(dtype: torch.dtype, M: int, N: int, K: int) -> int:
+    return int(library().awq_lowbit_gemv_workspace_size(_DTYPES[dtype], M, N, K))
 
 
 def awq_lowbit_gemv(Xs: torch.Tensor, codes_t: torch.Tensor, meta_t: torch.Tensor, bits: int,
@@ -413,7 +413,7 @@ def awq_lowbit_gemv(Xs: torch.Tensor, codes_t: torch.Tensor, meta_t: torch.Tenso
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=Xs.device)
     if workspace is None:
-        need = awq_lowbit_gemv_workspace_size(M, N, K)
+        need = awq_lowbit_gemv_workspace_size(Xs.dtype, M, N, K)
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=Xs.device)
     _check(library().awq_lowbit_gemv(Xs.data_ptr(), _dtype(Xs), M, K, codes_t.data_ptr(),
                                      meta_t.data_ptr(), N, bits, group, out.data_ptr(),

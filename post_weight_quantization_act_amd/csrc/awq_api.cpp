@@ -621,9 +621,9 @@ awq_status_t awq_lowbit_repack(const uint32_t* codes, const float* scales, const
   AWQ_GUARD_END
 }
 
-size_t awq_lowbit_gemv_workspace_size(int64_t M, int64_t N, int64_t K) {
-  if (M < 1 || N < 1 || K < 32) return 0;
-  return awq::lowbit_gemv_ws_bytes(M, N, K);
+size_t awq_lowbit_gemv_workspace_size(awq_dtype_t x_dtype, int64_t M, int64_t N, int64_t K) {
+  if (!valid_dtype(x_dtype) || M < 1 || N < 1 || K < 32) return 0;
+  return awq::lowbit_gemv_ws_bytes(x_dtype, M, N, K);
 }
 
 awq_status_t awq_lowbit_gemv(const void* X, awq_dtype_t x_dtype, int64_t M, int64_t K,
@@ -637,7 +637,7 @@ awq_status_t awq_lowbit_gemv(const void* X, awq_dtype_t x_dtype, int64_t M, int6
   if (!X || !codes_t || !meta_t || !Y) return fail(AWQ_ERR_INVALID_ARG, "null pointer");
   if (!aligned(X, 16) || !aligned(codes_t, 4) || !aligned(meta_t, 8) || !aligned(Y, 4))
     return fail(AWQ_ERR_UNSUPPORTED, "X 16-byte, codes_t and Y 4-byte, meta_t 8-byte aligned");
-  const size_t need = awq::lowbit_gemv_ws_bytes(M, N, K);
+  const size_t need = awq::lowbit_gemv_ws_bytes(x_dtype, M, N, K);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(AWQ_ERR_WORKSPACE, "workspace of %zu bytes is below %zu", workspace_bytes, need);
   if (need > 0 && !aligned(workspace, 4))

@@ -122,7 +122,7 @@ hipError_t launch_quantize_pack(const void* W, awq_dtype_t dt, int64_t N, int64_
 hipError_t launch_lowbit_repack(const uint32_t* codes, const float* scales, const uint8_t* zeros,
                                 int64_t N, int64_t K, int bits, int group, uint32_t* codes_t,
                                 void* meta_t, hipStream_t st);
-size_t lowbit_gemv_ws_bytes(int64_t M, int64_t N, int64_t K);
+size_t lowbit_gemv_ws_bytes(awq_dtype_t dt, int64_t M, int64_t N, int64_t K);
 hipError_t launch_lowbit_gemv(const void* X, awq_dtype_t dt, int64_t M, int64_t K,
                               const uint32_t* codes_t, const void* meta_t, int64_t N, int bits,
                               int group, float* Y, void* ws, hipStream_t st);

@@ -990,16 +990,25 @@ hipError_t gemm_bits(int bits, const void* X, int64_t M, int64_t K, const uint32
 
 }  // namespace
 
-size_t lowbit_gemv_ws_bytes(int64_t M, int64_t N, int64_t K) {
-  // the larger of the two paths' needs: the vector kernel (every dtype) and
-  // the matrix-core kernel (fp16 / bf16 activations, M <= 64)
-  const Split sp = choose_split(N, K);
-  size_t need = sp.s == 1 ? 0 : (size_t)sp.s * (size_t)M * (size_t)N * sizeof(float);
-  if (use_small(AWQ_F16, M, N)) {
-    const Split ss = small_split(M, N, K);
-    if (ss.s > 1) need = std::max(need, (size_t)ss.s * (size_t)M * (size_t)N * sizeof(float));
+namespace {
+// The kernel a call of these sizes runs; the workspace size and the launch
+// both follow it.
+enum class Route { kVector, kSmall, kTiles };
+Route gemv_route(awq_dtype_t dt, int64_t M, int64_t N, int64_t K) {
+  if (use_small(dt, M, N)) return Route::kSmall;
+  if (dt != AWQ_F32 && M > 4 && K <= kGemmMaxK && M <= kGemmMaxM) return Route::kTiles;
+  return Route::kVector;
+}
+}  // namespace
+
+size_t lowbit_gemv_ws_bytes(awq_dtype_t dt, int64_t M, int64_t N, int64_t K) {
+  Split sp{1, 0};
+  switch (gemv_route(dt, M, N, K)) {
+    case Route::kSmall: sp = small_split(M, N, K); break;
+    case Route::kVector: sp = choose_split(N, K); break;
+    case Route::kTiles: break;                      // no partial sums
   }
-  return need;
+  return sp.s == 1 ? 0 : (size_t)sp.s * (size_t)M * (size_t)N * sizeof(float);
 }
 
 hipError_t launch_lowbit_repack(const uint32_t* codes, const float* scales, const uint8_t* zeros,
@@ -1026,12 +1035,12 @@ hipError_t launch_lowbit_gemv(const void* X, awq_dtype_t dt, int64_t M, int64_t 
                               int group, float* Y, void* ws, hipStream_t st) {
   const float2* meta = static_cast<const float2*>(meta_t);
   float* partials = static_cast<float*>(ws);
-  if (use_small(dt, M, N)) {
+  const Route r = gemv_route(dt, M, N, K);
+  if (r == Route::kSmall) {
     if (dt == AWQ_F16) return small_bits<_Float16>(bits, X, M, K, codes_t, meta, N, group, Y, partials, st);
     return small_bits<__bf16>(bits, X, M, K, codes_t, meta, N, group, Y, partials, st);
   }
-  if (dt != AWQ_F32 && M > 4 && K <= kGemmMaxK && M <= kGemmMaxM)
-    return launch_lowbit_gemm(X, dt, M, K, codes_t, meta_t, N, bits, group, Y, st);
+  if (r == Route::kTiles) return launch_lowbit_gemm(X, dt, M, K, codes_t, meta_t, N, bits, group, Y, st);
   switch (dt) {
     case AWQ_F32: return gemv_bits<float>(bits, X, M, K, codes_t, meta, N, group, Y, partials, st);
     case AWQ_F16: return gemv_bits<_Float16>(bits, X, M, K, codes_t, meta, N, group, Y, partials, st);

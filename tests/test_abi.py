@@ -222,11 +222,21 @@ def test_lowbit_repack_validation(over, status):
 
 
 def test_lowbit_gemv_workspace_size():
-    # one fp32 partial per (k-split, activation row, output row); none when K
-    # is not split
-    n = awq.awq_lowbit_gemv_workspace_size(4, 4096, 4096)
-    assert n > 0 and n % (4 * 4096 * 4) == 0
-    assert awq.awq_lowbit_gemv_workspace_size(1, 4096, 96) == 0
+    # one fp32 partial per (k-split, activation row, output row) of the kernel
+    # the dtype and sizes select; none when K is not split or the large-tile
+    # kernel runs
+    for dt in (torch.float32, torch.float16, torch.bfloat16):
+        n = awq.awq_lowbit_gemv_workspace_size(dt, 4, 4096, 4096)
+        assert n > 0 and n % (4 * 4096 * 4) == 0
+        assert awq.awq_lowbit_gemv_workspace_size(dt, 1, 4096, 96) == 0
+    # 4096 rows of a wide layer: the large-tile kernel, no workspace, for
+    # fp16 / bf16; the vector kernel's partial sums for fp32
+    assert awq.awq_lowbit_gemv_workspace_size(torch.float16, 4096, 28672, 8192) == 0
+    assert awq.awq_lowbit_gemv_workspace_size(torch.float32, 4096, 28672, 8192) > 0
+    # 5 to 64 fp16 rows: the matrix-core kernel's splits (at most 64 MiB of sums)
+    n = awq.awq_lowbit_gemv_workspace_size(torch.bfloat16, 64, 28672, 8192)
+    assert 0 < n <= 64 << 20
+    assert awq.awq_lowbit_gemv_workspace_size(torch.float16, 0, 4096, 4096) == 0
 
 
 @pytest.mark.parametrize("over,status", [
