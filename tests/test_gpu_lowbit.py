@@ -85,6 +85,9 @@ CASES = [
     ("fp16", 6, 64, 20, 1000, 320),      # one split of 10 stages: a partial activation fill
     ("bf16", 7, 128, 48, 77, 4096),      # codes that straddle words at both lane halves
     ("bf16", 5, 256, 9, 513, 2304),
+    ("fp16", 4, 32, 5, 1, 32),           # one output row, one 32-column stage
+    ("bf16", 6, 32, 64, 33, 64),         # N one past a 32-row wave, two stages
+    ("fp16", 2, 32, 7, 100, 288),        # a second fill holding a single stage
     # 65 to 1024 rows on layers too narrow to fill the chip with 256-row tiles:
     # the matrix-core kernel with 96-row tiles
     ("bf16", 4, 128, 65, 300, 1024),
