@@ -251,3 +251,26 @@ def test_lowbit_gemm_full_size(name, M):
     torch.cuda.synchronize()
     rows = np.concatenate([np.arange(0, 64), np.arange(N // 2, N // 2 + 64), np.arange(N - 64, N)])
     check(Y.cpu().numpy(), Xs, codes, delta, zero, bits, G, rows=rows)
+
+
+def test_lowbit_layer_random_shapes():
+    """Seeded random shapes across every kernel the layer call can pick (1-300
+    rows, fp32 / fp16 / bf16, bits 2-8, groups 32-512, ragged N and K), each
+    against the oracle's exact product under the same bound."""
+    rng = np.random.default_rng(2024)
+    for case in range(40):
+        dtype = ("fp32", "fp16", "bf16")[int(rng.integers(3))]
+        bits = int(rng.integers(2, 9))
+        group = int(2 ** rng.integers(5, 10))
+        K = group * int(rng.integers(1, 13 if group <= 128 else 5))
+        N = int(rng.integers(1, 701))
+        M = int(rng.choice([1, 2, 3, 4, 5, 7, 16, 31, 33, 64, 65, 97, 200, 300]))
+        log_case(test="lowbit_random", case=case, dtype=dtype, bits=bits, group=group, M=M, N=N, K=K)
+        Xn, s, codes, delta, zero = packed_layer(1000 + case, N, K, max(M, 16), dtype, bits, group)
+        codes_t, meta_t = awq.awq_lowbit_repack(torch.from_numpy(codes.view(np.int32)).cuda(),
+                                                torch.from_numpy(delta).cuda(),
+                                                torch.from_numpy(zero).cuda(), K, bits, group)
+        Xs = activations(Xn, s, M, dtype)
+        Y = awq.awq_lowbit_gemv(Xs.cuda(), codes_t, meta_t, bits, group)
+        torch.cuda.synchronize()
+        check(Y.cpu().numpy(), Xs, codes, delta, zero, bits, group)
