@@ -323,20 +323,25 @@ __global__ __launch_bounds__(kThreads) void damp_kernel(double* __restrict__ H, 
 }
 
 // ---- Cholesky of one diagonal block and its inverse --------------------------
-// One wave; lane r owns row r of the 64x64 block in registers (lower part
-// read only).  The factor L_pp itself is never needed again (the panel below
-// is solved with its inverse, the later updates use the solved panel), so the
-// block is overwritten with L_pp^-1 (zeros above the diagonal).
+// Four waves share the 64x64 block: lane r of every wave stands for row r,
+// wave q owns the sixteen columns 16q..16q+15 of that row in registers (lower
+// part read only).  The factor L_pp itself is never needed again (the panel
+// below is solved with its inverse, the later updates use the solved panel),
+// so the block is overwritten with L_pp^-1 (zeros above the diagonal).
 //
 // Both halves go four columns per step, the steps unrolled by template
 // recursion so every register index is static (a rolled loop would move the
-// row to scratch memory).  Factorisation step JB: every lane gathers the 4x4
-// diagonal block by readlane and factors it redundantly (1/sqrt from the
-// hardware estimate and two Newton steps), the rows below solve their four
-// entries against it, the four columns are published in LDS (row-major L, one
-// 32-byte write per lane) and every row updates its later entries with four
-// FMAs each.  Inverse step IB: lane c solves the 4x4 block for x_IB..x_IB+3
-// of column c of L^-1 and pushes them into the later rows.
+// row to scratch memory).  Factorisation step JB: the wave owning columns
+// JB..JB+3 gathers the 4x4 diagonal block by readlane and factors it in every
+// lane (1/sqrt from the hardware estimate and two Newton steps), the rows
+// below solve their four entries against it and the four columns are
+// published in LDS (row-major L, one 32-byte write per lane); after one
+// barrier every wave updates its own later columns with four FMAs each.
+// Inverse step IB: lane c now stands for column c of L^-1 and wave q owns its
+// rows 16q..16q+15; the wave owning rows IB..IB+3 solves the 4x4 block for
+// x_IB..x_IB+3, publishes them in LDS and every wave pushes them into its own
+// later rows.  Each entry sees the same operations in the same order as in a
+// one-wave sweep of the whole row, so the split changes no bit of the result.
 __device__ __forceinline__ double readlane64(double v, int lane) {
   const long long b = __double_as_longlong(v);
   const int lo = __builtin_amdgcn_readlane((int)b, lane);
@@ -357,111 +362,155 @@ __device__ __forceinline__ double rsqrt64(double x) {
   return y;
 }
 
-struct CholRow {
-  double a[kNb];
-};
+
+constexpr int kCq = 16;              // columns (rows, in the inverse) per wave
+constexpr int kQw = kNb / kCq;       // waves per block
 typedef double LRow[kNb + 2];
 
+// Columns i0..kCq-1 of this wave (global column 16q+i) take the rank-4 update
+// by the new columns JB..JB+3; w holds this row's own four new entries.
+template <int I0>
+__device__ __forceinline__ void chol_update(double* a, int kbase, int JB, d2 w0, d2 w1,
+                                            const LRow* Lr) {
+#pragma unroll
+  for (int i = I0; i < kCq; ++i) {
+    const int k = kbase + i;
+    const d2 u0 = *(const d2*)&Lr[k][JB], u1 = *(const d2*)&Lr[k][JB + 2];
+    double v = a[i];
+    v = fma(-w0.x, u0.x, v);
+    v = fma(-w0.y, u0.y, v);
+    v = fma(-w1.x, u1.x, v);
+    v = fma(-w1.y, u1.y, v);
+    a[i] = v;
+  }
+}
+
 template <int JB>
-__device__ __forceinline__ void chol_step(CholRow& st, int r, LRow* Lr, double* rdiag) {
+__device__ __forceinline__ void chol_step(double* a, int r, int q, LRow* Lr, double* rdiag) {
   if constexpr (JB < kNb) {
-    double* a = st.a;
-    double b[4][4], l[4][4], rr[4], x[4];
+    constexpr int qo = JB / kCq, li = JB % kCq;
+    if (q == qo) {
+      double b[4][4], l[4][4], rr[4], x[4];
 #pragma unroll
-    for (int p = 0; p < 4; ++p)
+      for (int p = 0; p < 4; ++p)
 #pragma unroll
-      for (int q = 0; q <= p; ++q) b[p][q] = readlane64(a[JB + q], JB + p);
+        for (int t = 0; t <= p; ++t) b[p][t] = readlane64(a[li + t], JB + p);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      double d = b[q][q];
+      for (int t = 0; t < 4; ++t) {
+        double d = b[t][t];
 #pragma unroll
-      for (int s = 0; s < q; ++s) d = fma(-l[q][s], l[q][s], d);
-      rr[q] = rsqrt64(d);
-      l[q][q] = d * rr[q];
+        for (int s = 0; s < t; ++s) d = fma(-l[t][s], l[t][s], d);
+        rr[t] = rsqrt64(d);
+        l[t][t] = d * rr[t];
 #pragma unroll
-      for (int p = q + 1; p < 4; ++p) {
-        double v = b[p][q];
+        for (int p = t + 1; p < 4; ++p) {
+          double v = b[p][t];
 #pragma unroll
-        for (int s = 0; s < q; ++s) v = fma(-l[p][s], l[q][s], v);
-        l[p][q] = v * rr[q];
+          for (int s = 0; s < t; ++s) v = fma(-l[p][s], l[t][s], v);
+          l[p][t] = v * rr[t];
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        double v = a[li + t];
+#pragma unroll
+        for (int s = 0; s < t; ++s) v = fma(-x[s], l[t][s], v);
+        x[t] = v * rr[t];
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        double inblk = 0.0;
+#pragma unroll
+        for (int p = t; p < 4; ++p) inblk = r == JB + p ? l[p][t] : inblk;
+        a[li + t] = r >= JB + 4 ? x[t] : inblk;
+      }
+      *(d2*)&Lr[r][JB] = d2{a[li], a[li + 1]};
+      *(d2*)&Lr[r][JB + 2] = d2{a[li + 2], a[li + 3]};
+      if (r == 0) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) rdiag[JB + t] = rr[t];
       }
     }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      double v = a[JB + q];
-#pragma unroll
-      for (int s = 0; s < q; ++s) v = fma(-x[s], l[q][s], v);
-      x[q] = v * rr[q];
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      double inblk = 0.0;
-#pragma unroll
-      for (int p = q; p < 4; ++p) inblk = r == JB + p ? l[p][q] : inblk;
-      a[JB + q] = r >= JB + 4 ? x[q] : inblk;
-    }
-    *(d2*)&Lr[r][JB] = d2{a[JB], a[JB + 1]};
-    *(d2*)&Lr[r][JB + 2] = d2{a[JB + 2], a[JB + 3]};
-    if (r == 0) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) rdiag[JB + q] = rr[q];
-    }
     __syncthreads();
-#pragma unroll
-    for (int k = JB + 4; k < kNb; ++k) {
-      const d2 u0 = *(const d2*)&Lr[k][JB], u1 = *(const d2*)&Lr[k][JB + 2];
-      double v = a[k];
-      v = fma(-a[JB], u0.x, v);
-      v = fma(-a[JB + 1], u0.y, v);
-      v = fma(-a[JB + 2], u1.x, v);
-      v = fma(-a[JB + 3], u1.y, v);
-      a[k] = v;
+    if (q == qo) {
+      if constexpr (li + 4 < kCq)
+        chol_update<li + 4>(a, qo * kCq, JB, d2{a[li], a[li + 1]}, d2{a[li + 2], a[li + 3]}, Lr);
+    } else if (q > qo) {
+      chol_update<0>(a, q * kCq, JB, *(const d2*)&Lr[r][JB], *(const d2*)&Lr[r][JB + 2], Lr);
     }
-    chol_step<JB + 4>(st, r, Lr, rdiag);
+    chol_step<JB + 4>(a, r, q, Lr, rdiag);
+  }
+}
+
+// Rows i0..kCq-1 of this wave (global row 16q+i) of column c take the four
+// new entries x_IB..x_IB+3.
+template <int I0>
+__device__ __forceinline__ void inv_update(double* a, int mbase, int IB, const double* x,
+                                           const LRow* Lr) {
+#pragma unroll
+  for (int i = I0; i < kCq; ++i) {
+    const int m = mbase + i;
+    const d2 u0 = *(const d2*)&Lr[m][IB], u1 = *(const d2*)&Lr[m][IB + 2];
+    double v = a[i];
+    v = fma(u0.x, x[0], v);
+    v = fma(u0.y, x[1], v);
+    v = fma(u1.x, x[2], v);
+    v = fma(u1.y, x[3], v);
+    a[i] = v;
   }
 }
 
 template <int IB>
-__device__ __forceinline__ void inv_step(CholRow& st, int c, const LRow* Lr, const double* rdiag,
-                                         double* blk, int64_t ld) {
+__device__ __forceinline__ void inv_step(double* a, int c, int q, const LRow* Lr,
+                                         const double* rdiag, double (*Xs)[kNb], double* blk,
+                                         int64_t ld) {
   if constexpr (IB < kNb) {
-    double* a = st.a;
-    double x[4];
+    constexpr int qo = IB / kCq, li = IB % kCq;
+    if (q == qo) {
+      double x[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      double v = (IB + q == c ? 1.0 : 0.0) - a[IB + q];
+      for (int t = 0; t < 4; ++t) {
+        double v = (IB + t == c ? 1.0 : 0.0) - a[li + t];
 #pragma unroll
-      for (int s = 0; s < q; ++s) v = fma(-Lr[IB + q][IB + s], x[s], v);
-      x[q] = v * rdiag[IB + q];
-      blk[(int64_t)(IB + q) * ld + c] = x[q];
+        for (int s = 0; s < t; ++s) v = fma(-Lr[IB + t][IB + s], x[s], v);
+        x[t] = v * rdiag[IB + t];
+        blk[(int64_t)(IB + t) * ld + c] = x[t];
+        if constexpr (qo + 1 < kQw) Xs[IB + t][c] = x[t];
+      }
+      if constexpr (li + 4 < kCq) inv_update<li + 4>(a, qo * kCq, IB, x, Lr);
     }
+    if constexpr (qo + 1 < kQw) {
+      __syncthreads();
+      if (q > qo) {
+        double x[4];
 #pragma unroll
-    for (int m = IB + 4; m < kNb; ++m) {
-      const d2 u0 = *(const d2*)&Lr[m][IB], u1 = *(const d2*)&Lr[m][IB + 2];
-      double v = a[m];
-      v = fma(u0.x, x[0], v);
-      v = fma(u0.y, x[1], v);
-      v = fma(u1.x, x[2], v);
-      v = fma(u1.y, x[3], v);
-      a[m] = v;
+        for (int t = 0; t < 4; ++t) x[t] = Xs[IB + t][c];
+        inv_update<0>(a, q * kCq, IB, x, Lr);
+      }
     }
-    inv_step<IB + 4>(st, c, Lr, rdiag, blk, ld);
+    inv_step<IB + 4>(a, c, q, Lr, rdiag, Xs, blk, ld);
   }
 }
 
-__global__ __launch_bounds__(64) void chol_diag_kernel(double* __restrict__ H, int64_t ld, int p) {
+__global__ __launch_bounds__(kNb * kQw) void chol_diag_kernel(double* __restrict__ H, int64_t ld,
+                                                               int p) {
   __shared__ __attribute__((aligned(16))) LRow Lr[kNb];
   __shared__ double rdiag[kNb];
-  const int r = threadIdx.x;
+  __shared__ double Xs[kNb][kNb];
+  const int r = threadIdx.x % kNb;
+  const int q = __builtin_amdgcn_readfirstlane(threadIdx.x / kNb);
   double* blk = H + (int64_t)p * kNb * ld + (int64_t)p * kNb;
-  CholRow st;
+  double a[kCq];
 #pragma unroll
-  for (int k = 0; k < kNb; ++k) st.a[k] = k <= r ? blk[(int64_t)r * ld + k] : 0.0;
-  chol_step<0>(st, r, Lr, rdiag);
+  for (int i = 0; i < kCq; ++i) {
+    const int k = q * kCq + i;
+    a[i] = k <= r ? blk[(int64_t)r * ld + k] : 0.0;
+  }
+  chol_step<0>(a, r, q, Lr, rdiag);
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < kNb; ++i) st.a[i] = 0.0;
-  inv_step<0>(st, r, Lr, rdiag, blk, ld);
+  for (int i = 0; i < kCq; ++i) a[i] = 0.0;
+  inv_step<0>(a, r, q, Lr, rdiag, Xs, blk, ld);
 }
 
 // U[a][b] = Linv[K-1-a][K-1-b]: swap every entry of the leading K x K block
@@ -771,7 +820,7 @@ hipError_t launch_gptq(const void* W, const void* X, awq_dtype_t dt, int64_t N, 
   {
     ProfScope ps("awq_gptq_cholesky", st);
     for (int p = 0; p < nblk; ++p) {
-      hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(64), 0, st, H, Kp, p);
+      hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(kNb * kQw), 0, st, H, Kp, p);
       RET_IF(hipGetLastError());
       const int rest = nblk - p - 1;
       if (rest == 0) break;
