@@ -323,11 +323,11 @@ __global__ __launch_bounds__(kThreads) void damp_kernel(double* __restrict__ H, 
 }
 
 // ---- Cholesky of one diagonal block and its inverse --------------------------
-// Four waves share the 64x64 block: lane r of every wave stands for row r,
-// wave q owns the sixteen columns 16q..16q+15 of that row in registers (lower
-// part read only).  The factor L_pp itself is never needed again (the panel
-// below is solved with its inverse, the later updates use the solved panel),
-// so the block is overwritten with L_pp^-1 (zeros above the diagonal).
+// Sixteen waves share the 64x64 block: lane r of every wave stands for row r,
+// wave q owns the four columns 4q..4q+3 of that row in registers (lower part
+// read only).  The factor L_pp itself is never needed again (the panel below
+// is solved with its inverse, the later updates use the solved panel), so the
+// block is overwritten with L_pp^-1 (zeros above the diagonal).
 //
 // Both halves go four columns per step, the steps unrolled by template
 // recursion so every register index is static (a rolled loop would move the
@@ -338,7 +338,7 @@ __global__ __launch_bounds__(kThreads) void damp_kernel(double* __restrict__ H, 
 // published in LDS (row-major L, one 32-byte write per lane); after one
 // barrier every wave updates its own later columns with four FMAs each.
 // Inverse step IB: lane c now stands for column c of L^-1 and wave q owns its
-// rows 16q..16q+15; the wave owning rows IB..IB+3 solves the 4x4 block for
+// rows 4q..4q+3; the wave owning rows IB..IB+3 solves the 4x4 block for
 // x_IB..x_IB+3, publishes them in LDS and every wave pushes them into its own
 // later rows.  Each entry sees the same operations in the same order as in a
 // one-wave sweep of the whole row, so the split changes no bit of the result.
@@ -362,12 +362,11 @@ __device__ __forceinline__ double rsqrt64(double x) {
   return y;
 }
 
-
-constexpr int kCq = 16;              // columns (rows, in the inverse) per wave
+constexpr int kCq = 4;               // columns (rows, in the inverse) per wave
 constexpr int kQw = kNb / kCq;       // waves per block
 typedef double LRow[kNb + 2];
 
-// Columns i0..kCq-1 of this wave (global column 16q+i) take the rank-4 update
+// Columns i0..kCq-1 of this wave (global column kCq q + i) take the rank-4 update
 // by the new columns JB..JB+3; w holds this row's own four new entries.
 template <int I0>
 __device__ __forceinline__ void chol_update(double* a, int kbase, int JB, d2 w0, d2 w1,
@@ -442,7 +441,7 @@ __device__ __forceinline__ void chol_step(double* a, int r, int q, LRow* Lr, dou
   }
 }
 
-// Rows i0..kCq-1 of this wave (global row 16q+i) of column c take the four
+// Rows i0..kCq-1 of this wave (global row kCq q + i) of column c take the four
 // new entries x_IB..x_IB+3.
 template <int I0>
 __device__ __forceinline__ void inv_update(double* a, int mbase, int IB, const double* x,
