@@ -102,7 +102,8 @@ __device__ __forceinline__ uint32_t code_at(const uint32_t (&w)[BITS], int i) {
 }
 
 // Pair t of (c - z) as two fp16: 1024 + c is exact in fp16 for c < 1024, so
-// OR-ing c into the mantissa of 1024 and adding -(1024 + z) is exact.
+// OR-ing c into the mantissa of 1024 and adding -(1024 + z) is exact (packed
+// fp16 arithmetic: two codes per instruction).
 template <int BITS>
 __device__ __forceinline__ uint32_t pair_f16(const uint32_t (&w)[BITS], int t, half2v negz) {
   const uint32_t v = (code_at<BITS>(w, 2 * t) | (code_at<BITS>(w, 2 * t + 1) << 16)) | 0x64006400u;
@@ -110,13 +111,69 @@ __device__ __forceinline__ uint32_t pair_f16(const uint32_t (&w)[BITS], int t, h
   return __builtin_bit_cast(uint32_t, h);
 }
 
-// Pair t of (c - z) as two bf16: the integers are converted through fp32,
-// where they are exact, and their upper halves (exact bf16) are packed.
+// (c - z) as fp32 without integer conversions.  A code c at bit sh of a dword,
+// with sh + BITS <= 23, is AND-ed out in place and OR-ed under the exponent of
+// 2^(23 - sh), whose mantissa step is 2^-sh: the float reads 2^(23 - sh) + c
+// exactly, and subtracting 2^(23 - sh) + z (an integer below 2^24) leaves
+// c - z exactly.  Only AND / OR with constants and an fp32 subtraction are
+// needed, which the vector ALU issues at twice the rate of bit-field
+// extracts, integer conversions and permutes.  The chunk's bitstream is read
+// through windows: dwords starting at a code boundary b that hold the codes
+// whose bits lie in [b, b + 23), chosen greedily from bit 0.
 template <int BITS>
-__device__ __forceinline__ uint32_t pair_bf16(const uint32_t (&w)[BITS], int t, int z) {
-  const float lo = (float)((int)code_at<BITS>(w, 2 * t) - z);
-  const float hi = (float)((int)code_at<BITS>(w, 2 * t + 1) - z);
-  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+struct MagicWindows {
+  static constexpr int kSpan = 23;                          // mantissa bits of fp32
+  static constexpr int kPerWin = (kSpan - BITS) / BITS + 1;  // codes per window
+  static constexpr int start(int i) { return (i / kPerWin) * kPerWin * BITS; }
+  static constexpr int shift(int i) { return BITS * i - start(i); }
+  static constexpr int last_bit(int i) {                    // last bit of i's window
+    const int w_end = (i / kPerWin + 1) * kPerWin;          // first code of the next window
+    return (w_end < 32 ? w_end : 32) * BITS - 1;
+  }
+};
+
+template <int BITS>
+__device__ __forceinline__ uint32_t magic_window(const uint32_t (&w)[BITS], int i) {
+  using MW = MagicWindows<BITS>;
+  const int b = MW::start(i);                    // compile-time after unrolling
+  const int wi = b >> 5, sh = b & 31;
+  if (sh == 0) return w[wi];
+  if ((MW::last_bit(i) >> 5) == wi) return w[wi] >> sh;
+  return __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh);
+}
+
+// Subtrahends 2^(23 - sh) + z for the window offsets sh = 0, BITS, 2 BITS, ...
+template <int BITS>
+struct MagicNeg {
+  float v[MagicWindows<BITS>::kPerWin];
+};
+
+template <int BITS>
+__device__ __forceinline__ MagicNeg<BITS> magic_neg(float z) {
+  MagicNeg<BITS> n;
+#pragma unroll
+  for (int t = 0; t < MagicWindows<BITS>::kPerWin; ++t)
+    n.v[t] = (float)(1 << (23 - BITS * t)) + z;
+  return n;
+}
+
+template <int BITS>
+__device__ __forceinline__ float magic_cz(const uint32_t (&w)[BITS], int i,
+                                          const MagicNeg<BITS>& neg) {
+  using MW = MagicWindows<BITS>;
+  const int sh = MW::shift(i);
+  const uint32_t mask = ((1u << BITS) - 1u) << sh;
+  const uint32_t expo = (uint32_t)(150 - sh) << 23;          // 2^(23 - sh)
+  const float m = __uint_as_float((magic_window<BITS>(w, i) & mask) | expo);
+  return m - neg.v[sh / BITS];
+}
+
+// Pair t of (c - z) as two bf16 (exact: |c - z| <= 255 has 8 significant bits).
+template <int BITS>
+__device__ __forceinline__ uint32_t pair_bf16(const uint32_t (&w)[BITS], int t,
+                                              const MagicNeg<BITS>& neg) {
+  const bf162v p = {(__bf16)magic_cz<BITS>(w, 2 * t, neg), (__bf16)magic_cz<BITS>(w, 2 * t + 1, neg)};
+  return __builtin_bit_cast(uint32_t, p);
 }
 
 template <typename S>
@@ -140,7 +197,6 @@ __global__ __launch_bounds__(kRows) void lowbit_gemv_kernel(
     const float2* __restrict__ meta_t, int64_t N, int group, int cps,
     float* __restrict__ partials /* [splits][M][N] */, float* __restrict__ Y) {
   constexpr bool kF32 = sizeof(S) == 4;
-  constexpr bool kHalf = std::is_same<S, _Float16>::value;
   __shared__ __attribute__((aligned(16))) S xs[MB][kMaxChunks * 32];
   const int tid = threadIdx.x;
   const int64_t n = (int64_t)blockIdx.x * kRows + tid;
@@ -196,23 +252,24 @@ __global__ __launch_bounds__(kRows) void lowbit_gemv_kernel(
       const int kl = (j - c_begin) * 32;      // column of the chunk inside the staged block
       if constexpr (kF32) {
         // fp32 activations: plain fp32 products of x and the exact (c - z)
+        const MagicNeg<BITS> neg = magic_neg<BITS>(g[u].y);
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
-          const float cz = (float)code_at<BITS>(w[u], i) - g[u].y;
+          const float cz = magic_cz<BITS>(w[u], i, neg);
 #pragma unroll
           for (int m = 0; m < MB; ++m) accg[m] = fmaf(cz, (float)xs[m][kl + i], accg[m]);
         }
       } else {
         uint32_t pr[16];
-        if constexpr (kHalf) {
+        if constexpr (std::is_same<S, _Float16>::value) {
           const _Float16 nz = (_Float16)(-(1024.0f + g[u].y));
           const half2v negz = {nz, nz};
 #pragma unroll
           for (int t = 0; t < 16; ++t) pr[t] = pair_f16<BITS>(w[u], t, negz);
         } else {
-          const int z = (int)g[u].y;
+          const MagicNeg<BITS> neg = magic_neg<BITS>(g[u].y);
 #pragma unroll
-          for (int t = 0; t < 16; ++t) pr[t] = pair_bf16<BITS>(w[u], t, z);
+          for (int t = 0; t < 16; ++t) pr[t] = pair_bf16<BITS>(w[u], t, neg);
         }
 #pragma unroll
         for (int m = 0; m < MB; ++m) {
