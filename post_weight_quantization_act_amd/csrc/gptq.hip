@@ -61,6 +61,8 @@ enum Map : int {
   kLower = 1,    // tiles (i, j), off <= j <= i < off + r, blockIdx.x enumerates them
   kInvT1 = 2,    // inverse level, first product (stored transposed)
   kInvT2 = 3,    // inverse level, second product
+  kStrict = 4,   // tiles (i, j), 0 <= j < i < r: the lower triangle without its diagonal
+  kDiag = 5,     // the three lower TILE-tiles of each diagonal 2 TILE block d < r
 };
 
 struct GArgs {
@@ -110,9 +112,16 @@ __device__ __forceinline__ Job make_job(const GArgs& g) {
     jb.nk = g.depth;
     jb.mlim = g.M - m0 < TILE ? (int)(g.M - m0) : TILE;
     jb.nlim = g.Nn - n0 < TILE ? (int)(g.Nn - n0) : TILE;
-  } else if constexpr (MAP == kLower) {
+  } else if constexpr (MAP == kLower || MAP == kStrict || MAP == kDiag) {
     int ti, tj;
-    tri_index((int)blockIdx.x, ti, tj);
+    if constexpr (MAP == kDiag) {
+      const int d = (int)blockIdx.x / 3, sub = (int)blockIdx.x % 3;
+      ti = 2 * d + (sub > 0);
+      tj = 2 * d + (sub == 2);
+    } else {
+      tri_index((int)blockIdx.x, ti, tj);
+      if constexpr (MAP == kStrict) ++ti;
+    }
     const int64_t m0 = (int64_t)(g.off + ti) * TILE, n0 = (int64_t)(g.off + tj) * TILE;
     jb.a0 = at(g.a, g.lda, A_KC, m0, 0);
     jb.b0 = at(g.b, g.ldb, B_KC, n0, 0);
@@ -795,7 +804,11 @@ hipError_t launch_gptq(const void* W, const void* X, awq_dtype_t dt, int64_t N, 
       g.r = r;
       g.alpha = 1.0;
       g.beta = t0 == 0 ? 0.0 : 1.0;
-      RET_IF((gemm64<128, false, false, kLower>(dim3(r * (r + 1) / 2), g, st)));
+      // The r (r - 1) / 2 tiles below the diagonal as 128-tiles (two per CU fit at once, so
+      // this count stays within one round where the full triangle would spill a few tiles
+      // into a second), the diagonal blocks as three 64-tiles each in a second launch.
+      RET_IF((gemm64<128, false, false, kStrict>(dim3(r * (r - 1) / 2), g, st)));
+      RET_IF((gemm64<64, false, false, kDiag>(dim3(3 * r), g, st)));
     }
   }
   // 2. damping and dead channels; the scaled weights
@@ -922,8 +935,10 @@ hipError_t launch_gptq(const void* W, const void* X, awq_dtype_t dt, int64_t N, 
       g.depth = (int)(s1 - s0);
       g.alpha = -1.0;
       g.beta = 1.0;
-      const dim3 grid((unsigned)((rest + 127) / 128), (unsigned)((N + 127) / 128));
-      RET_IF((gemm64<128, true, false, kRect>(grid, g, st)));
+      // 64-tiles: four fit on a CU at once, so the launch fills the chip in even rounds
+      // (128-tiles, two per CU, left most of a second round idle at these sizes)
+      const dim3 grid((unsigned)((rest + 63) / 64), (unsigned)((N + 63) / 64));
+      RET_IF((gemm64<64, true, false, kRect>(grid, g, st)));
     }
   }
   // 6. packed codes
