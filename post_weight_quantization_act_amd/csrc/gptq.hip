@@ -222,21 +222,30 @@ __global__ __launch_bounds__(kThreads, 2) void gemm64_kernel(GArgs g) {
 #pragma unroll
     for (int j = 0; j < F; ++j) acc[i][j] = d4{0.0, 0.0, 0.0, 0.0};
 
-  d2 ra[PER / 2], rb[PER / 2];
+  // Two register sets keep the global loads of the next two stages in flight
+  // while a stage multiplies out of LDS (double-buffered): stage st + 1 goes
+  // to LDS at the end of stage st, stage st + 2 is loaded into the set that
+  // stage st has just vacated.
+  d2 ra0[PER / 2], rb0[PER / 2], ra1[PER / 2], rb1[PER / 2];
   const int nst = jb.nk / kKS;
   if (nst > 0) {
-    load(jb.a0, lda, A_KC, jb.mlim, 0, ra);
-    load(jb.b0, ldb, B_KC, jb.nlim, 0, rb);
-    store(As[0], A_KC, ra);
-    store(Bs[0], B_KC, rb);
+    load(jb.a0, lda, A_KC, jb.mlim, 0, ra0);
+    load(jb.b0, ldb, B_KC, jb.nlim, 0, rb0);
+  }
+  if (nst > 1) {
+    load(jb.a0, lda, A_KC, jb.mlim, kKS, ra1);
+    load(jb.b0, ldb, B_KC, jb.nlim, kKS, rb1);
+  }
+  if (nst > 0) {
+    store(As[0], A_KC, ra0);
+    store(Bs[0], B_KC, rb0);
   }
   __syncthreads();
-  for (int st = 0; st < nst; ++st) {
+  auto step = [&](int st, d2* ra_free, d2* rb_free, const d2* ra_next, const d2* rb_next) {
     const int cur = st & 1;
-    const bool more = st + 1 < nst;
-    if (more) {
-      load(jb.a0, lda, A_KC, jb.mlim, (st + 1) * kKS, ra);
-      load(jb.b0, ldb, B_KC, jb.nlim, (st + 1) * kKS, rb);
+    if (st + 2 < nst) {
+      load(jb.a0, lda, A_KC, jb.mlim, (st + 2) * kKS, ra_free);
+      load(jb.b0, ldb, B_KC, jb.nlim, (st + 2) * kKS, rb_free);
     }
 #pragma unroll
     for (int kk = 0; kk < kKS / 4; ++kk) {
@@ -251,11 +260,15 @@ __global__ __launch_bounds__(kThreads, 2) void gemm64_kernel(GArgs g) {
         for (int j = 0; j < F; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[i], bv[j], acc[i][j], 0, 0, 0);
     }
-    if (more) {
-      store(As[cur ^ 1], A_KC, ra);
-      store(Bs[cur ^ 1], B_KC, rb);
+    if (st + 1 < nst) {
+      store(As[cur ^ 1], A_KC, ra_next);
+      store(Bs[cur ^ 1], B_KC, rb_next);
     }
     __syncthreads();
+  };
+  for (int st = 0; st < nst; st += 2) {
+    step(st, ra0, rb0, ra1, rb1);
+    if (st + 1 < nst) step(st + 1, ra1, rb1, ra0, rb0);
   }
 
   // Epilogue: lane holds rows (lane / 16) + 4 e, column lane % 16 of each block.
