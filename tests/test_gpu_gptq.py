@@ -126,6 +126,7 @@ CASES = [
     ("fp16", 64, 512, 700, 8, 512, "awq", 0.01),      # one group per row
     ("bf16", 77, 640, 640, 3, 128, "awq", 0.0),       # no damping, full rank
     ("fp16", 256, 256, 64, 4, 32, "awq", 0.05),       # T far below K: heavily rank-deficient
+    ("fp16", 48, 4608, 600, 4, 128, "awq", 0.01),     # 630 below-diagonal Hessian tiles: two rounds
 ]
 
 
