@@ -116,8 +116,9 @@ __device__ __forceinline__ uint32_t pair_f16(const uint32_t (&w)[BITS], int t, h
 // 2^(23 - sh), whose mantissa step is 2^-sh: the float reads 2^(23 - sh) + c
 // exactly, and subtracting 2^(23 - sh) + z (an integer below 2^24) leaves
 // c - z exactly.  Only AND / OR with constants and an fp32 subtraction are
-// needed, which the vector ALU issues at twice the rate of bit-field
-// extracts, integer conversions and permutes.  The chunk's bitstream is read
+// needed: instructions that two waves of a SIMD can issue side by side,
+// unlike bit-field extracts, integer conversions and permutes (one wave64
+// instruction per 4 cycles).  The chunk's bitstream is read
 // through windows: dwords starting at a code boundary b that hold the codes
 // whose bits lie in [b, b + 23), chosen greedily from bit 0.
 template <int BITS>
