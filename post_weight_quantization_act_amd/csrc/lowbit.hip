@@ -206,7 +206,9 @@ __global__ __launch_bounds__(kRows) void lowbit_gemv_kernel(
   const int mb = (int)((M - m0) < MB ? (M - m0) : MB);
   const bool row_ok = n < N;
   const int64_t nn = row_ok ? n : 0;        // rows past N load row 0 and store nothing
-  const int cpg = group / 32;                // chunks per group
+  // chunks per group: a power of two (the group size is one), so the group of
+  // chunk j and its last chunk come from a shift and a mask
+  const int lg_cpg = __builtin_ctz((unsigned)group >> 5), cmask = (1 << lg_cpg) - 1;
   const int chunks = (int)(K / 32);
   const int c_begin = split * cps;
   const int c_end = c_begin + cps < chunks ? c_begin + cps : chunks;
@@ -223,7 +225,7 @@ __global__ __launch_bounds__(kRows) void lowbit_gemv_kernel(
         const uint32_t* src = codes_t + (j * N + nn) * BITS;
 #pragma unroll
         for (int i = 0; i < BITS; ++i) w[u][i] = src[i];
-        g[u] = meta_t[(j / cpg) * N + nn];
+        g[u] = meta_t[(j >> lg_cpg) * N + nn];
       }
     }
   };
@@ -286,7 +288,7 @@ __global__ __launch_bounds__(kRows) void lowbit_gemv_kernel(
           }
         }
       }
-      if ((j + 1) % cpg == 0 || j + 1 == c_end) {   // group (or this split) ends
+      if (((j + 1) & cmask) == 0 || j + 1 == c_end) {   // group (or this split) ends
 #pragma unroll
         for (int m = 0; m < MB; ++m) {
           acc[m] = fmaf(accg[m], g[u].x, acc[m]);
