@@ -225,7 +225,8 @@ __global__ __launch_bounds__(kRows) void lowbit_gemv_kernel(
         const uint32_t* src = codes_t + (j * N + nn) * BITS;
 #pragma unroll
         for (int i = 0; i < BITS; ++i) w[u][i] = src[i];
-        g[u] = meta_t[(j >> lg_cpg) * N + nn];
+        // (delta, z) once per group: at its first chunk, or the split's
+        if ((j & cmask) == 0 || j == c_begin) g[u] = meta_t[(j >> lg_cpg) * N + nn];
       }
     }
   };
@@ -247,15 +248,20 @@ __global__ __launch_bounds__(kRows) void lowbit_gemv_kernel(
   float acc[MB], accg[MB];
 #pragma unroll
   for (int m = 0; m < MB; ++m) acc[m] = accg[m] = 0.0f;
+  float2 gc = {0.0f, 0.0f};                  // the current group's (delta, z)
+  MagicNeg<BITS> neg;                         // and its subtrahends
   auto sum_chunks = [&](int c0, const uint32_t (&w)[kUnroll][BITS], const float2 (&g)[kUnroll]) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int j = c0 + u;
       if (j >= c_end) break;
+      if ((j & cmask) == 0 || j == c_begin) {
+        gc = g[u];
+        neg = magic_neg<BITS>(gc.y);
+      }
       const int kl = (j - c_begin) * 32;      // column of the chunk inside the staged block
       if constexpr (kF32) {
         // fp32 activations: plain fp32 products of x and the exact (c - z)
-        const MagicNeg<BITS> neg = magic_neg<BITS>(g[u].y);
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
           const float cz = magic_cz<BITS>(w[u], i, neg);
@@ -265,12 +271,11 @@ __global__ __launch_bounds__(kRows) void lowbit_gemv_kernel(
       } else {
         uint32_t pr[16];
         if constexpr (std::is_same<S, _Float16>::value) {
-          const _Float16 nz = (_Float16)(-(1024.0f + g[u].y));
+          const _Float16 nz = (_Float16)(-(1024.0f + gc.y));
           const half2v negz = {nz, nz};
 #pragma unroll
           for (int t = 0; t < 16; ++t) pr[t] = pair_f16<BITS>(w[u], t, negz);
         } else {
-          const MagicNeg<BITS> neg = magic_neg<BITS>(g[u].y);
 #pragma unroll
           for (int t = 0; t < 16; ++t) pr[t] = pair_bf16<BITS>(w[u], t, neg);
         }
@@ -291,7 +296,7 @@ __global__ __launch_bounds__(kRows) void lowbit_gemv_kernel(
       if (((j + 1) & cmask) == 0 || j + 1 == c_end) {   // group (or this split) ends
 #pragma unroll
         for (int m = 0; m < MB; ++m) {
-          acc[m] = fmaf(accg[m], g[u].x, acc[m]);
+          acc[m] = fmaf(accg[m], gc.x, acc[m]);
           accg[m] = 0.0f;
         }
       }
