@@ -274,3 +274,35 @@ def test_lowbit_layer_random_shapes():
         Y = awq.awq_lowbit_gemv(Xs.cuda(), codes_t, meta_t, bits, group)
         torch.cuda.synchronize()
         check(Y.cpu().numpy(), Xs, codes, delta, zero, bits, group)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
+def test_lowbit_gemv_extreme_codes(dtype, bits):
+    """Codes and zero-points at both ends of their range, for every bit width:
+    c - z = qmax, -qmax and 0 in whole groups, plus rows of random codes with
+    z in {0, qmax}.  Every code position of a 32-code chunk takes both end
+    values, so each field offset and word boundary of the unpacking is
+    exercised; 1 and 4 activation rows run the vector kernel."""
+    log_case(test="lowbit_extreme", dtype=dtype, bits=bits)
+    rng = np.random.default_rng(1000 + bits)
+    qmax = (1 << bits) - 1
+    N, K, group = 70, 512, 64
+    codes = rng.integers(0, qmax + 1, size=(N, K)).astype(np.uint8)
+    zero = rng.choice(np.array([0, qmax], dtype=np.uint8), size=(N, K // group))
+    codes[0], zero[0] = qmax, 0                    # c - z = qmax everywhere
+    codes[1], zero[1] = 0, qmax                    # c - z = -qmax everywhere
+    codes[2], zero[2] = qmax, qmax                 # c - z = 0
+    codes[3] = np.where(np.arange(K) % 2 == 0, qmax, 0)
+    codes[4] = np.where(np.arange(K) % 2 == 0, 0, qmax)
+    delta = (rng.random((N, K // group)) * 0.01 + 1e-4).astype(F32)
+    words = oracle.pack_codes(codes, bits)
+    c_d = torch.from_numpy(words.view(np.int32)).cuda()
+    codes_t, meta_t = awq.awq_lowbit_repack(c_d, torch.from_numpy(delta).cuda(),
+                                            torch.from_numpy(zero).cuda(), K, bits, group)
+    for M in (1, 4):
+        x = rng.standard_normal((M, K)).astype(F32)
+        Xs = torch.from_numpy(x).to(DT[dtype])
+        Y = awq.awq_lowbit_gemv(Xs.cuda(), codes_t, meta_t, bits, group)
+        torch.cuda.synchronize()
+        check(Y.cpu().numpy(), Xs, words, delta, zero, bits, group)
