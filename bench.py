@@ -4,12 +4,18 @@ One step = the whole hot path on one synthetic layer already resident in HBM:
 activation statistics, the 20-point alpha search (scale table, reference
 output, fake quantisation, candidate GEMMs with the fused squared-error
 epilogue, loss reduction and argmin) and the final quantise + pack with the
-chosen scales.  The metric is alpha-candidates scored per second.
+chosen scales.  The metric is alpha-candidates scored per second.  The
+default layer is the largest one: a 70B-class MLP projection (W bf16
+28672 x 8192, 16384 calibration tokens, INT3 g128).
 
 Prints one JSON line.  Besides the throughput it reports the dominant kernel
 (the candidate GEMM) against the dense fp16/bf16 MFMA peak, with its average
 launch time taken from HIP events recorded on the launch stream during the
-timed steps, and the CPU oracle timed on a bounded sample of the same layer.
+timed steps; the three HBM-bound passes (statistics, fake quantisation,
+quantise + pack) against the HBM peak, each timed after a write that evicts
+the 256 MB last-level cache; and the CPU oracle timed on a bounded sample of
+the same layer, with its losses compared against the GPU's on the same
+outputs.
 """
 
 from __future__ import annotations
@@ -27,6 +33,9 @@ sys.path.insert(0, str(ROOT))
 
 METRIC = "alpha-candidates/sec per layer; fake-quant GEMM TFLOP/s as % of MFMA peak"
 PEAK_TFLOPS = {"fp16": 2516.6, "bf16": 2516.6, "fp32": 157.3}
+PEAK_HBM_GBPS = 8000.0
+HBM_TARGET = 0.60          # statistics and quantisation passes: fraction of HBM peak
+FLUSH_BYTES = 1 << 30      # written before each timed HBM pass: 4x the 256 MB MALL
 PROFILES = ROOT / "profiles"
 
 
@@ -35,7 +44,11 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=30)
-    p.add_argument("--config", default="llama7b-qproj")
+    p.add_argument("--config", default="70b-mlp",
+                   help="synthetic layer: tiny-512, llama7b-qproj, llama7b-upgate, llama7b-down, "
+                        "70b-mlp (default, the largest)")
+    p.add_argument("--hbm-reps", type=int, default=3,
+                   help="cache-evicted repetitions per HBM-bound pass")
     p.add_argument("--flags", type=int, default=0, help="0 weight-delta form, 1 reference-output form")
     p.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -420,36 +433,104 @@ def measured_traffic(key: str):
     return None
 
 
-def cpu_baseline(spec, W, X, budget_s: float) -> dict:
-    """The oracle as it is, on the first k alphas of the same layer."""
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
+    except Exception:  # pragma: no cover - informational only
+        return -1
+
+
+def cpu_baseline(spec, W, X, lay: dict, parts, budget_s: float) -> dict:
+    """The oracle as it is (oracle.search) on the same layer, bounded to about
+    budget_s seconds: on the whole layer when that fits, else on a block of
+    whole 256-channel output tiles (every token), sized from a one-alpha probe.
+    The statistic always covers all of X.  The layer's time is the statistic
+    plus the block's search time scaled to all output channels.  The oracle's
+    losses are compared with the GPU's on exactly the same outputs: the sum of
+    the GPU's per-tile squared-error partials (`parts`, [n_alpha, tiles_m,
+    tiles_n] fp64, from the last timed step) over the block's tiles."""
     import numpy as np
 
     import oracle
     from datagen import to_numpy
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover - informational only
-        threads = len(os.sched_getaffinity(0))
     Wn, Xn = to_numpy(W), to_numpy(X)
-    alphas = oracle.alpha_grid(spec.n_alpha)
+    N, T, n_a = spec.N, spec.T, spec.n_alpha
+    alphas = oracle.alpha_grid(n_a)
+    tile_n, tiles_n = lay["tile_n"], lay["tiles_n"]
     t0 = time.perf_counter()
-    oracle.search(Wn, Xn, spec.bits, spec.group, alphas[:1])
-    t1 = time.perf_counter() - t0
-    k = 1
-    elapsed = t1
-    if t1 < budget_s / 2:
-        # the fixed part (statistics + reference output) is included in every run
-        k = int(min(spec.n_alpha, max(2, budget_s / max(t1, 1e-3))))
-        t0 = time.perf_counter()
-        oracle.search(Wn, Xn, spec.bits, spec.group, alphas[:k])
-        elapsed = time.perf_counter() - t0
-    return {"value": k / elapsed, "unit": "alpha-candidates/s", "cores": int(threads),
+    a = oracle.act_stats(Xn)
+    t_stats = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.search(Wn[:min(N, tile_n)], Xn, spec.bits, spec.group, alphas[:1], a=a)
+    per_tile = (time.perf_counter() - t0) * (n_a + 1) / 2    # reference output + n_a candidates
+    n_tiles = int(max(1, min(tiles_n, (budget_s - t_stats) // max(per_tile, 1e-6))))
+    n0 = (tiles_n - n_tiles) // 2
+    r0, r1 = n0 * tile_n, min(N, (n0 + n_tiles) * tile_n)
+    t0 = time.perf_counter()
+    ref = oracle.search(Wn[r0:r1], Xn, spec.bits, spec.group, alphas, a=a)
+    t_search = time.perf_counter() - t0
+    layer_s = t_stats + t_search * N / (r1 - r0)
+    got = parts[:, :, n0:n0 + n_tiles].reshape(n_a, -1).sum(1) / (float(T) * (r1 - r0))
+    rel = np.abs(got / ref["losses"] - 1.0)
+    best_got, best_ref = oracle.argmin_lowest(got), ref["best"]
+    choice = ("identical" if best_got == best_ref else
+              "within 1e-3" if ref["losses"][best_got] - ref["losses"][best_ref]
+              < 1e-3 * ref["losses"][best_ref] else "differs")
+    whole = (r0, r1) == (0, N)
+    block = ("the whole layer" if whole else
+             f"output channels [{r0}, {r1}) ({r1 - r0} of {N}) over all {T} tokens")
+    return {"value": n_a / layer_s, "unit": "alpha-candidates/s",
+            "cores": len(os.sched_getaffinity(0)), "blas_threads": blas_threads(),
             "kind": "oracle",
-            "sample": f"oracle.search (statistics, fp64 reference output, fake quantisation and "
-                      f"fp64 loss) over the first {k} of {spec.n_alpha} alphas of the full "
-                      f"{spec.name} layer, {elapsed:.1f} s on {threads} BLAS threads"}
+            "sample": f"oracle.search (fp64 reference output, fake quantisation and fp64 loss "
+                      f"for all {n_a} alphas) on {block} of the {spec.name} layer: "
+                      f"{t_search:.1f} s, plus the statistic over all of X ({t_stats:.1f} s); "
+                      + ("" if whole else
+                         f"the layer time is the statistic plus the search time scaled to all "
+                         f"{N} output channels, ") + f"{layer_s:.1f} s per layer",
+            "max_rel_loss_err": float(rel.max()), "alpha_choice": choice,
+            "alpha_oracle": float(alphas[best_ref]), "alpha_gpu": float(alphas[best_got])}
+
+
+def hbm_passes(step, spec, dev, reps: int) -> dict:
+    """Time the HBM-bound kernels exactly as the step launches them: before
+    each repetition a 1 GiB device write evicts the last-level cache, then one
+    step runs with HIP events (on the launch stream) around the named kernels
+    only.  Bytes are the algorithmic ones: what the pass must read and write."""
+    import torch
+
+    import post_weight_quantization_act_amd as awq
+
+    N, K, T, n_a = spec.N, spec.K, spec.T, spec.n_alpha
+    e = 4 if spec.dtype == "fp32" else 2
+    passes = {
+        "act_stats": ("awq_act_stats", T * K * e + K * 4),
+        "fake_quant": ("awq_fake_quant", N * K * e + n_a * K * 4 + n_a * N * K * e),
+        "quantize_pack": ("awq_quantize_pack",
+                          N * K * e + K * 4 + N * K * spec.bits // 8 + N * (K // spec.group) * 5),
+    }
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    out = {}
+    for name, (prefix, nbytes) in passes.items():
+        awq.awq_profile_reset()
+        awq.awq_profile_select(prefix)
+        for _ in range(reps):
+            flush.fill_(1.0)
+            awq.awq_profile_enable(True)
+            step()
+            awq.awq_profile_enable(False)
+        torch.cuda.synchronize()
+        n, ms = awq.awq_profile_read(prefix)
+        awq.awq_profile_reset()
+        ms_pass = ms / reps                       # every launch of the pass within one step
+        gbps = nbytes / (ms_pass * 1e-3) / 1e9
+        out[name] = {"ms": ms_pass, "launches_per_step": n / reps, "bytes": nbytes,
+                     "gbps": gbps, "frac": gbps / PEAK_HBM_GBPS,
+                     "meets_target": gbps / PEAK_HBM_GBPS >= HBM_TARGET}
+    del flush
+    return out
 
 
 def main():
@@ -524,9 +605,6 @@ def main():
         step()
     torch.cuda.synchronize()
     awq.awq_profile_enable(False)
-    n_fq, ms_fq = awq.awq_profile_read("awq_fake_quant")
-    n_st, ms_st = awq.awq_profile_read("awq_act_stats")
-    n_pk, ms_pk = awq.awq_profile_read("awq_quantize_pack")
     n_ref, ms_ref = awq.awq_profile_read("awq_gemm_ref_output")
     n_tl, ms_tl = awq.awq_profile_read("awq_tile_rows")
     n_la, ms_la = awq.awq_profile_read("awq_loss_argmin")
@@ -542,22 +620,18 @@ def main():
     achieved = flop_per_launch / (avg_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[spec.dtype]
     traffic = measured_traffic(f"{args.config}:{args.flags}")
-    esize = 4 if spec.dtype == "fp32" else 2
     def avg(ms, n):
         return ms / max(n, 1)
 
-    fq_alphas = spec.n_alpha * 2 / max(n_fq, 1)        # the breakdown ran two steps
+    # the partial sums of the last step's search, for the oracle comparison
+    parts = ws[lay["partials_offset"]:lay["partials_offset"] +
+               spec.n_alpha * lay["tiles_m"] * lay["tiles_n"] * 8].view(torch.float64)
+    parts = parts.view(spec.n_alpha, lay["tiles_m"], lay["tiles_n"]).cpu().numpy()
+    passes = hbm_passes(step, spec, dev, args.hbm_reps)
 
     detail = {
         "gemm_sse": {"launches": n_gemm, "per_step": n_gemm / args.steps, "avg_ms": avg_ms,
                      "tflops": achieved},
-        "fake_quant": {"avg_ms": avg(ms_fq, n_fq), "alphas_per_launch": fq_alphas,
-                       "gbps": (N * K * esize + fq_alphas * N * K * esize) / (avg(ms_fq, n_fq) * 1e-3) / 1e9},
-        "act_stats": {"avg_ms": avg(ms_st, 2),
-                      "gbps": (T * K * esize) / (avg(ms_st, 2) * 1e-3) / 1e9},
-        "quantize_pack": {"avg_ms": avg(ms_pk, n_pk),
-                          "gbps": (N * K * esize + N * K * spec.bits / 8 + 5 * N * K / spec.group)
-                          / (avg(ms_pk, n_pk) * 1e-3) / 1e9},
         "tile_rows_ms": avg(ms_tl, n_tl) if n_tl else None,
         "scale_table_ms": avg(ms_sc, n_sc) if n_sc else None,
         "loss_argmin_ms": avg(ms_la, n_la) if n_la else None,
@@ -584,10 +658,12 @@ def main():
                      "frac": achieved / peak, "traffic": traffic,
                      "kernel": "gemm_mfma_kernel (candidate GEMM + squared-error epilogue)",
                      "flop_per_launch": flop_per_launch},
+        "hbm_passes": passes,
+        "hbm_target_frac": HBM_TARGET,
         "kernels": detail,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(spec, W, X, args.cpu_budget)
+        out["cpu_baseline"] = cpu_baseline(spec, W, X, lay, parts, args.cpu_budget)
     print(json.dumps(out), flush=True)
 
 

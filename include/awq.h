@@ -204,6 +204,15 @@ awq_status_t awq_search_layout(awq_dtype_t dtype, int64_t N, int64_t K, int64_t 
                                int n_alpha, uint32_t flags, size_t workspace_bytes,
                                awq_search_layout_t* layout_out);
 
+/* Host-only query: workspace bytes that let awq_search_scales score all
+ * n_alpha candidates of a W [N, K], X [T, K] layer in one batch with the
+ * default form (AWQ_SEARCH_WEIGHT_DELTA), whatever the layer dtype: the
+ * largest layout.total_bytes that awq_search_layout reports over AWQ_F32,
+ * AWQ_F16 and AWQ_BF16 for workspace_bytes = 0.  0 when a size is < 1 or
+ * n_alpha is outside [1, 4096].  The reference-output form needs
+ * awq_search_layout's figure, which adds the fp32 [T][N] layer output. */
+size_t awq_search_workspace_size(int64_t N, int64_t K, int64_t T, int n_alpha);
+
 awq_status_t awq_search_scales(const void* W, const void* X, awq_dtype_t dtype,
                                int64_t N, int64_t K, int64_t T,
                                const float* a, int bits, int group,

@@ -20,7 +20,8 @@ __all__ = [
     "AWQ_SEARCH_REFERENCE_OUTPUT", "AWQ_SEARCH_WEIGHT_DELTA", "AWQ_FQ_WEIGHT_HAT",
     "AWQ_FQ_WEIGHT_DELTA",
     "awq_version", "awq_act_stats", "awq_act_stats_workspace_size", "awq_scale_table",
-    "awq_fake_quant", "awq_search_layout", "awq_search_scales", "awq_quantize_pack",
+    "awq_fake_quant", "awq_search_layout", "awq_search_workspace_size", "awq_search_scales",
+    "awq_quantize_pack",
     "awq_salient_keep_workspace_size", "awq_salient_keep_loss", "awq_lowbit_repack",
     "awq_lowbit_gemv_workspace_size", "awq_lowbit_gemv", "awq_lowbit_gemm",
     "awq_gptq_workspace_size",
@@ -83,6 +84,7 @@ _SIGS = {
     "awq_fake_quant": ([_P, _I32, _I64, _I64, _P, _I32, _I32, _I32, _U32, _P, _I32, _P], _I32),
     "awq_search_layout": ([_I32, _I64, _I64, _I64, _I32, _U32, _SZ, ctypes.POINTER(SearchLayout)],
                           _I32),
+    "awq_search_workspace_size": ([_I64, _I64, _I64, _I32], _SZ),
     "awq_search_scales": ([_P, _P, _I32, _I64, _I64, _I64, _P, _I32, _I32, _P, _I32, _U32,
                            _P, _P, _P, _P, _SZ, _P], _I32),
     "awq_quantize_pack": ([_P, _I32, _I64, _I64, _P, _I32, _I32, _P, _P, _P, _P], _I32),
@@ -215,6 +217,11 @@ def awq_search_layout(dtype: torch.dtype, N: int, K: int, T: int, n_alpha: int,
     _check(library().awq_search_layout(_DTYPES[dtype], N, K, T, n_alpha, flags, workspace_bytes,
                                        ctypes.byref(lay)))
     return lay.as_dict()
+
+
+def awq_search_workspace_size(N: int, K: int, T: int, n_alpha: int) -> int:
+    """Bytes for a one-batch search of the default form, whatever the dtype."""
+    return int(library().awq_search_workspace_size(N, K, T, n_alpha))
 
 
 def awq_search_scales(W: torch.Tensor, X: torch.Tensor, a: torch.Tensor, bits: int, group: int,

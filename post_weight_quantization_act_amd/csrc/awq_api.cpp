@@ -269,6 +269,17 @@ awq_status_t awq_search_layout(awq_dtype_t dtype, int64_t N, int64_t K, int64_t 
   AWQ_GUARD_END
 }
 
+size_t awq_search_workspace_size(int64_t N, int64_t K, int64_t T, int n_alpha) {
+  if (N < 1 || K < 1 || T < 1 || n_alpha < 1 || n_alpha > kMaxAlpha) return 0;
+  size_t most = 0;
+  for (awq_dtype_t dt : {AWQ_F32, AWQ_F16, AWQ_BF16}) {
+    awq_search_layout_t L;
+    if (compute_layout(dt, N, K, T, n_alpha, AWQ_SEARCH_WEIGHT_DELTA, 0, &L) != AWQ_OK) return 0;
+    most = std::max(most, L.total_bytes);
+  }
+  return most;
+}
+
 awq_status_t awq_search_scales(const void* W, const void* X, awq_dtype_t dtype, int64_t N,
                                int64_t K, int64_t T, const float* a, int bits, int group,
                                const float* alphas, int n_alpha, uint32_t flags,

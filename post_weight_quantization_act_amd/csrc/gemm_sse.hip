@@ -117,12 +117,21 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t num_bytes)
 // 16 bytes per lane from rsrc + voff into LDS at m0 + 16 * lane.  Issued as
 // inline asm so the compiler does not serialise the ring with a full
 // vmcnt(0) before every LDS read; the kernel waits with explicit counts.
+// m0 is declared clobbered, so the compiler neither keeps a value of its own
+// in m0 across the transfer nor skips the wait state it owes before its own
+// next use of m0; inside the block, an SALU write of m0 needs one wait state
+// before an LDS-DMA load reads it, hence the s_nop.  clang warns that m0 is a
+// reserved register whenever it appears in a clobber list; the clobber is
+// honoured all the same (the hazard recognizer pads after the block).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds_addr, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :
                : "s"(lds_addr), "v"(voff), "s"(rsrc)
-               : "memory");
+               : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // Wait until at most n transfers of this lane are outstanding.
 template <int n>

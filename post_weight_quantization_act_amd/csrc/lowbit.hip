@@ -434,13 +434,20 @@ __device__ __forceinline__ i32x4 byte_range(const void* base, uint32_t num_bytes
 
 // 16 bytes per lane from rsrc + voff into LDS at lds_addr + 16 * lane.  Inline
 // asm, so that the compiler does not wait for every transfer before each LDS
-// read; the kernel waits with explicit counts.
+// read; the kernel waits with explicit counts.  m0 is declared clobbered (the
+// compiler keeps nothing of its own in it across the transfer and pads its own
+// next use), and the SALU write of m0 gets the one wait state an LDS-DMA load
+// needs before it reads m0.  clang warns about any reserved register in a
+// clobber list; the clobber is honoured all the same.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void to_lds16(i32x4 rsrc, uint32_t lds_addr, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :
                : "s"(lds_addr), "v"(voff), "s"(rsrc)
-               : "memory");
+               : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // Wait until at most n transfers of this lane are outstanding.
 template <int n>

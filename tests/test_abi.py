@@ -150,6 +150,24 @@ def test_search_layout_full_and_batched():
     assert f32["total_bytes"] - f32["w_hat_offset"] == 2 * 100 * 256 * 4
 
 
+def test_search_workspace_size_covers_every_dtype():
+    for N, K, T, n in ((4096, 4096, 4096, 20), (28672, 8192, 16384, 20), (300, 256, 77, 3),
+                       (1, 32, 1, 1)):
+        got = awq.awq_search_workspace_size(N, K, T, n)
+        sizes = [awq.awq_search_layout(dt, N, K, T, n, awq.AWQ_SEARCH_WEIGHT_DELTA, 0)
+                 for dt in (torch.float32, torch.float16, torch.bfloat16)]
+        assert got == max(lay["total_bytes"] for lay in sizes)
+        # a workspace of that size scores the whole grid in one batch for every dtype
+        for dt in (torch.float32, torch.float16, torch.bfloat16):
+            lay = awq.awq_search_layout(dt, N, K, T, n, awq.AWQ_SEARCH_WEIGHT_DELTA, got)
+            assert lay["alpha_batch"] == n
+    # 70B MLP layer: the tiled X, then 20 tiled weight-difference matrices
+    big = awq.awq_search_workspace_size(28672, 8192, 16384, 20)
+    assert big >= 16384 * 8192 * 2 + 20 * 28672 * 8192 * 2
+    for bad in ((0, 8, 8, 1), (8, 0, 8, 1), (8, 8, 0, 1), (8, 8, 8, 0), (8, 8, 8, 5000)):
+        assert awq.awq_search_workspace_size(*bad) == 0
+
+
 def test_act_stats_workspace_size_is_positive():
     assert awq.awq_act_stats_workspace_size(65536, 11008) >= 11008 * 8
     assert awq.awq_act_stats_workspace_size(0, 5) == 0

@@ -175,17 +175,18 @@ def test_quantize_pack_unit_scale_is_rtn_and_unpacks():
 # steps 2-5: the whole search
 # ---------------------------------------------------------------------------
 def check_losses(got, ref, best_got, best_ref, tol=None):
-    """Losses within 1e-3 relative (or the per-alpha bound `tol`); the argmin
-    may only differ where the oracle's two best losses are that close."""
+    """Losses within 1e-3 relative (or the per-alpha bound `tol`).  The GPU's
+    chosen alpha must be the oracle's, or one whose oracle loss lies within
+    1e-3 of the oracle's minimum (within tol[best_got] + tol[best_ref] for a
+    degenerate layer, the most that the two losses' errors can reorder)."""
     if tol is None:
         np.testing.assert_allclose(got, ref, rtol=1e-3, atol=0)
-        rel = 1e-3
     else:
         assert np.all(np.abs(got - ref) <= tol), (got, ref, tol)
-        rel = float(np.max(tol / ref))
     if best_got != best_ref:
-        top = np.sort(ref)[:2]
-        assert (top[1] - top[0]) / top[0] < 2 * rel, (best_got, best_ref, ref)
+        gap = ref[best_got] - ref[best_ref]
+        allowed = 1e-3 * ref[best_ref] if tol is None else tol[best_got] + tol[best_ref]
+        assert gap < allowed, (best_got, best_ref, ref)
 
 
 UNIT_ROUNDOFF = {"fp16": 2.0 ** -11, "bf16": 2.0 ** -8, "fp32": 2.0 ** -24}
