@@ -89,10 +89,6 @@ __device__ __forceinline__ GroupQ group_params(float mn, float mx, float qmax, f
   return g;
 }
 
-__device__ __forceinline__ float code_of(float wp, const GroupQ& g, float qmax) {
-  return __builtin_amdgcn_fmed3f(__builtin_rintf(div_rn(wp, g.delta, g.rdelta)) + g.z, 0.0f, qmax);
-}
-
 // c - z for c = clamp(rint(q) + z, 0, qmax), formed as clamp(rint(q), -z, qmax - z).
 // The two agree exactly: the integers involved are exact in fp32 unless
 // |rint(q)| >= 2^24, and then both clamp to the same bound.
@@ -271,93 +267,186 @@ __global__ __launch_bounds__(kFqThreads) void fake_quant_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Rounding decision of the code without the exact quotient.
+//
+// The oracle's code is c = clamp(rint(RN(w'/delta)) + z, 0, qmax).  With
+// y = RN(1/delta) (a correctly rounded division, once per group) the kernel
+// forms t = RN(w' * y + z) (one fma).  Let Q = w'/delta and V = RN(Q) + z.
+// Then |t - V| <= 2^-24 (3 |Q| + z) + 2^-149: y and the fma each round once
+// (relative 2^-24) and RN(Q) is within 2^-24 |Q| of Q.  If t lies farther than
+// that from every half-integer, V rounds to the same integer as t and is no
+// tie, so rint(t) = rint(RN(Q)) + z exactly (z is an integer) and
+// c = clamp(rint(t), 0, qmax).  The group-wide bound uses M = max(-mn, mx)
+// >= |w'|:
+//   lim = 1/2 - (M y 2^-21 + (z + 1) 2^-23)
+// 2^-21 covers 3 * 2^-24 |Q| with room for the roundings of the bound itself,
+// and (z + 1) 2^-23 covers 2^-24 z plus the rounding of lim (at most 2^-25)
+// and the underflow term.  A code is safe when |t - rint(t)| < lim (t - rint(t)
+// is exact); otherwise, or when lim <= 0, the wave recomputes the row's
+// quotients exactly.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float safe_limit(float mn, float mx, float y, float z) {
+  const float m = fmaxf(-mn, mx);
+  return 0.5f - (m * y * 0x1p-21f + (z + 1.0f) * 0x1p-23f);
+}
+
+// ---------------------------------------------------------------------------
 // Final quantisation + packing for one scale vector.
 //
-// One lane owns 32 consecutive columns of kPackRows rows: it loads the 32
-// scales once, then per row loads the 32 weights, reduces its share of the
-// group (G/32 lanes per group, DPP), computes the 32 codes and writes them as
-// `bits` uint32 words -- exactly its slice of the row's little-endian
-// bitstream (32 codes x bits bits).  The first lane of each group writes the
-// group's step and zero-point.  Consecutive lanes own consecutive column
-// chunks (a group never straddles a wave: K/32 is a multiple of G/32).
+// A wave owns 1024 consecutive columns (16 per lane: two 16-byte loads of a
+// 16-bit row) of kPackRows rows.  Its 16 scales are loaded once; all
+// kPackRows rows are loaded up front, so a lane has that many rows of
+// transfers in flight, and then handled row by row: scale, group min / max
+// over the group's G/16 lanes (DPP), step, reciprocal and zero-point, the 16
+// codes, and the packing.  Two neighbouring lanes hold 32 consecutive codes,
+// i.e. exactly `bits` words of the row's little-endian bitstream: each lane
+// places its 16 codes (16 * bits bits) at bit offset 16 * bits * (lane % 2)
+// of the pair's stream, the pair ORs its words together (DPP), and lane j
+// stores the words w with w % 2 == j.  The first lane of each group writes the
+// group's step and zero-point.  The codes take the rounding decision above.
 // ---------------------------------------------------------------------------
-constexpr int kPackRows = 4;
+constexpr int kPackLaneCols = 16;                  // columns per lane
+constexpr int kPackCols = 64 * kPackLaneCols;      // columns per wave
+constexpr int kPackRows = 4;                       // rows per wave
+constexpr int kPackWaves = 4;                      // waves per workgroup
 
+// 16 consecutive elements of a row, as raw 16-byte loads (four for fp32).
+template <typename S>
+struct Raw16 {
+  i32x4 v[sizeof(S)];
+};
+template <typename S>
+__device__ __forceinline__ Raw16<S> load_raw16(const S* p) {
+  Raw16<S> r;
+#pragma unroll
+  for (int i = 0; i < (int)sizeof(S); ++i) r.v[i] = reinterpret_cast<const i32x4*>(p)[i];
+  return r;
+}
+template <typename S>
+__device__ __forceinline__ void unpack16(const Raw16<S>& r, float (&v)[16]) {
+  const S* e = reinterpret_cast<const S*>(&r.v[0]);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = to_f32(e[i]);
+}
+
+__device__ __forceinline__ uint32_t pair_or(uint32_t v) {
+  return v | (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xf, 0xf, true);   // [1,0,3,2]
+}
+
+// Word wi of a bit stream that holds `f` (NW words, little-endian) shifted left by SH bits.
+template <int NW, int SH>
+__device__ __forceinline__ uint32_t shifted_word(const uint32_t (&f)[NW], int wi) {
+  const int q = SH / 32, r = SH % 32;
+  const int src = wi - q;
+  const uint32_t lo = (src >= 0 && src < NW) ? f[src] : 0u;
+  if (r == 0) return lo;
+  const uint32_t below = (src - 1 >= 0 && src - 1 < NW) ? f[src - 1] : 0u;
+  return (lo << r) | (below >> (32 - r));
+}
+
+// Sizes arrive precomputed (no integer division in the kernel): col_blocks =
+// ceil(K / 1024) waves per row block, group_shift = log2(group), lanes =
+// group / 16 (a power of two, at least 2).
 template <typename S, int BITS>
-__global__ __launch_bounds__(256) void quantize_pack_kernel(
-    const S* __restrict__ W, int64_t N, int64_t K, const float* __restrict__ s, int group,
-    int lanes, uint32_t* __restrict__ codes, float* __restrict__ scales,
+__global__ __launch_bounds__(64 * kPackWaves) void quantize_pack_kernel(
+    const S* __restrict__ W, int N, int K, const float* __restrict__ s, int group_shift,
+    int lanes, int col_blocks, uint32_t* __restrict__ codes, float* __restrict__ scales,
     uint8_t* __restrict__ zeros) {
-  const int64_t chunks_per_row = K / 32;
-  const int64_t row_blocks = (N + kPackRows - 1) / kPackRows;
-  const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const bool ok = q < row_blocks * chunks_per_row;
-  const int64_t rb = ok ? q / chunks_per_row : 0;
-  const int64_t cc = ok ? q % chunks_per_row : 0;
-  const int64_t col0 = cc * 32;
+  constexpr int NW = (16 * BITS + 31) / 32;                // words of one lane's 16 codes
+  const int lane = threadIdx.x & 63;
+  const int wave_id = __builtin_amdgcn_readfirstlane(blockIdx.x * kPackWaves + (threadIdx.x >> 6));
+  const int rb = wave_id / col_blocks;                     // scalar
+  const int cb = wave_id - rb * col_blocks;
+  const int row0 = rb * kPackRows;
+  if (row0 >= N) return;                                   // wave-uniform
+  const int col = cb * kPackCols + lane * kPackLaneCols;
+  const bool col_ok = col < K;                             // whole groups of lanes
   const float qmax = (float)((1 << BITS) - 1);
   const float rq = 1.0f / qmax;
 
-  float sv[32];
+  float sv[16];
+  if (col_ok) {
+    float a[8], b[8];
+    load8(s + col, a);
+    load8(s + col + 8, b);
 #pragma unroll
-  for (int h = 0; h < 4; ++h) {
-    float v[8];
-    if (ok) {
-      load8(s + col0 + h * 8, v);
+    for (int i = 0; i < 8; ++i) {
+      sv[i] = a[i];
+      sv[8 + i] = b[i];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sv[i] = 1.0f;
+  }
+  const S* wrow = W + (int64_t)row0 * K + col;
+  Raw16<S> raw[kPackRows];
+#pragma unroll
+  for (int p = 0; p < kPackRows; ++p) {
+    if (col_ok && row0 + p < N) {
+      raw[p] = load_raw16(wrow + (int64_t)p * K);
     } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = 1.0f;
+      for (int i = 0; i < (int)sizeof(S); ++i) raw[p].v[i] = i32x4{0, 0, 0, 0};
     }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) sv[h * 8 + i] = v[i];
   }
-
-  for (int r = 0; r < kPackRows; ++r) {
-    const int64_t row = rb * kPackRows + r;
-    const bool row_ok = ok && row < N;      // uniform across a group's lanes
-    float wp[32];
+  const int j = lane & 1;                                  // position in the pair
+  const int words_per_row = (K >> 5) * BITS;
+  const int groups_per_row = K >> group_shift;
+  uint32_t* dst = codes + (int64_t)row0 * words_per_row + (col >> 5) * BITS;
+  const int64_t g0 = (int64_t)row0 * groups_per_row + (col >> group_shift);
+  const bool group_lead = (lane & (lanes - 1)) == 0;
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      float v[8];
-      if (row_ok) {
-        load8(W + row * K + col0 + h * 8, v);
-      } else {
+  for (int p = 0; p < kPackRows; ++p) {
+    if (row0 + p >= N) break;                              // wave-uniform
+    float w[16], wp[16];
+    unpack16(raw[p], w);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = 0.0f;
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) wp[h * 8 + i] = v[i] * sv[h * 8 + i];
-    }
+    for (int i = 0; i < 16; ++i) wp[i] = w[i] * sv[i];
     float mn = wp[0], mx = wp[0];
 #pragma unroll
-    for (int i = 1; i < 32; ++i) {
+    for (int i = 1; i < 16; ++i) {
       mn = fminf(mn, wp[i]);
       mx = fmaxf(mx, wp[i]);
     }
     group_minmax(mn, mx, lanes);
     const GroupQ g = group_params(mn, mx, qmax, rq);
+    const float lim = safe_limit(mn, mx, g.rdelta, g.z);
 
-    // 32 codes of `bits` bits -> `bits` words; bit p of the slice is bit
-    // p%32 of word p/32.
-    uint32_t words[BITS];
+    float r[16];
+    bool risky = false;
 #pragma unroll
-    for (int i = 0; i < BITS; ++i) words[i] = 0u;
-#pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      const uint32_t c = (uint32_t)code_of(wp[j], g, qmax);
-      const int p = BITS * j;               // compile-time after unrolling
-      const int wi = p >> 5, sh = p & 31;
-      words[wi] |= c << sh;
-      if (sh + BITS > 32) words[wi + 1] |= c >> (32 - sh);   // BITS <= 8: two words at most
+    for (int i = 0; i < 16; ++i) {
+      const float t = fmaf(wp[i], g.rdelta, g.z);
+      r[i] = __builtin_rintf(t);
+      risky |= !(fabsf(t - r[i]) < lim);
     }
-    if (row_ok) {
-      uint32_t* dst = codes + row * (chunks_per_row * BITS) + cc * BITS;
+    if (__builtin_amdgcn_ballot_w64(risky) != 0) {         // wave-uniform
 #pragma unroll
-      for (int t = 0; t < BITS; ++t) dst[t] = words[t];
-      if ((cc % lanes) == 0) {
-        const int64_t gi = row * (K / group) + col0 / group;
-        scales[gi] = g.delta;
-        zeros[gi] = (uint8_t)g.z;
+      for (int i = 0; i < 16; ++i) r[i] = __builtin_rintf(div_rn(wp[i], g.delta, g.rdelta)) + g.z;
+    }
+    // the lane's 16 codes as NW words, bit BITS * i + b of code i at stream bit BITS * i + b
+    uint32_t f[NW];
+#pragma unroll
+    for (int q = 0; q < NW; ++q) f[q] = 0u;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t c = (uint32_t)__builtin_amdgcn_fmed3f(r[i], 0.0f, qmax);
+      const int pos = BITS * i;                            // compile-time after unrolling
+      f[pos >> 5] |= c << (pos & 31);
+      if ((pos & 31) + BITS > 32) f[(pos >> 5) + 1] |= c >> (32 - (pos & 31));
+    }
+    // the pair's BITS words: lane 0's codes at bit 0, lane 1's at bit 16 * BITS
+    uint32_t word[BITS];
+#pragma unroll
+    for (int wi = 0; wi < BITS; ++wi)
+      word[wi] = pair_or(j ? shifted_word<NW, 16 * BITS>(f, wi) : shifted_word<NW, 0>(f, wi));
+    if (col_ok) {
+#pragma unroll
+      for (int wi = 0; wi < BITS; ++wi)
+        if ((wi & 1) == j) dst[(int64_t)p * words_per_row + wi] = word[wi];
+      if (group_lead) {
+        scales[g0 + (int64_t)p * groups_per_row] = g.delta;
+        zeros[g0 + (int64_t)p * groups_per_row] = (uint8_t)g.z;
       }
     }
   }
@@ -402,20 +491,28 @@ hipError_t fq_dispatch(const void* W, int64_t N, int64_t K, const float* s, cons
 template <typename S>
 hipError_t pack_dispatch(const void* W, int64_t N, int64_t K, const float* s, int bits, int group,
                          uint32_t* codes, float* scales, uint8_t* zeros, hipStream_t st) {
-  const int64_t threads = (N + kPackRows - 1) / kPackRows * (K / 32);
-  const unsigned blocks = (unsigned)((threads + 255) / 256);
+  // the caller keeps N and K below 2^31 (operands below 4 GiB), so do the wave counts
+  const int col_blocks = (int)((K + kPackCols - 1) / kPackCols);
+  const int64_t waves = (int64_t)col_blocks * ((N + kPackRows - 1) / kPackRows);
+  if (waves > INT32_MAX - kPackWaves) return hipErrorInvalidValue;
+  const unsigned blocks = (unsigned)((waves + kPackWaves - 1) / kPackWaves);
   const S* w = static_cast<const S*>(W);
+  const int lanes = group / kPackLaneCols;
+  const int group_shift = __builtin_ctz((unsigned)group);
   ProfScope p("awq_quantize_pack", st);
-  const int lanes = group / 32;
+#define AWQ_PACK(B)                                                                               \
+  quantize_pack_kernel<S, B><<<blocks, 64 * kPackWaves, 0, st>>>(                                 \
+      w, (int)N, (int)K, s, group_shift, lanes, col_blocks, codes, scales, zeros)
   switch (bits) {
-    case 2: quantize_pack_kernel<S, 2><<<blocks, 256, 0, st>>>(w, N, K, s, group, lanes, codes, scales, zeros); break;
-    case 3: quantize_pack_kernel<S, 3><<<blocks, 256, 0, st>>>(w, N, K, s, group, lanes, codes, scales, zeros); break;
-    case 4: quantize_pack_kernel<S, 4><<<blocks, 256, 0, st>>>(w, N, K, s, group, lanes, codes, scales, zeros); break;
-    case 5: quantize_pack_kernel<S, 5><<<blocks, 256, 0, st>>>(w, N, K, s, group, lanes, codes, scales, zeros); break;
-    case 6: quantize_pack_kernel<S, 6><<<blocks, 256, 0, st>>>(w, N, K, s, group, lanes, codes, scales, zeros); break;
-    case 7: quantize_pack_kernel<S, 7><<<blocks, 256, 0, st>>>(w, N, K, s, group, lanes, codes, scales, zeros); break;
-    default: quantize_pack_kernel<S, 8><<<blocks, 256, 0, st>>>(w, N, K, s, group, lanes, codes, scales, zeros); break;
+    case 2: AWQ_PACK(2); break;
+    case 3: AWQ_PACK(3); break;
+    case 4: AWQ_PACK(4); break;
+    case 5: AWQ_PACK(5); break;
+    case 6: AWQ_PACK(6); break;
+    case 7: AWQ_PACK(7); break;
+    default: AWQ_PACK(8); break;
   }
+#undef AWQ_PACK
   return hipGetLastError();
 }
 

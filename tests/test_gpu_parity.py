@@ -171,6 +171,46 @@ def test_quantize_pack_unit_scale_is_rtn_and_unpacks():
     assert c.max() <= 7
 
 
+def near_tie_weights(N, K, bits, group, seed):
+    """fp32 weights whose quotients w / delta (with s = 1) sit on, or within
+    four ulps of, half-integers: where the rounding decision is closest to
+    flipping and the kernels must take their exact quotient.  The first two
+    entries of every group fix its min and max, so its step is known."""
+    rng = np.random.default_rng(seed)
+    qmax = F32((1 << bits) - 1)
+    W = np.empty((N, K), F32)
+    for i in range(N):
+        for g0 in range(0, K, group):
+            lo, hi = F32(-rng.uniform(0.2, 1.0)), F32(rng.uniform(0.2, 1.0))
+            delta = F32(F32(hi - lo) / qmax)
+            m = rng.integers(int(np.ceil(lo / delta)), int(np.floor(hi / delta)), group - 2)
+            w = ((m + 0.5) * np.float64(delta)).astype(F32)
+            for _ in range(4):    # up to 4 ulps away, either side, at random
+                step = rng.integers(-1, 2, group - 2)
+                w = np.where(step > 0, np.nextafter(w, F32(np.inf)),
+                             np.where(step < 0, np.nextafter(w, F32(-np.inf)), w)).astype(F32)
+            W[i, g0], W[i, g0 + 1] = lo, hi
+            W[i, g0 + 2:g0 + group] = np.clip(w, lo, hi)
+    return W
+
+
+@pytest.mark.parametrize("bits,group", [(2, 32), (3, 128), (4, 64), (8, 256)])
+def test_quantize_pack_near_ties(bits, group):
+    """Codes whose quotients lie on or next to half-integers: the kernel's fast
+    rounding decision must hand these to the exact quotient (bit-exact codes)."""
+    log_case(test="quantize_pack_near_ties", bits=bits, group=group)
+    N, K = 24, 1024
+    Wn = near_tie_weights(N, K, bits, group, 100 + bits)
+    for s in (np.ones(K, F32), np.full(K, F32(0.25))):    # power-of-two s keeps the ties
+        codes, scales, zeros = awq.awq_quantize_pack(torch.from_numpy(Wn).cuda(),
+                                                     torch.from_numpy(s).cuda(), bits, group)
+        torch.cuda.synchronize()
+        c_ref, d_ref, z_ref = oracle.quantize_pack(Wn, s, bits, group)
+        np.testing.assert_array_equal(codes.cpu().numpy().view(np.uint32), c_ref)
+        np.testing.assert_array_equal(scales.cpu().numpy(), d_ref)
+        np.testing.assert_array_equal(zeros.cpu().numpy(), z_ref)
+
+
 # ---------------------------------------------------------------------------
 # steps 2-5: the whole search
 # ---------------------------------------------------------------------------
