@@ -304,6 +304,24 @@ awq_status_t awq_lowbit_gemv(const void* X, awq_dtype_t x_dtype, int64_t M, int6
                              const uint32_t* codes_t, const void* meta_t, int64_t N, int bits,
                              int group, float* Y, void* workspace, size_t workspace_bytes,
                              hipStream_t stream);
+/* awq_lowbit_gemv_noalloc: awq_lowbit_gemv for callers that cannot allocate
+ *   device memory (code under HIP graph capture, tight serving loops,
+ *   harnesses that forbid allocation).  Same arguments, kernels, results (bit
+ *   for bit) and workspace-free cases as awq_lowbit_gemv; the k-split partial
+ *   sums go to a static array of AWQ_LOWBIT_STATIC_SCRATCH_BYTES that the
+ *   library keeps on each GPU it runs on until the process ends, instead of a
+ *   caller workspace.  The call allocates nothing (no hipMalloc, no library
+ *   allocation); the first call on a device looks the array's address up.
+ *   Sizes whose partial sums (awq_lowbit_gemv_workspace_size) exceed the
+ *   array return AWQ_ERR_UNSUPPORTED before anything is enqueued.  Every call
+ *   on one GPU shares that GPU's array: calls that overlap in time on one GPU
+ *   (other streams, other host threads) race and must not be issued.  The
+ *   array keeps the last call's partial sums; no call depends on its earlier
+ *   contents. */
+#define AWQ_LOWBIT_STATIC_SCRATCH_BYTES (32u << 20)
+awq_status_t awq_lowbit_gemv_noalloc(const void* X, awq_dtype_t x_dtype, int64_t M, int64_t K,
+                                     const uint32_t* codes_t, const void* meta_t, int64_t N,
+                                     int bits, int group, float* Y, hipStream_t stream);
 /* awq_lowbit_gemm: the same layer for many activation rows (prefill, M from
  *   a few tens up): the same Y, the same repacked operands, the same exact
  *   products x (c - z) with fp32 sums and one product by delta per group and

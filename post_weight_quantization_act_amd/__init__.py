@@ -23,7 +23,8 @@ __all__ = [
     "awq_fake_quant", "awq_search_layout", "awq_search_workspace_size", "awq_search_scales",
     "awq_quantize_pack",
     "awq_salient_keep_workspace_size", "awq_salient_keep_loss", "awq_lowbit_repack",
-    "awq_lowbit_gemv_workspace_size", "awq_lowbit_gemv", "awq_lowbit_gemm",
+    "awq_lowbit_gemv_workspace_size", "awq_lowbit_gemv", "awq_lowbit_gemv_noalloc",
+    "awq_lowbit_gemm", "AWQ_LOWBIT_STATIC_SCRATCH_BYTES",
     "awq_gptq_workspace_size",
     "awq_gptq_factor_ld", "awq_gptq_quantize", "awq_smooth_scales", "awq_quantize_rows_int8",
     "awq_w8a8_workspace_size", "awq_w8a8_loss",
@@ -36,6 +37,7 @@ AWQ_SEARCH_WEIGHT_DELTA = 0
 AWQ_SEARCH_REFERENCE_OUTPUT = 1
 AWQ_FQ_WEIGHT_HAT = 0
 AWQ_FQ_WEIGHT_DELTA = 1
+AWQ_LOWBIT_STATIC_SCRATCH_BYTES = 32 << 20
 
 _DTYPES = {torch.float32: AWQ_F32, torch.float16: AWQ_F16, torch.bfloat16: AWQ_BF16}
 _STATUS = {0: "AWQ_OK", -1: "AWQ_ERR_INVALID_ARG", -2: "AWQ_ERR_UNSUPPORTED",
@@ -94,6 +96,7 @@ _SIGS = {
     "awq_lowbit_repack": ([_P, _P, _P, _I64, _I64, _I32, _I32, _P, _P, _P], _I32),
     "awq_lowbit_gemv_workspace_size": ([_I32, _I64, _I64, _I64], _SZ),
     "awq_lowbit_gemv": ([_P, _I32, _I64, _I64, _P, _P, _I64, _I32, _I32, _P, _P, _SZ, _P], _I32),
+    "awq_lowbit_gemv_noalloc": ([_P, _I32, _I64, _I64, _P, _P, _I64, _I32, _I32, _P, _P], _I32),
     "awq_lowbit_gemm": ([_P, _I32, _I64, _I64, _P, _P, _I64, _I32, _I32, _P, _P], _I32),
     "awq_gptq_workspace_size": ([_I64, _I64, _I64], _SZ),
     "awq_gptq_factor_ld": ([_I64], _I64),
@@ -426,6 +429,25 @@ def awq_lowbit_gemv(Xs: torch.Tensor, codes_t: torch.Tensor, meta_t: torch.Tenso
                                      meta_t.data_ptr(), N, bits, group, out.data_ptr(),
                                      workspace.data_ptr(), workspace.numel(),
                                      _stream(Xs.device)))
+    return out
+
+
+def awq_lowbit_gemv_noalloc(Xs: torch.Tensor, codes_t: torch.Tensor, meta_t: torch.Tensor,
+                            bits: int, group: int, out: torch.Tensor) -> torch.Tensor:
+    """awq_lowbit_gemv with its partial sums in the library's static per-GPU
+    array instead of a workspace: the C call allocates nothing, and this
+    wrapper allocates nothing either (the caller passes `out`, [M, N] fp32)."""
+    _dev(Xs, "Xs")
+    _dev(codes_t, "codes_t")
+    _dev(meta_t, "meta_t")
+    _dev(out, "out")
+    M, K = Xs.shape
+    N = codes_t.shape[1]
+    if out.shape != (M, N) or out.dtype != torch.float32:
+        raise ValueError("out must be fp32 [M, N]")
+    _check(library().awq_lowbit_gemv_noalloc(Xs.data_ptr(), _dtype(Xs), M, K, codes_t.data_ptr(),
+                                             meta_t.data_ptr(), N, bits, group, out.data_ptr(),
+                                             _stream(Xs.device)))
     return out
 
 

@@ -660,6 +660,35 @@ awq_status_t awq_lowbit_gemv(const void* X, awq_dtype_t x_dtype, int64_t M, int6
   AWQ_GUARD_END
 }
 
+awq_status_t awq_lowbit_gemv_noalloc(const void* X, awq_dtype_t x_dtype, int64_t M, int64_t K,
+                                     const uint32_t* codes_t, const void* meta_t, int64_t N,
+                                     int bits, int group, float* Y, hipStream_t stream) {
+  AWQ_GUARD_BEGIN
+  awq_status_t st = check_quant_args(x_dtype, N, K, bits, group);
+  if (st != AWQ_OK) return st;
+  if (M < 1) return fail(AWQ_ERR_INVALID_ARG, "M must be >= 1");
+  if (!X || !codes_t || !meta_t || !Y) return fail(AWQ_ERR_INVALID_ARG, "null pointer");
+  if (!aligned(X, 16) || !aligned(codes_t, 4) || !aligned(meta_t, 8) || !aligned(Y, 4))
+    return fail(AWQ_ERR_UNSUPPORTED, "X 16-byte, codes_t and Y 4-byte, meta_t 8-byte aligned");
+  const size_t need = awq::lowbit_gemv_ws_bytes(x_dtype, M, N, K);
+  if (need > (size_t)AWQ_LOWBIT_STATIC_SCRATCH_BYTES)
+    return fail(AWQ_ERR_UNSUPPORTED,
+                "partial sums of %zu bytes exceed the static scratch of %u bytes (M=%lld N=%lld "
+                "K=%lld); use awq_lowbit_gemv with a workspace",
+                need, (unsigned)AWQ_LOWBIT_STATIC_SCRATCH_BYTES, (long long)M, (long long)N,
+                (long long)K);
+  void* ws = nullptr;
+  if (need > 0) {
+    hipError_t e = awq::lowbit_static_scratch(&ws);
+    if (e != hipSuccess) return hip_fail(e, "static scratch lookup");
+  }
+  hipError_t e = awq::launch_lowbit_gemv(X, x_dtype, M, K, codes_t, meta_t, N, bits, group, Y, ws,
+                                         stream);
+  if (e != hipSuccess) return hip_fail(e, "lowbit gemv launch");
+  return AWQ_OK;
+  AWQ_GUARD_END
+}
+
 awq_status_t awq_lowbit_gemm(const void* X, awq_dtype_t x_dtype, int64_t M, int64_t K,
                              const uint32_t* codes_t, const void* meta_t, int64_t N, int bits,
                              int group, float* Y, hipStream_t stream) {

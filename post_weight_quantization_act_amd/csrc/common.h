@@ -126,6 +126,9 @@ size_t lowbit_gemv_ws_bytes(awq_dtype_t dt, int64_t M, int64_t N, int64_t K);
 hipError_t launch_lowbit_gemv(const void* X, awq_dtype_t dt, int64_t M, int64_t K,
                               const uint32_t* codes_t, const void* meta_t, int64_t N, int bits,
                               int group, float* Y, void* ws, hipStream_t st);
+// Device address of this GPU's static scratch array for the allocation-free
+// GEMV (AWQ_LOWBIT_STATIC_SCRATCH_BYTES), looked up on the first call per device.
+hipError_t lowbit_static_scratch(void** out);
 // fp16/bf16 activations only; K a multiple of the group, group >= 32.
 hipError_t launch_lowbit_gemm(const void* X, awq_dtype_t dt, int64_t M, int64_t K,
                               const uint32_t* codes_t, const void* meta_t, int64_t N, int bits,

@@ -27,6 +27,7 @@
 // per workgroup to make the partials visible across XCDs, which measured
 // slower than the second launch.)
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "common.h"
@@ -1118,6 +1119,36 @@ hipError_t launch_lowbit_gemv(const void* X, awq_dtype_t dt, int64_t M, int64_t 
     case AWQ_F16: return gemv_bits<_Float16>(bits, X, M, K, codes_t, meta, N, group, Y, partials, st);
     default: return gemv_bits<__bf16>(bits, X, M, K, codes_t, meta, N, group, Y, partials, st);
   }
+}
+
+// ---- allocation-free GEMV: the partial sums in a static array ----------------
+// One array per GPU: the runtime places it when this code object is loaded on
+// the device and it stays until the process ends.  In host code `scratch`
+// names a host-side stand-in, not the device address, so every use goes
+// through the address hipGetSymbolAddress returns, looked up once per device
+// with that device current.
+static __device__ __align__(256) unsigned char scratch[AWQ_LOWBIT_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t lowbit_static_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress((void**)&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_lowbit_gemm(const void* X, awq_dtype_t dt, int64_t M, int64_t K,

@@ -201,6 +201,23 @@ def test_lowbit_gemv_validation(over, status):
     assert _call("awq_lowbit_gemv", *_gemv_args(**over)) == status
 
 
+@pytest.mark.parametrize("over,status", [
+    (dict(X=NULL), -1),
+    (dict(Y=NULL), -1),
+    (dict(M=0), -1),
+    (dict(K=200), -1),
+    (dict(bits=9), -2),
+    (dict(X=ctypes.c_void_p(0x1008)), -2),
+    (dict(dt=0, M=4000, N=8192, K=4096), -2),     # partial sums beyond the static array
+])
+def test_lowbit_gemv_noalloc_validation(over, status):
+    a = dict(X=FAKE, dt=1, M=2, K=256, codes_t=FAKE, meta_t=FAKE, N=300, bits=4, group=128,
+             Y=FAKE, stream=NULL)
+    a.update(over)
+    assert _call("awq_lowbit_gemv_noalloc", *tuple(a.values())) == status
+    assert awq.library().awq_last_error().decode() != ""
+
+
 def _gemm_args(**over):
     a = dict(X=FAKE, dt=1, M=300, K=256, codes_t=FAKE, meta_t=FAKE, N=300, bits=4, group=128,
              Y=FAKE, stream=NULL)
