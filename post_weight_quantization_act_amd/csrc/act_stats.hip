@@ -6,25 +6,26 @@
 // gathered on calibration data.
 //
 // X is row-major [T, K]; the reduction runs down the columns, so a wavefront
-// reads rows: 16 lanes cover 256 contiguous bytes of one row and the 4 lane
-// sets of a wave read 4 rows.  Every lane accumulates its columns in fp64.
+// reads rows: 32 lanes cover 512 contiguous bytes of one row and the 2 lane
+// sets of a wave read 2 rows.  Every lane accumulates its columns in fp64.
 // Pass 1 sums a fixed chunk of rows per workgroup into fp64 partials
-// [chunks, K]; pass 2 adds the chunks in a fixed order (four interleaved
-// running sums) and divides by T, so the result does not depend on scheduling.
+// [chunks, K]; pass 2 adds each column's chunks in a fixed order (8 lanes per
+// column, each a strided share of the chunks, then a fixed tree in LDS) and
+// divides by T, so the result does not depend on scheduling.
 #include "common.h"
 
 namespace awq {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kColThreads = 16;
+constexpr int kColThreads = 32;
 constexpr int kRowThreads = kThreads / kColThreads;
 constexpr int kTargetBlocks = 2048;   // ~8 workgroups per CU on 256 CUs
 constexpr int kMinRowsPerChunk = 64;
 
 // Chunking depends only on (T, K) so the workspace query needs no dtype.
 void chunking(int64_t T, int64_t K, int64_t* chunks, int64_t* rows_per_chunk) {
-  int64_t gx_ref = (K + 127) / 128;
+  int64_t gx_ref = (K + 255) / 256;
   int64_t c = (kTargetBlocks + gx_ref - 1) / gx_ref;
   int64_t cmax = (T + kMinRowsPerChunk - 1) / kMinRowsPerChunk;
   if (c > cmax) c = cmax;
@@ -110,23 +111,35 @@ __global__ __launch_bounds__(kThreads) void act_stats_partial(const S* __restric
   }
 }
 
-__global__ __launch_bounds__(256) void act_stats_finish(const double* __restrict__ part,
-                                                        int64_t chunks, int64_t K, int64_t T,
-                                                        float* __restrict__ a) {
-  const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (j >= K) return;
-  // four interleaved running sums (chunks c = 0,4,8,.. / 1,5,9,.. / ...),
-  // added together in a fixed order: deterministic, and four loads in flight
-  double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
-  int64_t c = 0;
-  for (; c + 3 < chunks; c += 4) {
-    s0 += part[c * K + j];
-    s1 += part[(c + 1) * K + j];
-    s2 += part[(c + 2) * K + j];
-    s3 += part[(c + 3) * K + j];
+// One workgroup per 32 columns: lane group q (8 lanes per column) sums chunks
+// q, q + 8, q + 16, ... of its column, then the 8 sums are added in a fixed
+// tree through LDS.
+constexpr int kFinCols = 32;
+constexpr int kFinSplit = kThreads / kFinCols;
+
+__global__ __launch_bounds__(kThreads) void act_stats_finish(const double* __restrict__ part,
+                                                             int64_t chunks, int64_t K, int64_t T,
+                                                             float* __restrict__ a) {
+  __shared__ double red[kFinSplit][kFinCols];
+  const int c = threadIdx.x % kFinCols, q = threadIdx.x / kFinCols;
+  const int64_t j = (int64_t)blockIdx.x * kFinCols + c;
+  double s0 = 0.0, s1 = 0.0;
+  if (j < K) {
+    int64_t i = q;
+    for (; i + kFinSplit < chunks; i += 2 * kFinSplit) {
+      s0 += part[i * K + j];
+      s1 += part[(i + kFinSplit) * K + j];
+    }
+    if (i < chunks) s0 += part[i * K + j];
   }
-  for (; c < chunks; ++c) s0 += part[c * K + j];
-  a[j] = (float)(((s0 + s1) + (s2 + s3)) / (double)T);
+  red[q][c] = s0 + s1;
+  __syncthreads();
+#pragma unroll
+  for (int w = kFinSplit / 2; w >= 1; w >>= 1) {
+    if (q < w) red[q][c] += red[q + w][c];
+    __syncthreads();
+  }
+  if (q == 0 && j < K) a[j] = (float)(red[0][c] / (double)T);
 }
 
 template <typename S>
@@ -151,7 +164,8 @@ hipError_t run(const void* X, int64_t T, int64_t K, float* a, void* ws, hipStrea
   if (e != hipSuccess) return e;
   {
     ProfScope p("awq_act_stats_finish", st);
-    act_stats_finish<<<(unsigned)((K + 255) / 256), 256, 0, st>>>(part, chunks, K, T, a);
+    act_stats_finish<<<(unsigned)((K + kFinCols - 1) / kFinCols), kThreads, 0, st>>>(part, chunks, K,
+                                                                                   T, a);
   }
   return hipGetLastError();
 }

@@ -96,6 +96,32 @@ __device__ __forceinline__ float code_minus_z(float wp, const GroupQ& g, float q
   return __builtin_amdgcn_fmed3f(__builtin_rintf(div_rn(wp, g.delta, g.rdelta)), -g.z, qmax - g.z);
 }
 
+// ---------------------------------------------------------------------------
+// Rounding decision of the code without the exact quotient.
+//
+// The oracle's code is c = clamp(rint(RN(w'/delta)) + z, 0, qmax).  With
+// y = RN(1/delta) (a correctly rounded division, once per group) the kernel
+// forms t = RN(w' * y + z) (one fma).  Let Q = w'/delta and V = RN(Q) + z.
+// Then |t - V| <= 2^-24 (3 |Q| + z) + 2^-149: y and the fma each round once
+// (relative 2^-24) and RN(Q) is within 2^-24 |Q| of Q.  If t lies farther than
+// that from every half-integer, V rounds to the same integer as t and is no
+// tie, so rint(t) = rint(RN(Q)) + z exactly (z is an integer) and
+// c = clamp(rint(t), 0, qmax).  The group-wide bound uses M = max(-mn, mx)
+// >= |w'|:
+//   lim = 1/2 - (M y 2^-21 + (z + 1) 2^-23)
+// 2^-21 covers 3 * 2^-24 |Q| with room for the roundings of the bound itself,
+// and (z + 1) 2^-23 covers 2^-24 z plus the rounding of lim (at most 2^-25)
+// and the underflow term.  A code is safe when |t - rint(t)| < lim (t - rint(t)
+// is exact); otherwise, or when lim <= 0, the wave recomputes the row's
+// quotients exactly.  Clamping t to [-1/4, qmax + 1/4] before the test leaves
+// it valid: a t beyond those bounds gets code 0 or qmax whichever way its
+// exact value rounds, and the clamped t is 1/4 from its rounding.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float safe_limit(float mn, float mx, float y, float z) {
+  const float m = fmaxf(-mn, mx);
+  return 0.5f - (m * y * 0x1p-21f + (z + 1.0f) * 0x1p-23f);
+}
+
 constexpr float kRecipSafeLo = 0x1p-60f, kRecipSafeHi = 0x1p60f;
 
 template <typename S>
@@ -129,6 +155,25 @@ __device__ __forceinline__ void store8(S* p, const float (&v)[8]) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) e[i] = from_f32<S>(v[i]);
   *reinterpret_cast<i32x4*>(p) = raw;
+}
+
+// 8 consecutive elements of a row in their storage type (16 bytes; 32 for fp32).
+template <typename S>
+struct WRow {
+  i32x4 v[sizeof(S) / 2];
+};
+template <typename S>
+__device__ __forceinline__ WRow<S> load_wrow(const S* p) {
+  WRow<S> r;
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(S) / 2); ++i) r.v[i] = reinterpret_cast<const i32x4*>(p)[i];
+  return r;
+}
+template <typename S>
+__device__ __forceinline__ void widen_wrow(const WRow<S>& r, float (&v)[8]) {
+  const S* e = reinterpret_cast<const S*>(&r.v[0]);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = to_f32(e[i]);
 }
 
 // ---------------------------------------------------------------------------
@@ -180,17 +225,20 @@ __global__ __launch_bounds__(kFqThreads) void fake_quant_kernel(
   const int64_t row0 = (int64_t)blockIdx.y * kFqRows + wave;
   const bool col_ok = col < K;
 
-  float w[kFqRowSteps][8];
+  // The tile stays in registers in its storage type (8 16-bit values in four
+  // registers per row), widened to fp32 per scale vector: half the registers
+  // of an fp32 copy, for one shift or conversion per element.
+  WRow<S> wraw[kFqRowSteps];
   bool row_ok[kFqRowSteps];
 #pragma unroll
   for (int p = 0; p < kFqRowSteps; ++p) {
     const int64_t r = row0 + (int64_t)p * (kFqThreads / 64);
     row_ok[p] = r < N;
     if (col_ok && row_ok[p]) {
-      load8(W + r * K + col, w[p]);
+      wraw[p] = load_wrow(W + r * K + col);
     } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) w[p][i] = 0.0f;
+      for (int i = 0; i < (int)(sizeof(S) / 2); ++i) wraw[p].v[i] = i32x4{0, 0, 0, 0};
     }
   }
 
@@ -218,10 +266,11 @@ __global__ __launch_bounds__(kFqThreads) void fake_quant_kernel(
     O* outk = out + (int64_t)k * out_rows * K;
 #pragma unroll
     for (int p = 0; p < kFqRowSteps; ++p) {
-      float wp[8];
+      float w[8], wp[8];
       float mn, mx;
+      widen_wrow(wraw[p], w);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) wp[i] = w[p][i] * sv[i];
+      for (int i = 0; i < 8; ++i) wp[i] = w[i] * sv[i];
       if (kKeep) {
         mn = kept[0] ? __builtin_inff() : wp[0];
         mx = kept[0] ? -__builtin_inff() : wp[0];
@@ -241,13 +290,32 @@ __global__ __launch_bounds__(kFqThreads) void fake_quant_kernel(
       }
       group_minmax(mn, mx, lanes);
       const GroupQ g = group_params(mn, mx, qmax, rq);
+      // c - z = clamp(rint(w' / delta), -z, qmax - z), decided from t = RN(w' y)
+      // (the bound of safe_limit holds with z = 0 in the fma, so it holds here);
+      // t is clamped to [-z - 1/4, qmax - z + 1/4] and rounded to an integer by
+      // adding 1.5 * 2^23 (spacing 1 there, even, ties to even), which also
+      // gives the exact difference to t.  A risky lane sends the wave to the
+      // exact quotients.
+      const float lim = safe_limit(mn, mx, g.rdelta, g.z);
+      float cmz[8];
+      bool risky = false;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float t = __builtin_amdgcn_fmed3f(wp[i] * g.rdelta, -g.z - 0.25f, qmax - g.z + 0.25f);
+        cmz[i] = (t + 0x1.8p23f) - 0x1.8p23f;
+        risky |= !(fabsf(t - cmz[i]) < lim);
+      }
+      if (__builtin_amdgcn_ballot_w64(risky) != 0) {       // wave-uniform
+#pragma unroll
+        for (int i = 0; i < 8; ++i) cmz[i] = code_minus_z(wp[i], g, qmax);
+      }
       float o[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float deq = code_minus_z(wp[i], g, qmax) * g.delta;
+        const float deq = cmz[i] * g.delta;
         const float what = exact_div ? deq / sv[i] : div_rn(deq, sv[i], ys[i]);
-        o[i] = kDelta ? (w[p][i] - what) : what;
-        if (kKeep && kept[i]) o[i] = kDelta ? 0.0f : w[p][i];
+        o[i] = kDelta ? (w[i] - what) : what;
+        if (kKeep && kept[i]) o[i] = kDelta ? 0.0f : w[i];
       }
       const int64_t r = row0 + (int64_t)p * (kFqThreads / 64);
       if (kTiled) {
@@ -264,30 +332,6 @@ __global__ __launch_bounds__(kFqThreads) void fake_quant_kernel(
       }
     }
   }
-}
-
-// ---------------------------------------------------------------------------
-// Rounding decision of the code without the exact quotient.
-//
-// The oracle's code is c = clamp(rint(RN(w'/delta)) + z, 0, qmax).  With
-// y = RN(1/delta) (a correctly rounded division, once per group) the kernel
-// forms t = RN(w' * y + z) (one fma).  Let Q = w'/delta and V = RN(Q) + z.
-// Then |t - V| <= 2^-24 (3 |Q| + z) + 2^-149: y and the fma each round once
-// (relative 2^-24) and RN(Q) is within 2^-24 |Q| of Q.  If t lies farther than
-// that from every half-integer, V rounds to the same integer as t and is no
-// tie, so rint(t) = rint(RN(Q)) + z exactly (z is an integer) and
-// c = clamp(rint(t), 0, qmax).  The group-wide bound uses M = max(-mn, mx)
-// >= |w'|:
-//   lim = 1/2 - (M y 2^-21 + (z + 1) 2^-23)
-// 2^-21 covers 3 * 2^-24 |Q| with room for the roundings of the bound itself,
-// and (z + 1) 2^-23 covers 2^-24 z plus the rounding of lim (at most 2^-25)
-// and the underflow term.  A code is safe when |t - rint(t)| < lim (t - rint(t)
-// is exact); otherwise, or when lim <= 0, the wave recomputes the row's
-// quotients exactly.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ float safe_limit(float mn, float mx, float y, float z) {
-  const float m = fmaxf(-mn, mx);
-  return 0.5f - (m * y * 0x1p-21f + (z + 1.0f) * 0x1p-23f);
 }
 
 // ---------------------------------------------------------------------------
@@ -412,17 +456,25 @@ __global__ __launch_bounds__(64 * kPackWaves) void quantize_pack_kernel(
     const GroupQ g = group_params(mn, mx, qmax, rq);
     const float lim = safe_limit(mn, mx, g.rdelta, g.z);
 
-    float r[16];
+    // Code = clamp(rint(t), 0, qmax).  t is first clamped to [-1/4, qmax + 1/4]
+    // (beyond, the clamp decides the code whatever the rounding); adding 2^23
+    // then rounds it to the nearest integer, ties to even (2^23 is even, and
+    // just below 2^23 the tie at -1/4 goes up to 2^23), leaving rint(t) in
+    // the low mantissa bits; the difference to t is exact.
+    uint32_t code[16];
     bool risky = false;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const float t = fmaf(wp[i], g.rdelta, g.z);
-      r[i] = __builtin_rintf(t);
-      risky |= !(fabsf(t - r[i]) < lim);
+      const float t = __builtin_amdgcn_fmed3f(fmaf(wp[i], g.rdelta, g.z), -0.25f, qmax + 0.25f);
+      const float u = t + 0x1p23f;
+      risky |= !(fabsf(t - (u - 0x1p23f)) < lim);
+      code[i] = __float_as_uint(u) - 0x4B000000u;        // bits of 2^23
     }
     if (__builtin_amdgcn_ballot_w64(risky) != 0) {         // wave-uniform
 #pragma unroll
-      for (int i = 0; i < 16; ++i) r[i] = __builtin_rintf(div_rn(wp[i], g.delta, g.rdelta)) + g.z;
+      for (int i = 0; i < 16; ++i)
+        code[i] = (uint32_t)__builtin_amdgcn_fmed3f(
+            __builtin_rintf(div_rn(wp[i], g.delta, g.rdelta)) + g.z, 0.0f, qmax);
     }
     // the lane's 16 codes as NW words, bit BITS * i + b of code i at stream bit BITS * i + b
     uint32_t f[NW];
@@ -430,7 +482,7 @@ __global__ __launch_bounds__(64 * kPackWaves) void quantize_pack_kernel(
     for (int q = 0; q < NW; ++q) f[q] = 0u;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const uint32_t c = (uint32_t)__builtin_amdgcn_fmed3f(r[i], 0.0f, qmax);
+      const uint32_t c = code[i];
       const int pos = BITS * i;                            // compile-time after unrolling
       f[pos >> 5] |= c << (pos & 31);
       if ((pos & 31) + BITS > 32) f[(pos >> 5) + 1] |= c >> (32 - (pos & 31));

@@ -211,6 +211,25 @@ def test_quantize_pack_near_ties(bits, group):
         np.testing.assert_array_equal(zeros.cpu().numpy(), z_ref)
 
 
+@pytest.mark.parametrize("bits,group", [(2, 32), (3, 128), (4, 64), (8, 256)])
+@pytest.mark.parametrize("delta", [False, True])
+def test_fake_quant_near_ties(bits, group, delta):
+    """Quotients on or next to half-integers through the fake quantisation:
+    its fast decision of c - z must hand these to the exact quotient."""
+    log_case(test="fake_quant_near_ties", bits=bits, group=group, delta=delta)
+    N, K = 24, 1024
+    Wn = near_tie_weights(N, K, bits, group, 200 + bits)
+    s = np.stack([np.ones(K, F32), np.full(K, F32(0.25))])
+    out = awq.awq_fake_quant(torch.from_numpy(Wn).cuda(), torch.from_numpy(s).cuda(), bits, group,
+                             awq.AWQ_FQ_WEIGHT_DELTA if delta else awq.AWQ_FQ_WEIGHT_HAT)
+    got = dev_f32(out)
+    for k in range(2):
+        what = oracle.fake_quant(Wn, s[k], bits, group)
+        ref = (Wn - what).astype(F32) if delta else what
+        bad = got[k] != ref
+        assert not bad.any(), (k, np.argwhere(bad)[:5])
+
+
 # ---------------------------------------------------------------------------
 # steps 2-5: the whole search
 # ---------------------------------------------------------------------------
