@@ -60,7 +60,15 @@
 extern "C" {
 #endif
 
-typedef enum { AWQ_F32 = 0, AWQ_F16 = 1, AWQ_BF16 = 2 } awq_dtype_t;
+/* AWQ_DTYPE_MAX_ENUM is no dtype: it gives the enumeration the range of a
+ * 32-bit int, so that whatever value a caller passes is a valid value for the
+ * library to check (and refuse), in C and in C++ alike. */
+typedef enum {
+  AWQ_F32 = 0,
+  AWQ_F16 = 1,
+  AWQ_BF16 = 2,
+  AWQ_DTYPE_MAX_ENUM = 0x7fffffff
+} awq_dtype_t;
 
 typedef enum {
   AWQ_OK = 0,
