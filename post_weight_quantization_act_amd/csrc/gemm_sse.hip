@@ -492,30 +492,44 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(Epi epi, const float* __r
 }
 
 // ============================================================================
-// loss[k] = (sum of partials of alpha k, fixed order) / (T N); argmin (lowest
-// index on a tie); s_best = s_table[argmin].  One workgroup of 16 waves: wave w
-// reduces alphas w, w + 16, ... (each lane a strided slice of the tiles, then a
-// fixed butterfly across the wave), then one lane takes the argmin and all
-// lanes copy the winning row of the scale table.
+// loss[k] = (sum of partials of alpha k, fixed order) / (T N), one workgroup
+// per alpha: lane t sums tiles t, t + 1024, ... in index order, then a fixed
+// butterfly across each wave and a fixed sum over the 16 waves.  Then one
+// workgroup takes the argmin (lowest index on a tie) and copies s_best =
+// s_table[argmin].
 // ============================================================================
 constexpr int kLossThreads = 1024;
 
+__global__ __launch_bounds__(kLossThreads) void loss_reduce_kernel(
+    const double* __restrict__ partials, int64_t tiles, double inv_count,
+    double* __restrict__ losses) {
+  __shared__ double red[kLossThreads / 64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const double* p = partials + (int64_t)blockIdx.x * tiles;
+  double s0 = 0.0, s1 = 0.0;
+  int64_t i = threadIdx.x;
+  for (; i + kLossThreads < tiles; i += 2 * kLossThreads) {
+    s0 += p[i];
+    s1 += p[i + kLossThreads];
+  }
+  if (i < tiles) s0 += p[i];
+  double s = s0 + s1;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+  if (lane == 0) red[wave] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double t = 0.0;
+#pragma unroll
+    for (int w = 0; w < kLossThreads / 64; ++w) t += red[w];
+    losses[blockIdx.x] = t * inv_count;
+  }
+}
+
 __global__ __launch_bounds__(kLossThreads) void loss_argmin_kernel(
-    const double* __restrict__ partials, int n_alpha, int64_t tiles, double inv_count,
-    const float* __restrict__ s_table, int64_t K, double* __restrict__ losses,
+    const double* __restrict__ losses, int n_alpha, const float* __restrict__ s_table, int64_t K,
     int32_t* __restrict__ best, float* __restrict__ s_best) {
   __shared__ int best_sh;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int k = wave; k < n_alpha; k += kLossThreads / 64) {
-    const double* p = partials + (int64_t)k * tiles;
-    double s = 0.0;
-    for (int64_t i = lane; i < tiles; i += 64) s += p[i];
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
-    if (lane == 0) losses[k] = s * inv_count;
-  }
-  __threadfence_block();
-  __syncthreads();
   if (threadIdx.x == 0) {
     int bi = 0;
     for (int k = 1; k < n_alpha; ++k)
@@ -632,8 +646,11 @@ hipError_t launch_loss_argmin(const double* partials, int n_alpha, int64_t tiles
                               double inv_count, const float* s_table, int64_t K, double* losses,
                               int32_t* best, float* s_best, hipStream_t st) {
   ProfScope p("awq_loss_argmin", st);
-  loss_argmin_kernel<<<1, kLossThreads, 0, st>>>(partials, n_alpha, tiles_per_alpha, inv_count, s_table, K,
-                                        losses, best, s_best);
+  loss_reduce_kernel<<<(unsigned)n_alpha, kLossThreads, 0, st>>>(partials, tiles_per_alpha,
+                                                                 inv_count, losses);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  loss_argmin_kernel<<<1, kLossThreads, 0, st>>>(losses, n_alpha, s_table, K, best, s_best);
   return hipGetLastError();
 }
 
