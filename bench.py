@@ -50,6 +50,9 @@ def parse():
     p.add_argument("--hbm-reps", type=int, default=3,
                    help="cache-evicted repetitions per HBM-bound pass")
     p.add_argument("--flags", type=int, default=0, help="0 weight-delta form, 1 reference-output form")
+    p.add_argument("--alpha-batch", type=int, default=0,
+                   help="size the search workspace for this many candidates per fake-quant + GEMM "
+                        "launch (0: the library's default layout)")
     p.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--lowbit", action="store_true",
@@ -585,6 +588,10 @@ def main():
     N, K, T = spec.N, spec.K, spec.T
     alphas = (np.arange(spec.n_alpha, dtype=np.float64) / spec.n_alpha).astype(np.float32)
     lay = awq.awq_search_layout(Wd.dtype, N, K, T, spec.n_alpha, args.flags, 0)
+    if args.alpha_batch:
+        per_alpha = (lay["total_bytes"] - lay["w_hat_offset"]) // lay["alpha_batch"]
+        lay = awq.awq_search_layout(Wd.dtype, N, K, T, spec.n_alpha, args.flags,
+                                    lay["w_hat_offset"] + args.alpha_batch * per_alpha)
     ws = torch.empty(lay["total_bytes"], dtype=torch.uint8, device=dev)
     a = torch.empty(K, dtype=torch.float32, device=dev)
     ws_stats = torch.empty(max(1, awq.awq_act_stats_workspace_size(T, K)), dtype=torch.uint8,

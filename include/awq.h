@@ -173,9 +173,11 @@ awq_status_t awq_fake_quant(const void* W, awq_dtype_t w_dtype, int64_t N, int64
  *
  * workspace: device scratch laid out as awq_search_layout() reports for the
  * same arguments and workspace_bytes.  With the full size (layout with
- * workspace_bytes = 0) every alpha is fake-quantised and scored in one batch;
- * a smaller workspace (at least one alpha's W_hat) makes the library process
- * the grid in batches of layout.alpha_batch.  After the call the workspace
+ * workspace_bytes = 0) every alpha is fake-quantised in one batch (one launch,
+ * W read once); a smaller workspace (at least one alpha's W_hat) makes the
+ * library process the grid in batches of layout.alpha_batch.  A batch's
+ * candidate GEMMs run in launches of at most 8 TFLOP of work each (2 T N K
+ * per alpha; at least one alpha per launch).  Losses do not depend on either.  After the call the workspace
  * holds the scale table, the reference output (REFERENCE_OUTPUT form), the
  * tiled copy of X, the last batch's D (or W_hat) and the per-tile partial
  * sums, at the reported offsets.
@@ -206,18 +208,19 @@ typedef struct {
 } awq_search_layout_t;
 
 /* Host-only query (no device work).  workspace_bytes = 0 asks for the layout
- * that scores every alpha in one batch; otherwise the largest batch that fits
- * in workspace_bytes.  AWQ_ERR_WORKSPACE if not even one alpha fits. */
+ * that fake-quantises every alpha in one batch; otherwise the largest batch
+ * that fits in workspace_bytes.  AWQ_ERR_WORKSPACE if not even one alpha
+ * fits. */
 awq_status_t awq_search_layout(awq_dtype_t dtype, int64_t N, int64_t K, int64_t T,
                                int n_alpha, uint32_t flags, size_t workspace_bytes,
                                awq_search_layout_t* layout_out);
 
-/* Host-only query: workspace bytes that let awq_search_scales score all
- * n_alpha candidates of a W [N, K], X [T, K] layer in one batch with the
+/* Host-only query: workspace bytes that let awq_search_scales fake-quantise
+ * all n_alpha candidates of a W [N, K], X [T, K] layer in one batch with the
  * default form (AWQ_SEARCH_WEIGHT_DELTA), whatever the layer dtype: the
  * largest layout.total_bytes that awq_search_layout reports over AWQ_F32,
- * AWQ_F16 and AWQ_BF16 for workspace_bytes = 0.  0 when a size is < 1 or
- * n_alpha is outside [1, 4096].  The reference-output form needs
+ * AWQ_F16 and AWQ_BF16 for workspace_bytes = 0.  0 when a size is
+ * < 1 or n_alpha is outside [1, 4096].  The reference-output form needs
  * awq_search_layout's figure, which adds the fp32 [T][N] layer output. */
 size_t awq_search_workspace_size(int64_t N, int64_t K, int64_t T, int n_alpha);
 

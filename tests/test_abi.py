@@ -157,7 +157,7 @@ def test_search_workspace_size_covers_every_dtype():
         sizes = [awq.awq_search_layout(dt, N, K, T, n, awq.AWQ_SEARCH_WEIGHT_DELTA, 0)
                  for dt in (torch.float32, torch.float16, torch.bfloat16)]
         assert got == max(lay["total_bytes"] for lay in sizes)
-        # a workspace of that size scores the whole grid in one batch for every dtype
+        # a workspace of that size fake-quantises the whole grid in one batch for every dtype
         for dt in (torch.float32, torch.float16, torch.bfloat16):
             lay = awq.awq_search_layout(dt, N, K, T, n, awq.AWQ_SEARCH_WEIGHT_DELTA, got)
             assert lay["alpha_batch"] == n

@@ -113,10 +113,21 @@ def test_full_size_layer(name):
     alphas = oracle.alpha_grid(spec.n_alpha)
     Wd, Xd = W.cuda(), X.cuda()
     a = awq.awq_act_stats(Xd)
+    # the whole grid in one batch (the benchmark's layout: every candidate's D
+    # stays in the workspace); then a workspace for 3 candidates (seven
+    # batches), whose losses must be the same bits
     res = awq.awq_search_scales(Wd, Xd, a, bits, G, alphas)
+    full = res["layout"]
+    per_alpha = (full["total_bytes"] - full["w_hat_offset"]) // full["alpha_batch"]
+    ws3 = torch.empty(full["w_hat_offset"] + 3 * per_alpha, dtype=torch.uint8, device="cuda")
+    res3 = awq.awq_search_scales(Wd, Xd, a, bits, G, alphas, workspace=ws3)
     codes, scales, zeros = awq.awq_quantize_pack(Wd, res["s_best"], bits, G)
     torch.cuda.synchronize()
     print("  gpu done", flush=True)
+    assert res3["layout"]["alpha_batch"] == 3
+    assert torch.equal(res3["losses"], res["losses"])
+    assert torch.equal(res3["best_idx"], res["best_idx"])
+    del res3, ws3
 
     # statistics over the whole of X
     a_ref = oracle.act_stats(Xn)
