@@ -637,8 +637,8 @@ def main():
 
     ms_per_step = 1e3 * elapsed / args.steps
     value = spec.n_alpha * args.steps / elapsed
-    # the library may split the candidates over several launches (a batch that
-    # does not fit the workspace, or the two overlapped halves of one that does)
+    # the library runs the candidate GEMMs in launches of a few rounds of its
+    # persistent grid: flop per launch is the step's GEMM flop over its launches
     flop_per_launch = 2.0 * T * N * K * spec.n_alpha * args.steps / max(n_gemm, 1)
     avg_ms = ms_gemm / max(n_gemm, 1)
     achieved = flop_per_launch / (avg_ms * 1e-3) / 1e12

@@ -176,11 +176,12 @@ awq_status_t awq_fake_quant(const void* W, awq_dtype_t w_dtype, int64_t N, int64
  * workspace_bytes = 0) every alpha is fake-quantised in one batch (one launch,
  * W read once); a smaller workspace (at least one alpha's W_hat) makes the
  * library process the grid in batches of layout.alpha_batch.  A batch's
- * candidate GEMMs run in launches of at most 8 TFLOP of work each (2 T N K
- * per alpha; at least one alpha per launch).  Losses do not depend on either.  After the call the workspace
- * holds the scale table, the reference output (REFERENCE_OUTPUT form), the
- * tiled copy of X, the last batch's D (or W_hat) and the per-tile partial
- * sums, at the reported offsets.
+ * fp16/bf16 candidate GEMMs run in launches of 4 rounds of the persistent grid
+ * (4 x 256 output tiles of 256 x 256 on 256 compute units), the last launch
+ * of a batch taking the rest.  Losses do not depend on either.  After the
+ * call the workspace holds the scale table, the reference output
+ * (REFERENCE_OUTPUT form), the tiled copy of X, the last batch's D (or W_hat)
+ * and the per-tile partial sums, at the reported offsets.
  *
  * Tiled layout (fp16/bf16 GEMM operands): rows padded with zeros to a multiple
  * of 256, K split in stages of 32.  Element (row, k) of a [rows, K] matrix

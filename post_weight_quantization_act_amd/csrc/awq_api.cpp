@@ -36,7 +36,7 @@ awq_status_t hip_fail(hipError_t e, const char* what) {
 
 constexpr uint64_t kMaxBufferBytes = 0xFFFFFF00ull;  // byte offsets inside kernels are 32-bit
 constexpr int kMaxAlpha = 4096;
-constexpr double kLaunchFlop = 8e12;   // candidate-GEMM flop per launch
+constexpr int kLaunchRounds = 4;      // candidate-GEMM rounds of the persistent grid per launch
 constexpr int64_t kGptqMaxK = 32768;   // the fp64 factor matrix is K^2 * 8 bytes
 constexpr int64_t kLowbitGemmMaxM = 65535ll * 128;  // activation-row tiles on grid y
 constexpr int64_t kLowbitGemmMaxK = 1ll << 22;       // a 256-row activation tile in 32-bit offsets
@@ -66,20 +66,6 @@ awq_status_t check_quant_args(awq_dtype_t dt, int64_t N, int64_t K, int bits, in
   return AWQ_OK;
 }
 
-// Candidates per candidate-GEMM launch: as many as keep a launch within
-// kLaunchFlop, in [1, n_alpha] (capped before the conversion to int: a tiny
-// layer's quotient is far beyond the int range).  Measured on the layer
-// shapes: where one candidate's GEMM is several TFLOP (70B MLP, down_proj),
-// one launch per candidate runs 2-3% faster than one launch for the whole
-// batch (the chip holds a higher clock: 1.70 against 1.64 GHz on the 70B
-// layer); below a TFLOP per candidate, fewer and larger launches are faster.
-// The fake quantisation still covers the whole batch in one launch.
-int gemm_batch_for(int64_t T, int64_t N, int64_t K, int n_alpha) {
-  const double cand_flop = 2.0 * (double)T * (double)N * (double)K;
-  const double fit = std::floor(kLaunchFlop / cand_flop);
-  return (int)std::max(1.0, std::min((double)n_alpha, fit));
-}
-
 // ---------------------------------------------------------------------------
 // Workspace layout of the search.
 // ---------------------------------------------------------------------------
@@ -90,8 +76,13 @@ awq_status_t compute_layout(awq_dtype_t dt, int64_t N, int64_t K, int64_t T, int
   std::memset(L, 0, sizeof(*L));
   L->tile_m = gt.tile_m;
   L->tile_n = gt.tile_n;
-  L->tiles_m = (int32_t)((T + gt.tile_m - 1) / gt.tile_m);
-  L->tiles_n = (int32_t)((N + gt.tile_n - 1) / gt.tile_n);
+  // the flattened GEMM grid (tiles of every candidate of a batch) is an int
+  const int64_t tm = (T + gt.tile_m - 1) / gt.tile_m, tn = (N + gt.tile_n - 1) / gt.tile_n;
+  if (tm > INT32_MAX / 2 || tn > INT32_MAX / 2 || tm * tn > INT32_MAX / 2)
+    return fail(AWQ_ERR_UNSUPPORTED, "%lld x %lld output tiles of one candidate exceed the GEMM's "
+                "range", (long long)tm, (long long)tn);
+  L->tiles_m = (int32_t)tm;
+  L->tiles_n = (int32_t)tn;
   size_t off = 0;
   L->s_table_offset = off;   // s [n_alpha][K], then RN(1/s) [n_alpha][K]
   off = align_up(off + 2 * (size_t)n_alpha * (size_t)K * 4);
@@ -365,19 +356,30 @@ awq_status_t awq_search_scales(const void* W, const void* X, awq_dtype_t dtype, 
     if (e != hipSuccess) return hip_fail(e, "reference GEMM launch");
   }
   // steps 3-4 over the grid: alpha_batch candidates fake-quantised per pass (W
-  // read once per pass), their GEMMs in launches of at most kLaunchFlop
-  const int gemm_batch = gemm_batch_for(T, N, K, n_alpha);
-  const size_t cand_bytes = (size_t)(tiled ? awq::padded_rows(N) : N) * (size_t)K * esize(dtype);
+  // read once per pass); the pass's GEMM tiles (fp16/bf16) in launches of
+  // kLaunchRounds full rounds of the persistent grid, the last launch taking
+  // the rest.  Measured on the layer shapes: launches of a few rounds run 1-5%
+  // faster than one launch per pass or per candidate, and a launch that ends
+  // on a partly filled round leaves CUs idle, which is why the split is by
+  // rounds and not by candidates.
+  const int64_t cand_tiles = (int64_t)L.tiles_m * L.tiles_n;
+  const int64_t chunk = (int64_t)kLaunchRounds * awq::gemm_grid();
+  const awq::Epi epi = delta ? awq::Epi::kSseDelta : awq::Epi::kSseRef;
   for (int a0 = 0; a0 < n_alpha; a0 += L.alpha_batch) {
     const int nb = std::min(L.alpha_batch, n_alpha - a0);
     e = awq::launch_fake_quant(W, dtype, N, K, s_table + (size_t)a0 * K, rs_table + (size_t)a0 * K,
                                nb, bits, group, delta, tiled, w_hat, stream);
     if (e != hipSuccess) return hip_fail(e, "fake_quant launch");
-    for (int c0 = 0; c0 < nb; c0 += gemm_batch) {
-      const int nc = std::min(gemm_batch, nb - c0);
-      e = awq::launch_gemm(delta ? awq::Epi::kSseDelta : awq::Epi::kSseRef, dtype, gemm_x,
-                           static_cast<char*>(w_hat) + (size_t)c0 * cand_bytes, tiled, nc, T, N, K,
-                           y_ref, partials, a0 + c0, stream);
+    if (!tiled) {
+      e = awq::launch_gemm(epi, dtype, gemm_x, w_hat, false, nb, T, N, K, y_ref, partials, a0,
+                           stream);
+      if (e != hipSuccess) return hip_fail(e, "candidate GEMM launch");
+      continue;
+    }
+    const int64_t total = nb * cand_tiles;
+    for (int64_t t0 = 0; t0 < total; t0 += chunk) {
+      e = awq::launch_gemm(epi, dtype, gemm_x, w_hat, true, nb, T, N, K, y_ref, partials, a0,
+                           stream, (int)t0, (int)std::min(chunk, total - t0));
       if (e != hipSuccess) return hip_fail(e, "candidate GEMM launch");
     }
   }

@@ -169,6 +169,10 @@ struct GemmTiles {
   int tile_m, tile_n;
 };
 GemmTiles gemm_tiles(awq_dtype_t dt);
+// Workgroups of a persistent fp16/bf16 GEMM launch on the current device (its
+// compute units rounded down to a multiple of 8); a launch of more tiles
+// runs them in rounds of this many.
+int gemm_grid();
 // C[t, n] = sum_k X[t, k] * B_b[n, k] over nb weight matrices.
 //   fp16/bf16: X is tiled (padded_rows(T) rows); B is tiled with nb matrices of
 //   padded_rows(N) rows each (b_tiled = true) or row-major [N, K] (b_tiled =
@@ -176,9 +180,14 @@ GemmTiles gemm_tiles(awq_dtype_t dt);
 //   kStore:    Y[t, n] = C (nb must be 1)
 //   kSseRef:   partials[(a0 + b)][tm][tn] = sum over the tile of (Y - C)^2
 //   kSseDelta: partials[(a0 + b)][tm][tn] = sum over the tile of C^2
+// An fp16/bf16 launch may run part of the batch: logical tiles [tile0,
+// tile0 + ntiles) of its nb * tiles_m * tiles_n, numbered candidate by
+// candidate and, within a candidate, in the raster order of groups of 8 token
+// tiles (ntiles < 0: every tile from tile0 on).  fp32 launches run the whole
+// batch.
 hipError_t launch_gemm(Epi epi, awq_dtype_t dt, const void* X, const void* B, bool b_tiled,
                        int nb, int64_t T, int64_t N, int64_t K, float* Y, double* partials,
-                       int a0, hipStream_t st);
+                       int a0, hipStream_t st, int tile0 = 0, int ntiles = -1);
 // INT8 GEMM on tiled operands (Xq [padded T][K], Wq [padded N][K] int8, K a
 // multiple of 64, in the tiled layout of the 2-byte case with byte pairs as
 // elements): kStore writes Y = fp32(fp32(fp32(acc) sx[t]) sw[n]); kSseRef

@@ -177,7 +177,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 void gemm_mfma_kernel(const S* __restrict__ Xt, const S* __restrict__ B, int nb, int T, int N,
                          int K, float* __restrict__ Y, double* __restrict__ partials, int a0,
                          int tiles_m, int tiles_n, const float* __restrict__ rs,
-                         const float* __restrict__ cs) {
+                         const float* __restrict__ cs, int tile0, int ntiles) {
   __shared__ __attribute__((aligned(1024))) char smem[kStages * kStageBytes];
   __shared__ double red[kWaves];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -185,18 +185,19 @@ void gemm_mfma_kernel(const S* __restrict__ Xt, const S* __restrict__ B, int nb,
   const int grp = __builtin_amdgcn_readfirstlane(wave >> 2);
   const uint32_t gw = (uint32_t)__builtin_amdgcn_readfirstlane(wave & 3);
   const int nk = K / BK;                        // K is a multiple of 32
-  // Tiles of this workgroup: first + r * G for r < n_rounds.  G is a multiple
+  // The launch runs logical tiles [tile0, tile0 + ntiles) of the batch; this
+  // workgroup takes tile0 + first + r * G for r < n_rounds.  G is a multiple
   // of 8; when nk < kStages the host launches one workgroup per tile, so the
   // look-ahead never has to reach past the next tile.
   const int G = gridDim.x;
   const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8, per_xcd = G / 8;
-  const int total = tiles_m * tiles_n * nb;
+  const int total = ntiles;
   const int first = xcd * per_xcd + slot;
   const int n_rounds = first < total ? (total - first + G - 1) / G : 0;
   if (n_rounds == 0) return;
   const int nq = n_rounds * nk;                 // stages over all tiles
   auto tile_of = [&](int r) {
-    TileId t = raster(r * G + first, tiles_m, tiles_n);
+    TileId t = raster(tile0 + r * G + first, tiles_m, tiles_n);
     t.b = __builtin_amdgcn_readfirstlane(t.b);
     t.tm = __builtin_amdgcn_readfirstlane(t.tm);
     t.tn = __builtin_amdgcn_readfirstlane(t.tn);
@@ -558,13 +559,19 @@ int persistent_workgroups() {
   return cached[dev];
 }
 
+// The launch runs logical tiles [tile0, tile0 + ntiles) of the batch's
+// nb * tiles_m * tiles_n (ntiles < 0: all from tile0 on).
 template <typename S, Epi kEpi, bool B_TILED>
 hipError_t launch_mfma(const void* X, const void* B, int nb, int64_t T, int64_t N, int64_t K,
                        float* Y, double* partials, int a0, hipStream_t st,
-                       const float* rs = nullptr, const float* cs = nullptr) {
+                       const float* rs = nullptr, const float* cs = nullptr, int tile0 = 0,
+                       int ntiles = -1) {
   const int tiles_m = (int)((T + BM - 1) / BM);
   const int tiles_n = (int)((N + BN - 1) / BN);
-  const int total = tiles_m * tiles_n * nb;
+  const int all = tiles_m * tiles_n * nb;
+  if (tile0 < 0 || tile0 > all) return hipErrorInvalidValue;
+  const int total = ntiles < 0 ? all - tile0 : ntiles;
+  if (total < 1 || total > all - tile0) return hipErrorInvalidValue;
   // One workgroup per CU (a multiple of 8, one share per XCD), or one per tile
   // when there are fewer tiles or the ring is deeper than a tile.
   const int64_t per_tile = (total + 7) / 8 * 8;
@@ -575,20 +582,25 @@ hipError_t launch_mfma(const void* X, const void* B, int nb, int64_t T, int64_t 
   }
   gemm_mfma_kernel<S, kEpi, B_TILED><<<grid, kThreads, 0, st>>>(
       static_cast<const S*>(X), static_cast<const S*>(B), nb, (int)T, (int)N, (int)K, Y, partials,
-      a0, tiles_m, tiles_n, rs, cs);
+      a0, tiles_m, tiles_n, rs, cs, tile0, total);
   return hipGetLastError();
 }
 
 template <typename S>
 hipError_t dispatch_epi(Epi epi, const void* X, const void* B, bool b_tiled, int nb, int64_t T,
-                        int64_t N, int64_t K, float* Y, double* partials, int a0, hipStream_t st) {
+                        int64_t N, int64_t K, float* Y, double* partials, int a0, hipStream_t st,
+                        int tile0, int ntiles) {
   if (!b_tiled) {
     if (epi != Epi::kStore) return hipErrorInvalidValue;
     return launch_mfma<S, Epi::kStore, false>(X, B, nb, T, N, K, Y, partials, a0, st);
   }
   switch (epi) {
-    case Epi::kSseRef: return launch_mfma<S, Epi::kSseRef, true>(X, B, nb, T, N, K, Y, partials, a0, st);
-    case Epi::kSseDelta: return launch_mfma<S, Epi::kSseDelta, true>(X, B, nb, T, N, K, Y, partials, a0, st);
+    case Epi::kSseRef:
+      return launch_mfma<S, Epi::kSseRef, true>(X, B, nb, T, N, K, Y, partials, a0, st, nullptr,
+                                                nullptr, tile0, ntiles);
+    case Epi::kSseDelta:
+      return launch_mfma<S, Epi::kSseDelta, true>(X, B, nb, T, N, K, Y, partials, a0, st, nullptr,
+                                                  nullptr, tile0, ntiles);
     default: return hipErrorInvalidValue;
   }
 }
@@ -603,6 +615,8 @@ hipError_t tile_rows(const void* src, int64_t R, int64_t K, void* dst, hipStream
 
 }  // namespace
 
+int gemm_grid() { return persistent_workgroups(); }
+
 GemmTiles gemm_tiles(awq_dtype_t dt) {
   if (dt == AWQ_F32) return GemmTiles{FT, FT};
   return GemmTiles{BM, BN};
@@ -610,9 +624,10 @@ GemmTiles gemm_tiles(awq_dtype_t dt) {
 
 hipError_t launch_gemm(Epi epi, awq_dtype_t dt, const void* X, const void* B, bool b_tiled,
                        int nb, int64_t T, int64_t N, int64_t K, float* Y, double* partials,
-                       int a0, hipStream_t st) {
+                       int a0, hipStream_t st, int tile0, int ntiles) {
   ProfScope p(epi == Epi::kStore ? "awq_gemm_ref_output" : "awq_gemm_sse", st);
   if (dt == AWQ_F32) {
+    if (tile0 != 0 || ntiles >= 0) return hipErrorInvalidValue;   // whole batch only
     const int tiles_m = (int)((T + FT - 1) / FT);
     const int tiles_n = (int)((N + FT - 1) / FT);
     gemm_f32_kernel<<<tiles_m * tiles_n * nb, 256, 0, st>>>(
@@ -621,8 +636,10 @@ hipError_t launch_gemm(Epi epi, awq_dtype_t dt, const void* X, const void* B, bo
     return hipGetLastError();
   }
   if (dt == AWQ_F16)
-    return dispatch_epi<_Float16>(epi, X, B, b_tiled, nb, T, N, K, Y, partials, a0, st);
-  return dispatch_epi<__bf16>(epi, X, B, b_tiled, nb, T, N, K, Y, partials, a0, st);
+    return dispatch_epi<_Float16>(epi, X, B, b_tiled, nb, T, N, K, Y, partials, a0, st, tile0,
+                                  ntiles);
+  return dispatch_epi<__bf16>(epi, X, B, b_tiled, nb, T, N, K, Y, partials, a0, st, tile0,
+                              ntiles);
 }
 
 hipError_t launch_gemm_w8a8(Epi epi, const void* Xq, const void* Wq, int64_t T, int64_t N,

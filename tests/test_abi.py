@@ -150,6 +150,19 @@ def test_search_layout_full_and_batched():
     assert f32["total_bytes"] - f32["w_hat_offset"] == 2 * 100 * 256 * 4
 
 
+def test_search_layout_rejects_too_many_tiles():
+    # 2^17 x 2^17 output tiles of 256 x 256: beyond the GEMM's int tile index
+    with pytest.raises(awq.AwqError, match="output tiles"):
+        awq.awq_search_layout(torch.float16, 1 << 25, 32, 1 << 25, 1, 0, 0)
+    with pytest.raises(awq.AwqError, match="output tiles"):
+        awq.awq_search_layout(torch.float16, 1, 32, 1 << 50, 1, 0, 0)
+    with pytest.raises(awq.AwqError, match="output tiles"):
+        awq.awq_search_layout(torch.float16, 1 << 23, 32, 1 << 23, 1, 0, 0)   # 2^30 tiles
+    # 2^14 x 2^15 tiles fit: a batch holds one candidate
+    lay = awq.awq_search_layout(torch.float16, 1 << 23, 32, 1 << 22, 20, 0, 0)
+    assert (lay["tiles_m"], lay["tiles_n"], lay["alpha_batch"]) == (1 << 14, 1 << 15, 1)
+
+
 def test_search_workspace_size_covers_every_dtype():
     for N, K, T, n in ((4096, 4096, 4096, 20), (28672, 8192, 16384, 20), (300, 256, 77, 3),
                        (1, 32, 1, 1)):

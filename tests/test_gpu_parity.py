@@ -402,6 +402,59 @@ def test_search_multi_round(dtype, bits, group, N, K, T, n_alpha, flags):
         np.testing.assert_allclose(Y, Yr, rtol=0, atol=2e-6 * np.abs(Yr).max() + 1e-30)
 
 
+# The candidate GEMMs of a pass run in launches of 4 rounds of the persistent
+# grid (4 x 256 tiles on 256 CUs); these layers take several launches whose
+# boundaries fall inside a candidate and inside a group of 8 token tiles, with
+# a ragged last token tile and a short last launch.  Every partial sum of every
+# alpha is checked, so a tile skipped or run twice at a boundary fails.
+SPLIT_LAUNCH_CASES = [
+    # dtype, bits, group, N, K, T
+    ("fp16", 4, 128, 2560, 128, 2600),   # 110 tiles a candidate, 2200 in all
+    ("bf16", 3, 64, 1500, 256, 3000),    # 72 tiles a candidate, 1440 in all
+]
+
+
+@pytest.mark.parametrize("dtype,bits,group,N,K,T", SPLIT_LAUNCH_CASES)
+def test_search_split_launches(dtype, bits, group, N, K, T):
+    log_case(test="search_split_launches", dtype=dtype, bits=bits, group=group, N=N, K=K, T=T)
+    W, X = random_layer(5 * N + K + T, N, K, T, dtype=dtype, outlier_factor=30.0)
+    Wn, Xn = to_numpy(W), to_numpy(X)
+    alphas = oracle.alpha_grid(20)
+    ref = oracle.search(Wn, Xn, bits, group, alphas)
+    Wd, Xd = W.cuda(), X.cuda()
+    a = awq.awq_act_stats(Xd)
+    lay = awq.awq_search_scales(Wd, Xd, a, bits, group, alphas)["layout"]
+    tm_n, tn_n = lay["tiles_m"], lay["tiles_n"]
+    # a workspace of stale non-zero bytes: every partial must be written
+    ws = torch.full((lay["total_bytes"],), 0x7F, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    awq.awq_profile_reset()
+    awq.awq_profile_select("awq_gemm_sse")
+    awq.awq_profile_enable(True)
+    res = awq.awq_search_scales(Wd, Xd, a, bits, group, alphas, workspace=ws)
+    torch.cuda.synchronize()
+    awq.awq_profile_enable(False)
+    n_launch, _ = awq.awq_profile_read("awq_gemm_sse")
+    awq.awq_profile_reset()
+    awq.awq_profile_select("")
+    grid = torch.cuda.get_device_properties(0).multi_processor_count // 8 * 8
+    total = 20 * tm_n * tn_n
+    assert n_launch == -(-total // (4 * grid)) and n_launch > 1, (n_launch, total, grid)
+    losses = res["losses"].cpu().numpy()
+    best = int(res["best_idx"].cpu()[0])
+    check_losses(losses, ref["losses"], best, ref["best"])
+    p0 = lay["partials_offset"]
+    parts = ws[p0:p0 + total * 8].view(torch.float64).view(20, tm_n, tn_n).cpu().numpy()
+    np.testing.assert_allclose(parts.reshape(20, -1).sum(1) / (T * N), losses, rtol=1e-12)
+    X64 = Xn.astype(np.float64)
+    for k in range(20):
+        D = Wn.astype(np.float64) - oracle.fake_quant(Wn, ref["s_table"][k], bits, group).astype(np.float64)
+        E = X64 @ D.T
+        sse = np.add.reduceat(np.add.reduceat(E * E, np.arange(0, T, 256), axis=0),
+                              np.arange(0, N, 256), axis=1)
+        np.testing.assert_allclose(parts[k], sse, rtol=1e-3, atol=0, err_msg=f"alpha index {k}")
+
+
 def test_search_batched_workspace_is_identical():
     log_case(test="search_batched")
     W, X = random_layer(5, 200, 512, 300, dtype="fp16", outlier_factor=20.0)
