@@ -304,9 +304,11 @@ awq_status_t awq_salient_keep_loss(const void* W, const void* X, awq_dtype_t dty
  *   fp32 activations, or 1 to 4 rows, take a vector kernel (the packed weights read once per 8
  *   rows); from 5 fp16 / bf16 rows a matrix-core kernel unpacks every code once per tile of up
  *   to 96 rows; beyond 1024 rows, or from 65 rows once ceil(N/128) * ceil(M/256) >= 200,
- *   awq_lowbit_gemm's kernel runs (no workspace used).  All three sum exact products in fp32
- *   with one product by delta per group, so one error bound covers them, but their summation
- *   orders differ.  The workspace size is that of the kernel the dtype and sizes select.
+ *   awq_lowbit_gemm's kernels run (no workspace used).  All of them sum exact products in
+ *   fp32; the vector and small-M kernels multiply each group's sum by its delta once, within
+ *   (K + 2) 2^-24 sum_k |x_k w'_k| of the exact y, and awq_lowbit_gemm's kernels stay within
+ *   (K + 2 K/group + 2) 2^-24 sum_k |x_k w'_k|; their summation orders differ.  The workspace
+ *   size is that of the kernel the dtype and sizes select.
  * ------------------------------------------------------------------------ */
 awq_status_t awq_lowbit_repack(const uint32_t* codes, const float* scales, const uint8_t* zeros,
                                int64_t N, int64_t K, int bits, int group,
@@ -336,14 +338,22 @@ awq_status_t awq_lowbit_gemv_noalloc(const void* X, awq_dtype_t x_dtype, int64_t
                                      int bits, int group, float* Y, hipStream_t stream);
 /* awq_lowbit_gemm: the same layer for many activation rows (prefill, M from
  *   a few tens up): the same Y, the same repacked operands, the same exact
- *   products x (c - z) with fp32 sums and one product by delta per group and
- *   output, so the same error bound as awq_lowbit_gemv, which itself calls
- *   this kernel for large fp16 / bf16 inputs; below that awq_lowbit_gemv's
- *   kernels are the faster ones.  Runs on the matrix
- *   cores: each workgroup dequantises a 128-row tile of the packed weights
- *   into on-chip memory once and uses it for 256 activation rows.  x_dtype
- *   AWQ_F16 or AWQ_BF16 only (AWQ_ERR_UNSUPPORTED otherwise); Xs 16-byte
- *   aligned; M <= 8388480, K <= 4194304; no workspace.  Results are reproducible. */
+ *   products x (c - z) summed in fp32 on the matrix cores; awq_lowbit_gemv
+ *   itself calls it for large fp16 / bf16 inputs, below that its own kernels
+ *   are the faster ones.  Each workgroup dequantises a tile of the packed
+ *   weights into on-chip memory once and uses it for 256 activation rows; the
+ *   dequantised weights never reach device memory.  Two kernels, chosen by
+ *   the number of tiles: 256 x 128 output tiles whose group sums are scaled
+ *   by delta once per group and output (within (K + 2) 2^-24 sum |x w'| of
+ *   the exact y), and, when the layer needs at least about 1.5 times fewer
+ *   rounds of the chip's compute units that way, 256 x 256 tiles whose
+ *   running sums are kept in units of the current group's delta and rescaled
+ *   by the quotient of consecutive non-zero deltas at each group start (within
+ *   (K + 2 K/group + 2) 2^-24 sum |x w'|; deltas must be finite, and those of
+ *   one output row within a factor 2^100 of each other, or the scaled sums
+ *   may overflow).  x_dtype AWQ_F16 or AWQ_BF16 only (AWQ_ERR_UNSUPPORTED
+ *   otherwise); Xs 16-byte aligned; M <= 8388480, K <= 4194304; no workspace.
+ *   Results are reproducible. */
 awq_status_t awq_lowbit_gemm(const void* X, awq_dtype_t x_dtype, int64_t M, int64_t K,
                              const uint32_t* codes_t, const void* meta_t, int64_t N, int bits,
                              int group, float* Y, hipStream_t stream);

@@ -770,6 +770,397 @@ __global__ __launch_bounds__(kGThreads, 1) void lowbit_gemm_kernel(
     }
 }
 
+// Code T of 8 consecutive ones (bits [T BITS, T BITS + BITS) of hi:lo) as
+// the fp32 value c - z without integer conversions: the code is masked in
+// place inside a window dword that starts at a code boundary and holds it
+// below bit 23 - BITS, OR-ed under the exponent of 2^(23 - sh), so the float
+// reads 2^(23 - sh) + c exactly; sub[sh / BITS] = 2^(23 - sh) + z.
+template <int BITS>
+struct QuarterWindows {
+  static constexpr int kPer = (23 - BITS) / BITS + 1;   // codes per window
+};
+template <int BITS, int T>
+__device__ __forceinline__ float quarter_cz(uint32_t lo, uint32_t hi, const float* sub) {
+  constexpr int kPer = QuarterWindows<BITS>::kPer;
+  constexpr int w0 = (T / kPer) * kPer * BITS;          // first bit of T's window
+  constexpr int sh = T * BITS - w0;
+  uint32_t win;
+  if constexpr (w0 == 0) win = lo;
+  else if constexpr (w0 >= 32) win = hi >> (w0 - 32);
+  else win = __builtin_amdgcn_alignbit(hi, lo, w0);
+  constexpr uint32_t mask = ((1u << BITS) - 1u) << sh;
+  constexpr uint32_t expo = (uint32_t)(150 - sh) << 23;
+  return __uint_as_float((win & mask) | expo) - sub[sh / BITS];
+}
+
+// Pair P of a quarter as two bf16 (c - z), exact: the upper halves of the
+// exact fp32 values.
+template <int BITS, int P>
+__device__ __forceinline__ uint32_t quarter_pair_bf16(uint32_t lo, uint32_t hi, const float* sub) {
+  const float f0 = quarter_cz<BITS, 2 * P>(lo, hi, sub), f1 = quarter_cz<BITS, 2 * P + 1>(lo, hi, sub);
+  return __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+}
+
+// ---- prefill-sized GEMM, 256 x 256 tiles with running sums in step units ----------
+// The same Y [M, N] = Xs W'^T, now with one accumulator set per wave, which
+// lets each wave own 128 x 64 outputs (8 x 4 v_mfma_f32_16x16x32 blocks) and a
+// workgroup of 8 waves a 256 x 256 tile: half the operand traffic through LDS
+// per multiply-add of the 256 x 128 kernel above, whose two sets (the group's
+// sums and the totals) limit a wave to 64 x 64.
+//
+// Arithmetic.  The MFMA still sums exact products x (c - z) in fp32; the
+// running sum of an output row n is kept in units of U, the step of the
+// current group (or, while a group's step is zero, of the last non-zero step
+// before it; 1 before any).  When group g begins, the sum is multiplied by
+// U_{g-1} / U_g (correctly rounded quotient); a group whose step is zero is
+// unpacked as zeros and leaves U as it is; at the end y = sum * U.  Each
+// product x (c - z) thus reaches y through at most K fp32 additions, two
+// roundings per later group start and the final product:
+// |y - y_exact| <= (K + 2 K / G + 2) 2^-24 sum |x w'| (first order).  Steps
+// must be finite; where the steps of one row differ by more than a factor of
+// 2^100 the scaled sums may leave the fp32 range.
+//
+// Schedule (ping-pong as in the search GEMM): group 0 (waves 0-3, tile rows
+// 0-127) and group 1 (rows 128-255) hold one wave on each SIMD.  Each stage of
+// 32 k has two halves separated by a barrier.  In its multiplying half a group
+// issues its 32 MFMAs of stage k with the unpacking of stage k + 2 between
+// them; in its working half it reads the fragments of the stage it multiplies
+// next and that stage's codes (stage + 2), and rescales its sums if that stage
+// starts a group.  Transfers (buffer_load_dwordx4 ... lds, 1 KB each) go in
+// issue units, one per wave and stage: two of the activation tile (16 KB a
+// stage, each lane fetching the chunk that the swizzle puts at its LDS
+// position) four stages ahead into a ring of four, and the stage's packed
+// codes (256 rows x bits words, contiguous in the repacked layout) and
+// (delta, z) pairs of its group (2 KB) five stages ahead into rings of four:
+// item i of those bits + 2 kilobytes goes to waves i and i - 8.  A unit's
+// activations overwrite the slot of the stage group 1 has just read, so group
+// 0 issues in its working half and group 1 at the start of its multiplying
+// half, both after the barrier that ends group 1's reads.  Before the barrier
+// that precedes a working half each wave lets only its last issue unit stay
+// in flight, before the other barrier its last two.  Thread t unpacks codes
+// [16 (t / 256), +16) of weight row t % 256 into a ring of three B tiles;
+// group 0's threads also write the row's unit and, at a group start, the
+// factor U_{g-1} / U_g next to the tile.  Rows of 64 bytes; 16-byte chunk c
+// of row r at c ^ ((r >> 1) & 3).
+constexpr int kTM = 256, kTN = 256;             // activation rows, output rows per tile
+constexpr int kTWaves = 8;
+constexpr int kTThreads = 64 * kTWaves;
+constexpr int kTXRing = 4, kTXAhead = 4;        // activation slots, stages ahead
+constexpr int kTCRing = 4, kTCAhead = 5;        // code and (delta, z) slots, stages ahead
+constexpr int kTBRing = 3;                      // unpacked weight and unit slots
+constexpr int kTMI = 8, kTNI = 4;               // 16 x 16 blocks of a wave: 128 x 64
+
+template <int BITS>
+struct TileLds {
+  static constexpr int kCodeSlot = BITS * 1024;            // 256 rows x BITS words
+  static constexpr int kAux = BITS + 2;                    // kilobytes of codes and pairs a stage
+  static constexpr int kX = 0;
+  static constexpr int kB = kX + kTXRing * kTM * 64;
+  static constexpr int kC = kB + kTBRing * kTN * 64;
+  static constexpr int kMeta = kC + kTCRing * kCodeSlot;   // 256 (delta, z) pairs per slot
+  static constexpr int kUnit = kMeta + kTCRing * 2048;     // per slot: factor [256], unit [256]
+  static constexpr int kBytes = kUnit + kTBRing * 2048;
+  static_assert(kBytes <= 160 * 1024, "LDS of one CU");
+  static_assert(kAux <= 2 * kTWaves, "at most two aux transfers per wave");
+};
+
+template <typename S>
+__device__ __forceinline__ f32x4 mfma16x32(i32x4 a, i32x4 b, f32x4 c);
+template <>
+__device__ __forceinline__ f32x4 mfma16x32<_Float16>(i32x4 a, i32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a),
+                                                __builtin_bit_cast(half8, b), c, 0, 0, 0);
+}
+template <>
+__device__ __forceinline__ f32x4 mfma16x32<__bf16>(i32x4 a, i32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Wait until at most the last U issue units of this wave (2 + n_aux
+// transfers each) are in flight.
+template <int U>
+__device__ __forceinline__ void unit_wait(int n_aux) {
+  if (n_aux == 0) vm_wait<2 * U>();
+  else if (n_aux == 1) vm_wait<3 * U>();
+  else vm_wait<4 * U>();
+}
+
+template <int U = 2>
+__device__ __forceinline__ void tile_barrier(int n_aux) {
+  unit_wait<U>(n_aux);
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <typename S, int BITS>
+__global__ __launch_bounds__(kTThreads, 1) void lowbit_tile_kernel(
+    const S* __restrict__ X, int64_t M, int64_t K, const uint32_t* __restrict__ codes_t,
+    const float2* __restrict__ meta_t, int64_t N, int lg_cpg, float* __restrict__ Y) {
+  using L = TileLds<BITS>;
+  __shared__ __attribute__((aligned(1024))) char lds[L::kBytes];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2, w4 = wave & 3;
+  const int64_t m0 = (int64_t)blockIdx.y * kTM, n0 = (int64_t)blockIdx.x * kTN;
+  const int chunks = (int)(K / 32), cmask = (1 << lg_cpg) - 1;
+  const int64_t rows = M - m0 < kTM ? M - m0 : kTM;
+  const i32x4 rx = byte_range(X + m0 * K, (uint32_t)(rows * K * (int64_t)sizeof(S)));
+  const uint32_t base = (uint32_t)(uintptr_t)lds;
+  const uint32_t lane16 = (uint32_t)lane * 16;
+
+  // activation transfers: this lane's row and chunk in the wave's two 16-row
+  // slabs, as running offsets of the next stage to be issued
+  uint32_t xoff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = 16 * (2 * wave + i) + (lane >> 2);
+    const int c = (lane & 3) ^ ((row >> 1) & 3);
+    xoff[i] = (uint32_t)(((int64_t)row * K + 8 * c) * (int64_t)sizeof(S));
+  }
+  // aux transfers: item wave and item wave + 8 of the stage's BITS code
+  // kilobytes and two pair kilobytes.  Item i < BITS: source codes of chunk j
+  // at (j N + n0) BITS words + i KB; else pairs of group j >> lg_cpg at
+  // (g N + n0) pairs + (i - BITS) KB.  32-bit wrap-around of a source offset
+  // can only touch stages past the end, which are never used.
+  const int n_aux = __builtin_amdgcn_readfirstlane((wave < L::kAux) + (wave + 8 < L::kAux));
+  const i32x4 rc = byte_range(codes_t, (uint32_t)((uint64_t)chunks * N * BITS * 4));
+  const i32x4 rm = byte_range(meta_t, (uint32_t)((uint64_t)(K >> (lg_cpg + 5)) * N * 8));
+  int aux_s = 0, x_s = 0;
+  auto issue_item = [&](int item, int s) __attribute__((always_inline)) {
+    const int slot = s & (kTCRing - 1);
+    if (item < BITS) {
+      const uint32_t src = (uint32_t)(((uint64_t)s * N + n0) * BITS * 4) + item * 1024 + lane16;
+      to_lds16(rc, base + L::kC + slot * L::kCodeSlot + item * 1024, src);
+    } else {
+      const uint32_t g = (uint32_t)(s >> lg_cpg);
+      const uint32_t src = (uint32_t)(((uint64_t)g * N + n0) * 8) + (item - BITS) * 1024 + lane16;
+      to_lds16(rm, base + L::kMeta + slot * 2048 + (item - BITS) * 1024, src);
+    }
+  };
+  auto issue_aux = [&]() __attribute__((always_inline)) {
+    if (n_aux > 0) issue_item(wave, aux_s);
+    if (n_aux > 1) issue_item(wave + 8, aux_s);
+    ++aux_s;
+  };
+  auto issue_x = [&]() __attribute__((always_inline)) {
+    const int slot = x_s & (kTXRing - 1);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      to_lds16(rx, base + L::kX + slot * (kTM * 64) + (2 * wave + i) * 1024, xoff[i]);
+      xoff[i] += 32 * (uint32_t)sizeof(S);
+    }
+    ++x_s;
+  };
+
+  // Unpacking: thread -> weight row lr, quarters 2 grp and 2 grp + 1 (codes
+  // [8 q, 8 q + 8) of the chunk, bits [8 q BITS, 8 q BITS + 8 BITS) of the
+  // row's words).
+  const int lr = tid & (kTN - 1);
+  float unit = 1.0f;                           // group 0's threads: the row's unit
+  struct Quarter {
+    uint32_t w0, w1, w2;
+  };
+  struct Codes {
+    Quarter q[2];
+    float2 dz;
+  };
+  auto dq_load = [&](int s) __attribute__((always_inline)) {
+    const int slot = s & (kTCRing - 1);
+    const uint32_t* cw =
+        reinterpret_cast<const uint32_t*>(lds + L::kC + slot * L::kCodeSlot) + lr * BITS;
+    Codes c;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int qbit = 8 * (2 * grp + h) * BITS, qw = qbit >> 5;
+      const int qw1 = qw + 1 < BITS ? qw + 1 : BITS - 1, qw2 = qw + 2 < BITS ? qw + 2 : BITS - 1;
+      c.q[h].w0 = cw[qw];
+      c.q[h].w1 = cw[qw1];
+      c.q[h].w2 = BITS == 7 ? cw[qw2] : 0u;
+    }
+    c.dz = reinterpret_cast<const float2*>(lds + L::kMeta + slot * 2048)[lr];
+    return c;
+  };
+  auto dq_store = [&](int s, const Codes& c) __attribute__((always_inline)) {
+    // a zero step unpacks as zeros: codes and zero-point read as 0, so every
+    // c - z is 0
+    const bool live = c.dz.x != 0.0f;
+    const int z = live ? (int)c.dz.y : 0;
+    char* brow = lds + L::kB + (s % kTBRing) * (kTN * 64);
+    float sub[QuarterWindows<BITS>::kPer];
+#pragma unroll
+    for (int t = 0; t < QuarterWindows<BITS>::kPer; ++t) sub[t] = (float)(1 << (23 - BITS * t)) + (float)z;
+    const _Float16 nzh = (_Float16)(-(1024 + z));
+    const half2v negz = {nzh, nzh};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int qbit = 8 * (2 * grp + h) * BITS, qoff = qbit & 31;
+      uint32_t lo, hi;
+      if constexpr (BITS == 2 || BITS == 4) {
+        lo = c.q[h].w0 >> qoff;
+        hi = 0u;
+      } else if constexpr (BITS == 7) {
+        lo = __builtin_amdgcn_alignbit(c.q[h].w1, c.q[h].w0, qoff);
+        hi = __builtin_amdgcn_alignbit(c.q[h].w2, c.q[h].w1, qoff);
+      } else {
+        lo = __builtin_amdgcn_alignbit(c.q[h].w1, c.q[h].w0, qoff);
+        hi = c.q[h].w1 >> qoff;
+      }
+      lo = live ? lo : 0u;
+      hi = live ? hi : 0u;
+      i32x4 v;
+      if constexpr (std::is_same<S, _Float16>::value) {
+        v = i32x4{(int)pair_of<S, BITS, 0>(lo, hi, negz, z), (int)pair_of<S, BITS, 1>(lo, hi, negz, z),
+                  (int)pair_of<S, BITS, 2>(lo, hi, negz, z), (int)pair_of<S, BITS, 3>(lo, hi, negz, z)};
+      } else {
+        v = i32x4{(int)quarter_pair_bf16<BITS, 0>(lo, hi, sub), (int)quarter_pair_bf16<BITS, 1>(lo, hi, sub),
+                  (int)quarter_pair_bf16<BITS, 2>(lo, hi, sub), (int)quarter_pair_bf16<BITS, 3>(lo, hi, sub)};
+      }
+      *reinterpret_cast<i32x4*>(brow + g_off(lr, 2 * grp + h)) = v;
+    }
+    if (grp == 0) {
+      // the row's unit after stage s, and at a group start the factor that
+      // takes the running sums from the previous unit to this one
+      float* u = reinterpret_cast<float*>(lds + L::kUnit + (s % kTBRing) * 2048);
+      if ((s & cmask) == 0) {
+        const float nu = live ? c.dz.x : unit;
+        u[lr] = unit / nu;
+        unit = nu;
+      }
+      u[256 + lr] = unit;
+    }
+  };
+
+  f32x4 acc[kTMI][kTNI];
+#pragma unroll
+  for (int i = 0; i < kTMI; ++i)
+#pragma unroll
+    for (int j = 0; j < kTNI; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // fragments: A rows 128 grp + 16 i + l % 16, B rows 64 w4 + 16 j + l % 16,
+  // chunk l / 16 of the stage (8 consecutive k)
+  const int frow = lane & 15, fch = lane >> 4;
+  const uint32_t a_frag = (uint32_t)g_off(grp * 128 + frow, fch);
+  const uint32_t b_frag = (uint32_t)g_off(w4 * 64 + frow, fch);
+  i32x4 fa[kTMI], fb[kTNI];
+  auto read_frags = [&](int s) __attribute__((always_inline)) {
+    const char* A = lds + L::kX + (s & (kTXRing - 1)) * (kTM * 64);
+    const char* B = lds + L::kB + (s % kTBRing) * (kTN * 64);
+#pragma unroll
+    for (int i = 0; i < kTMI; ++i) fa[i] = *reinterpret_cast<const i32x4*>(A + a_frag + i * 1024);
+#pragma unroll
+    for (int j = 0; j < kTNI; ++j) fb[j] = *reinterpret_cast<const i32x4*>(B + b_frag + j * 1024);
+  };
+  auto mfmas = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kTMI; ++i)
+#pragma unroll
+      for (int j = 0; j < kTNI; ++j) acc[i][j] = mfma16x32<S>(fa[i], fb[j], acc[i][j]);
+  };
+  // at the start of group g > 0: the running sums of output column n times
+  // U_{g-1} / U_g (lane l holds column l % 16 of each 16-wide block)
+  const int ecol = lane & 15;
+  auto rescale = [&](int s) __attribute__((always_inline)) {
+    if (s == 0 || s >= chunks || (s & cmask) != 0) return;
+    const float* u = reinterpret_cast<const float*>(lds + L::kUnit + (s % kTBRing) * 2048);
+#pragma unroll
+    for (int j = 0; j < kTNI; ++j) {
+      const float r = u[w4 * 64 + 16 * j + ecol];
+#pragma unroll
+      for (int i = 0; i < kTMI; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[i][j][e] *= r;
+    }
+  };
+  // A wave's working half for stage f: fragment reads of f and its codes of
+  // stage f + 2, then (group 0) one issue unit, then the rescale before f's
+  // MFMAs.  Its multiplying half of stage s: (group 1) one issue unit, then
+  // its MFMAs, with the unpacking of the codes it read (stage s + 2) between
+  // them.  An issue unit's activations go to the slot of the stage that group
+  // 1 reads in its working half of the same iteration; group 1 issues after
+  // the barrier that ends it, group 0 issues in the half after it.  Work on
+  // stages past the end reads and writes only ring slots that are never used
+  // again.
+  Codes held;
+  auto issue = [&]() __attribute__((always_inline)) {
+    issue_aux();
+    issue_x();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto multiply = [&](int s) __attribute__((always_inline)) {
+    if (grp == 1) issue();
+    mfmas();
+    dq_store(s + 2, held);
+  };
+  auto work = [&](int f) __attribute__((always_inline)) {
+    read_frags(f);
+    held = dq_load(f + 2);
+    if (grp == 0) issue();
+    rescale(f);
+  };
+  // Prologue: issue units {aux 0}, then {aux t + 1, activations t} for
+  // t = 0 .. 2, in the loop's order; unpack stages 0 and 1 once units -1 and 0
+  // have landed; then unit 3, whose codes go to stage 0's slot.
+  issue_aux();
+#pragma unroll
+  for (int t = 0; t < kTXAhead - 1; ++t) {
+    issue_aux();
+    issue_x();
+  }
+  tile_barrier(n_aux);                       // units 1 and 2 may be in flight
+  dq_store(0, dq_load(0));
+  dq_store(1, dq_load(1));
+  __syncthreads();                           // every thread is done with slots 0 and 1
+  issue_aux();
+  issue_x();
+  tile_barrier(n_aux);                       // unit 1 (stage 2's codes) has landed
+  // Each group runs its own copy of the loop (same barriers in the same
+  // order), so that its registers are allocated for its own schedule.
+  auto run = [&](auto group) __attribute__((always_inline)) {
+    constexpr int G = decltype(group)::value;
+    // Before the barrier that precedes a working half (stage f: activations
+    // of issue unit f, codes of unit f + 1) at most one issue unit per wave
+    // may be in flight, before the other barrier two.
+    if constexpr (G == 0) {
+      read_frags(0);
+      held = dq_load(2);
+      for (int k = 0; k < chunks; ++k) {
+        multiply(k);                         // first half: multiply
+        tile_barrier<1>(n_aux);
+        work(k + 1);                         // second half: work
+        tile_barrier<2>(n_aux);
+      }
+    } else {
+      for (int k = 0; k < chunks; ++k) {
+        work(k);                             // first half: work
+        tile_barrier<1>(n_aux);
+        multiply(k);                         // second half: multiply
+        tile_barrier<2>(n_aux);
+      }
+    }
+  };
+  if (grp == 0) run(std::integral_constant<int, 0>());
+  else run(std::integral_constant<int, 1>());
+  vm_wait<0>();                              // no transfer may outlive the workgroup
+  // y = sum * U of the last stage; lane l holds column l % 16 and rows
+  // 4 (l / 16) .. + 3 of each block
+  const float* ul = reinterpret_cast<const float*>(lds + L::kUnit + ((chunks - 1) % kTBRing) * 2048) + 256;
+  const int erow = (lane >> 4) * 4;
+#pragma unroll
+  for (int j = 0; j < kTNI; ++j) {
+    const int nl = w4 * 64 + 16 * j + ecol;
+    const int64_t n = n0 + nl;
+    const float u = ul[nl];
+#pragma unroll
+    for (int i = 0; i < kTMI; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t m = m0 + grp * 128 + 16 * i + erow + e;
+        if (m < M && n < N) Y[m * N + n] = acc[i][j][e] * u;
+      }
+  }
+}
+
 // ---- small-M layer on the matrix cores --------------------------------------------
 // Up to 64 activation rows.  The GEMV's cost is vector work that grows with
 // the rows (one v_dot2 per pair of codes per row); here every code is unpacked
@@ -1036,14 +1427,35 @@ hipError_t small_bits(int bits, const void* X, int64_t M, int64_t K, const uint3
   }
 }
 
+// The large-tile kernels: 256 x 256 tiles (one accumulator set, rescaled at
+// group starts) or 256 x 128 tiles (two sets).  One round of 256x256 tiles over
+// the chip takes about 1.47 times as long as a round of 256x128 tiles (70B
+// MLP layer, K = 8192: 253 against 172 us) for twice the outputs, so the wide
+// tiles are used when they need fewer rounds by more than that factor: from a
+// few hundred tiles on, not where a layer fills the chip only once either way.
+bool use_wide_tiles(int64_t M, int64_t N) {
+  const int64_t g = gemm_grid();
+  const int64_t mt = (M + kTM - 1) / kTM;
+  const int64_t r_wide = ((N + kTN - 1) / kTN * mt + g - 1) / g;
+  const int64_t r_narrow = ((N + kGN - 1) / kGN * mt + g - 1) / g;
+  return 100 * r_narrow > 147 * r_wide;
+}
+
 template <typename S, int BITS>
 hipError_t gemm_launch(const void* X, int64_t M, int64_t K, const uint32_t* codes_t,
                        const float2* meta_t, int64_t N, int group, float* Y, hipStream_t st) {
-  ProfScope p("awq_lowbit_gemm", st);
-  const dim3 grid((unsigned)((N + kGN - 1) / kGN), (unsigned)((M + kGM - 1) / kGM));
   const int lg_cpg = __builtin_ctz((unsigned)(group / 32));   // group is a power of two >= 32
-  lowbit_gemm_kernel<S, BITS><<<grid, kGThreads, 0, st>>>(static_cast<const S*>(X), M, K, codes_t,
-                                                          meta_t, N, lg_cpg, Y);
+  if (use_wide_tiles(M, N)) {
+    ProfScope p("awq_lowbit_gemm_wide", st);
+    const dim3 grid((unsigned)((N + kTN - 1) / kTN), (unsigned)((M + kTM - 1) / kTM));
+    lowbit_tile_kernel<S, BITS><<<grid, kTThreads, 0, st>>>(static_cast<const S*>(X), M, K,
+                                                            codes_t, meta_t, N, lg_cpg, Y);
+  } else {
+    ProfScope p("awq_lowbit_gemm_narrow", st);
+    const dim3 grid((unsigned)((N + kGN - 1) / kGN), (unsigned)((M + kGM - 1) / kGM));
+    lowbit_gemm_kernel<S, BITS><<<grid, kGThreads, 0, st>>>(static_cast<const S*>(X), M, K,
+                                                            codes_t, meta_t, N, lg_cpg, Y);
+  }
   return hipGetLastError();
 }
 

@@ -4,11 +4,15 @@ accumulation bound.
 
 Inputs come from the CPU side only: seeded synthetic layers, scales from the
 oracle's statistic, codes from the oracle's quantize_pack.  The GPU result is
-compared per output with |Y_gpu - Y| <= (K + 2) 2^-24 sum_k |x_k w'_k|: the
-kernel forms y = sum_g delta_g sum_{k in g} x_k (c_k - z_g) with exact
-integer differences and exact products x (c - z), so its error is that of
-fp32 sums with fewer than K + 2 roundings on any path (group sums, one
-product by delta per group, the sums over groups and over k-splits).
+compared per output with |Y_gpu - Y| <= (K + 2 K/G + 2) 2^-24 sum_k |x_k w'_k|.
+The kernels sum exact products x (c - z) of exact integer differences in fp32.
+The vector and small-M kernels form y = sum_g delta_g sum_{k in g} x_k (c_k -
+z_g): fp32 sums with fewer than K + 2 roundings on any path (group sums, one
+product by delta per group, the sums over groups and over k-splits).  The
+large-tile kernel keeps its running sums in units of the current group's
+step and rescales them by the quotient of consecutive steps at each group
+start: two more roundings per later group on a product's path (the
+quotient and the product by it), hence the 2 K/G term.
 """
 
 import numpy as np
@@ -56,7 +60,7 @@ def activations(Xn, s, M, dtype):
 def check(Y, Xs_t, codes, delta, zero, bits, group, rows=None):
     Xs = Xs_t.to(torch.float32).numpy().astype(np.float64)
     K = Xs.shape[1]
-    n = K + 2
+    n = K + 2 * (K // group) + 2
     if rows is not None:
         codes, delta, zero = codes[rows], delta[rows], zero[rows]
         Y = Y[:, rows]
@@ -199,7 +203,50 @@ GEMM_CASES = [
 ]
 
 
-@pytest.mark.parametrize("dtype,bits,group,M,N,K", GEMM_CASES)
+# Layers with enough 256-row activation tiles x 256-row weight tiles that the
+# 256 x 256 kernel runs (on a 256-CU chip: one round of wide tiles against two
+# of 256 x 128 tiles): ragged M and N, fp16 and bf16, 2-8 bits, a group per
+# stage up to 16 stages per group.
+WIDE_CASES = [
+    # dtype, bits, group, M, N, K
+    ("bf16", 3, 128, 5000, 2000, 256),
+    ("fp16", 4, 32, 4200, 2100, 160),      # a rescale at every stage
+    ("bf16", 8, 64, 4096, 2304, 192),      # widest codes: two code transfers for some waves
+    ("fp16", 7, 512, 4000, 2560, 1024),
+    ("bf16", 5, 128, 4608, 2048, 512),
+    ("fp16", 2, 256, 4352, 1940, 768),
+]
+
+
+def expected_gemm_kernel(M, N):
+    """The rule awq_lowbit_gemm picks its kernel by: 256 x 256 tiles when they
+    need fewer rounds of the chip's workgroups than 256 x 128 tiles by more
+    than a factor 1.47."""
+    g = torch.cuda.get_device_properties(0).multi_processor_count // 8 * 8
+    mt = -(-M // 256)
+    r_wide = -(-(-(-N // 256) * mt) // g)
+    r_narrow = -(-(-(-N // 128) * mt) // g)
+    return "wide" if 100 * r_narrow > 147 * r_wide else "narrow"
+
+
+def run_gemm(Xs, codes_t, meta_t, bits, group):
+    """awq_lowbit_gemm, and which of its two kernels ran (from the library's
+    per-launch events)."""
+    awq.awq_profile_reset()
+    awq.awq_profile_select("awq_lowbit_gemm")
+    awq.awq_profile_enable(True)
+    Y = awq.awq_lowbit_gemm(Xs, codes_t, meta_t, bits, group)
+    torch.cuda.synchronize()
+    awq.awq_profile_enable(False)
+    wide = awq.awq_profile_read("awq_lowbit_gemm_wide")[0]
+    narrow = awq.awq_profile_read("awq_lowbit_gemm_narrow")[0]
+    awq.awq_profile_reset()
+    awq.awq_profile_select("")
+    assert wide + narrow == 1
+    return Y, "wide" if wide else "narrow"
+
+
+@pytest.mark.parametrize("dtype,bits,group,M,N,K", GEMM_CASES + WIDE_CASES)
 def test_lowbit_gemm_matches_oracle(dtype, bits, group, M, N, K):
     log_case(test="lowbit_gemm", dtype=dtype, bits=bits, group=group, M=M, N=N, K=K)
     Xn, s, codes, delta, zero = packed_layer(3 * N + K + bits, N, K, max(M, 16), dtype, bits, group)
@@ -207,9 +254,45 @@ def test_lowbit_gemm_matches_oracle(dtype, bits, group, M, N, K):
                                             torch.from_numpy(delta).cuda(),
                                             torch.from_numpy(zero).cuda(), K, bits, group)
     Xs = activations(Xn, s, M, dtype)
-    Y = awq.awq_lowbit_gemm(Xs.cuda(), codes_t, meta_t, bits, group)
-    torch.cuda.synchronize()
+    Y, kernel = run_gemm(Xs.cuda(), codes_t, meta_t, bits, group)
+    assert kernel == expected_gemm_kernel(M, N)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if (dtype, bits, group, M, N, K) in WIDE_CASES and cus == 256:
+        assert kernel == "wide"
     check(Y.cpu().numpy(), Xs, codes, delta, zero, bits, group)
+
+
+@pytest.mark.parametrize("dtype,M,N", [("fp16", 70, 300), ("bf16", 70, 300), ("bf16", 4200, 2100),
+                                       ("fp16", 4200, 2100)])
+def test_lowbit_layer_zero_and_far_apart_steps(dtype, M, N):
+    """Steps that awq_quantize_pack does not produce but the packed format
+    allows: whole groups with step zero (a row's first and last group, runs of
+    them, whole rows) and the steps of one row spread over 2^-40 .. 2^40.  The large-tile
+    kernel rescales its running sums between consecutive non-zero steps; every
+    kernel stays within the bound of the exact product."""
+    K, bits, G = 1024, 4, 64
+    log_case(test="lowbit_zero_far_steps", dtype=dtype, M=M, N=N)
+    Xn, s, codes, delta, zero = packed_layer(31, N, K, M, dtype, bits, G)
+    n_i, g_i = np.meshgrid(np.arange(N), np.arange(K // G), indexing="ij")
+    delta = (delta * np.exp2(((n_i + 7 * g_i) % 81) - 40).astype(F32)).astype(F32)
+    dead = (((n_i + g_i) % 5 == 0) | ((n_i % 11 == 0) & (g_i < 3)) | ((n_i % 13 == 0) & (g_i >= 13))
+            | (n_i % 97 == 5))
+    delta[dead] = 0.0
+    assert dead[:, 0].any() and dead[:, -1].any() and np.all(dead, axis=1).any()
+    codes_t, meta_t = awq.awq_lowbit_repack(torch.from_numpy(codes.view(np.int32)).cuda(),
+                                            torch.from_numpy(delta).cuda(),
+                                            torch.from_numpy(zero).cuda(), K, bits, G)
+    Xs = activations(Xn, s, M, dtype)
+    Yt, kernel = run_gemm(Xs.cuda(), codes_t, meta_t, bits, G)
+    assert kernel == expected_gemm_kernel(M, N)
+    check(Yt.cpu().numpy(), Xs, codes, delta, zero, bits, G)
+    assert np.all(Yt.cpu().numpy()[:, np.all(dead, axis=1)] == 0)
+    if M <= 64 * 2:                        # the GEMV layer's small-M and vector kernels too
+        Ys = awq.awq_lowbit_gemv(Xs.cuda(), codes_t, meta_t, bits, G)
+        Yv = awq.awq_lowbit_gemv(Xs[:3].cuda(), codes_t, meta_t, bits, G)
+        torch.cuda.synchronize()
+        check(Ys.cpu().numpy(), Xs, codes, delta, zero, bits, G)
+        check(Yv.cpu().numpy(), Xs[:3], codes, delta, zero, bits, G)
 
 
 def test_lowbit_gemm_is_reproducible_and_matches_the_gemv_layer():
@@ -230,12 +313,12 @@ def test_lowbit_gemm_is_reproducible_and_matches_the_gemv_layer():
     assert torch.equal(Y1, Y2)
     Xa = Xs.cpu().to(torch.float32).numpy().astype(np.float64)
     Wd = oracle.dequantize(codes, delta, zero, bits, G, K).astype(np.float64)
-    tol = 2 * (K + 2) * 2.0 ** -24 * (np.abs(Xa) @ np.abs(Wd).T)
+    tol = 2 * (K + 2 * (K // G) + 2) * 2.0 ** -24 * (np.abs(Xa) @ np.abs(Wd).T)
     assert np.all(np.abs(Y1.cpu().numpy().astype(np.float64) - Yv.cpu().numpy()) <= tol)
 
 
 @pytest.mark.parametrize("name,M", [("llama7b-qproj", 512), ("llama7b-down", 200),
-                                    ("70b-mlp", 256)])
+                                    ("70b-mlp", 256), ("70b-mlp", 1024), ("llama7b-upgate", 1024)])
 def test_lowbit_gemm_full_size(name, M):
     """Full weight shapes with prefill-sized activation blocks, every
     activation row checked on sampled output rows."""
@@ -247,8 +330,8 @@ def test_lowbit_gemm_full_size(name, M):
                                             torch.from_numpy(delta).cuda(),
                                             torch.from_numpy(zero).cuda(), K, bits, G)
     Xs = activations(Xn, s, M, spec.dtype)
-    Y = awq.awq_lowbit_gemm(Xs.cuda(), codes_t, meta_t, bits, G)
-    torch.cuda.synchronize()
+    Y, kernel = run_gemm(Xs.cuda(), codes_t, meta_t, bits, G)
+    assert kernel == expected_gemm_kernel(M, N)
     rows = np.concatenate([np.arange(0, 64), np.arange(N // 2, N // 2 + 64), np.arange(N - 64, N)])
     check(Y.cpu().numpy(), Xs, codes, delta, zero, bits, G, rows=rows)
 
