@@ -3,7 +3,8 @@ the C ABI, against the workspace entry point awq_lowbit_gemv on the same
 inputs: the same kernels with the same k-splits, so the outputs must agree bit
 for bit.  Two calls in a row share the GPU's static scratch array, the second
 with a smaller input, and each is checked; then the sizes that the array
-cannot hold are refused."""
+cannot hold are refused; last, the call is captured in a HIP graph (the
+callers it is for) and replayed."""
 
 import ctypes
 
@@ -97,3 +98,39 @@ def test_noalloc_refuses_sizes_beyond_the_array():
         Y.data_ptr(), awq._stream(X.device))
     assert st == -2
     assert "static scratch" in awq.library().awq_last_error().decode()
+
+
+def test_noalloc_replays_in_a_hip_graph():
+    """The entry point for callers under HIP graph capture: one decode call
+    (the GEMV and the kernel that sums its k-splits) captured in a graph and
+    replayed with new activations copied into the captured input between
+    replays; every replay gives the bits of the same call made eagerly and of
+    awq_lowbit_gemv (the same kernels and k-splits)."""
+    M, N, K, bits, group = 1, 28672, 8192, 3, 128
+    print("case graph", M, N, K, bits, group, flush=True)
+    assert awq.awq_lowbit_gemv_workspace_size(torch.bfloat16, M, N, K) > 0   # two kernels
+    codes_t, meta_t = packed_layer(N, K, bits, group, torch.bfloat16, 21)
+    X = torch.zeros(M, K, dtype=torch.bfloat16, device="cuda")
+    Y = torch.empty(M, N, dtype=torch.float32, device="cuda")
+    # eager first: the static array's address is looked up outside the capture
+    assert noalloc(X, codes_t, meta_t, bits, group, Y) == 0
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=torch.cuda.Stream()):
+        status = noalloc(X, codes_t, meta_t, bits, group, Y)
+    assert status == 0
+    ref = torch.empty_like(Y)
+    for rep in range(4):
+        g = torch.Generator().manual_seed(100 + rep)
+        X.copy_(torch.randn(M, K, generator=g).to(torch.bfloat16))
+        Y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = Y.clone()
+        assert noalloc(X, codes_t, meta_t, bits, group, ref) == 0
+        Yw = awq.awq_lowbit_gemv(X, codes_t, meta_t, bits, group)
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref), rep
+        assert torch.equal(got, Yw), rep
+        assert torch.isfinite(got).all()
