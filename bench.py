@@ -105,10 +105,12 @@ def calibrate_copy() -> None:
 def bench_lowbit(args) -> None:
     """Decode-shaped low-bit layer: packed-weight bytes per second of one whole
     awq_lowbit_gemv call (GEMV and, with several k-splits, the reduction),
-    timed with events around `reps` back-to-back calls; the headline case is
-    the 70B MLP layer (28672 x 8192 bf16, INT3) at one activation row.  The
-    prefill-sized matrix-core form (awq_lowbit_gemm) is timed beside the dense
-    fp16 / bf16 product for 64 to 4096 activation rows."""
+    timed with events around `reps` back-to-back calls, and again with 20
+    calls captured in one HIP graph and replayed (no host launch path between
+    the calls; the dense product likewise); the headline case is the 70B MLP
+    layer (28672 x 8192 bf16, INT3) at one activation row.  The prefill-sized
+    matrix-core form (awq_lowbit_gemm) is timed beside the dense fp16 / bf16
+    product for 64 to 4096 activation rows."""
     import torch
 
     import post_weight_quantization_act_amd as awq
@@ -129,6 +131,31 @@ def bench_lowbit(args) -> None:
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps * 1e3          # us per call
 
+    def graph_timed(fn, calls=20, reps=10):
+        """us per call with `calls` calls captured in one HIP graph and the
+        graph replayed: the GPU's time without the host's launch path (the
+        buffers are allocated beforehand, so the calls allocate nothing)."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            for _ in range(calls):
+                fn()
+        for _ in range(2):
+            graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (reps * calls) * 1e3
+
     cases, prefill = [], []
     for name in args.lowbit_layers.split(","):
         spec = CONFIGS[name]
@@ -143,13 +170,19 @@ def bench_lowbit(args) -> None:
             ws = torch.empty(max(1, awq.awq_lowbit_gemv_workspace_size(dt, M, N, K)),
                              dtype=torch.uint8, device=dev)
             Y = torch.empty(M, N, device=dev)
-            us = timed(lambda: awq.awq_lowbit_gemv(X, codes_t, meta_t, b, G, out=Y, workspace=ws),
-                       args.steps)
-            dense_us = timed(lambda: X @ Wt, args.steps)
+            call = lambda: awq.awq_lowbit_gemv(X, codes_t, meta_t, b, G, out=Y, workspace=ws)
+            us = timed(call, args.steps)
+            Yd = torch.empty(M, N, device=dev, dtype=dt)
+            dense = lambda: torch.matmul(X, Wt, out=Yd)
+            dense_us = timed(dense, args.steps)
+            graph_us, dense_graph_us = graph_timed(call), graph_timed(dense)
             nbytes = N * K * b / 8 + N * (K // G) * 8 + M * K * 2 + M * N * 4
             cases.append({"layer": name, "dtype": spec.dtype, "bits": b, "M": M, "N": N, "K": K,
                           "us": us, "bytes": nbytes, "gbps": nbytes / (us * 1e-6) / 1e9,
-                          "dense_us": dense_us, "speedup_vs_dense": dense_us / us})
+                          "dense_us": dense_us, "speedup_vs_dense": dense_us / us,
+                          "graph_us": graph_us, "graph_gbps": nbytes / (graph_us * 1e-6) / 1e9,
+                          "dense_graph_us": dense_graph_us,
+                          "graph_speedup_vs_dense": dense_graph_us / graph_us})
         for M in (int(v) for v in args.lowbit_m.split(",")):
             X = torch.randn(M, K, device=dev).to(dt)
             Y = torch.empty(M, N, device=dev)
