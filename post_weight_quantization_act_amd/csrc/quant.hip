@@ -153,7 +153,15 @@ __device__ __forceinline__ void store8(S* p, const float (&v)[8]) {
   i32x4 raw;
   S* e = reinterpret_cast<S*>(&raw);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) e[i] = from_f32<S>(v[i]);
+  for (int i = 0; i < 8; ++i) {
+    // The value is rounded to fp32 first and then converted.  The empty asm
+    // keeps the compiler from folding the conversion into the fma that
+    // produced the value: its mixed-precision fma with an fp16 result does not
+    // round as the two steps do (it resolved fp16 ties differently).
+    float x = v[i];
+    asm("" : "+v"(x));
+    e[i] = from_f32<S>(x);
+  }
   *reinterpret_cast<i32x4*>(p) = raw;
 }
 

@@ -523,9 +523,10 @@ def tiled_rows(flat, rows, K):
 def test_search_candidates_exact(dtype, bits, group):
     """The search's own fake-quant launch (tiled output, group width fixed at
     compile time, reciprocals from the scale table): every D = W - W_hat of
-    the batch equals the oracle's bit for bit, and the padding rows are zero."""
+    the batch equals the oracle's bit for bit, and the padding rows are zero.
+    Up to group 256, K = 1280 ends half-way through a 512-column block."""
     log_case(test="search_candidates", dtype=dtype, bits=bits, group=group)
-    N, K, T = 300, 1024, 40
+    N, K, T = 300, (1280 if group <= 256 else 1536), 40
     W, X = random_layer(N + group + bits, N, K, T, dtype=dtype, outlier_factor=30.0)
     Wn = to_numpy(W).astype(F32)
     Wn[1, :group] = np.abs(Wn[1, :group]) + F32(0.001)   # one-signed group
