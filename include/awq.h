@@ -189,12 +189,25 @@ awq_status_t awq_fake_quant(const void* W, awq_dtype_t w_dtype, int64_t N, int64
  * + k % 8 with t = row / 256, r = row % 256, s = k / 32, c = (k % 32) / 8:
  * each 256 x 32 block is one contiguous 16 KB unit, pre-swizzled for the
  * GEMM's LDS fragment reads.
+ *
+ * Fragment layout (the fp16/bf16 reference output at y_ref_offset): whole
+ * 256 x 256 output tiles, Tp x Np floats in all (T and N rounded up to
+ * multiples of 256).  Output (t, n) with tm = t / 256, tn = n / 256, a = t %
+ * 256, b = n % 256 sits at float index
+ * ((((tm * tiles_n + tn) * 8 + w) * 32 + i * 4 + j) * 64 + l) * 4 + r with
+ * w = (a / 128) * 4 + b / 64, i = (a % 128) / 16, j = (b % 64) / 16,
+ * l = ((a % 16) / 4) * 16 + b % 16, r = a % 4: the accumulator order of the
+ * GEMM's waves, so that its squared-error epilogue reads the reference in
+ * contiguous 1 KB pieces.  Entries past T or N hold the product of the zero
+ * padding.
  * ------------------------------------------------------------------------ */
 typedef struct {
   size_t total_bytes;       /* bytes the call uses */
   size_t s_table_offset;    /* fp32 [n_alpha][K] scale table, followed by fp32
                                [n_alpha][K] of its reciprocals RN(1/s) */
-  size_t y_ref_offset;      /* fp32 [T][N]; SIZE_MAX in the WEIGHT_DELTA form */
+  size_t y_ref_offset;      /* fp32 reference output X W^T: fp16/bf16 in the fragment
+                               layout below (Tp x Np floats), fp32 [T][N]; SIZE_MAX in
+                               the WEIGHT_DELTA form */
   size_t x_tiled_offset;    /* fp16/bf16: X in the tiled layout below, Tp = T rounded
                                up to a multiple of 256 rows; SIZE_MAX for fp32 */
   size_t w_hat_offset;      /* alpha_batch consecutive matrices D = W - W_hat (or

@@ -91,8 +91,11 @@ awq_status_t compute_layout(awq_dtype_t dt, int64_t N, int64_t K, int64_t T, int
   if (delta) {
     L->y_ref_offset = SIZE_MAX;
   } else {
+    // fp16/bf16: whole 256 x 256 tiles in the GEMM's fragment layout
+    const bool frag = dt != AWQ_F32;
     L->y_ref_offset = off;
-    off = align_up(off + (size_t)T * (size_t)N * 4);
+    off = align_up(off + (frag ? (size_t)awq::padded_rows(T) * (size_t)awq::padded_rows(N)
+                               : (size_t)T * (size_t)N) * 4);
   }
   const bool tiled = dt != AWQ_F32;   // the MFMA path reads tiled operands
   if (tiled) {
@@ -351,7 +354,7 @@ awq_status_t awq_search_scales(const void* W, const void* X, awq_dtype_t dtype, 
   }
   // reference output W X, once per layer (B = the caller's row-major W)
   if (!delta) {
-    e = awq::launch_gemm(awq::Epi::kStore, dtype, gemm_x, W, false, 1, T, N, K, y_ref, nullptr, 0,
+    e = awq::launch_gemm(awq::Epi::kRefOut, dtype, gemm_x, W, false, 1, T, N, K, y_ref, nullptr, 0,
                          stream);
     if (e != hipSuccess) return hip_fail(e, "reference GEMM launch");
   }
@@ -524,8 +527,8 @@ W8a8Layout w8a8_layout(int64_t N, int64_t K, int64_t T) {
   off = align_up(off + (size_t)Np * 4);
   L.xt = off;
   off = align_up(off + (size_t)Tp * K * 2);
-  L.yref = off;
-  off = align_up(off + (size_t)T * N * 4);
+  L.yref = off;                                     // fragment layout: whole tiles
+  off = align_up(off + (size_t)Tp * Np * 4);
   L.partials = off;
   off = align_up(off + (size_t)L.tiles_m * L.tiles_n * 8);
   L.scratch = off;                                  // argmin scratch: 2K floats and an index
@@ -616,7 +619,7 @@ awq_status_t awq_w8a8_loss(const void* W, const void* X, awq_dtype_t dtype, int6
   if (e != hipSuccess) return hip_fail(e, "int8 row quantiser launch");
   e = awq::launch_tile_rows(X, T, K, ws + L.xt, stream);
   if (e != hipSuccess) return hip_fail(e, "tile launch");
-  e = awq::launch_gemm(awq::Epi::kStore, dtype, ws + L.xt, W, false, 1, T, N, K, yref, nullptr, 0,
+  e = awq::launch_gemm(awq::Epi::kRefOut, dtype, ws + L.xt, W, false, 1, T, N, K, yref, nullptr, 0,
                        stream);
   if (e != hipSuccess) return hip_fail(e, "reference GEMM launch");
   e = awq::launch_gemm_w8a8(awq::Epi::kSseRef, xq, wq, T, N, K, sx, sw, yref, partials, stream);

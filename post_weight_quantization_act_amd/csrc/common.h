@@ -164,7 +164,20 @@ hipError_t launch_quant_rows_int8(const void* A, awq_dtype_t dt, int64_t R, int6
                                   int8_t* q, float* step, hipStream_t st);
 
 // gemm_sse.hip
-enum class Epi { kStore = 0, kSseRef = 1, kSseDelta = 2 };
+// GEMM epilogues.  kStore writes y row-major [T][N].  kRefOut writes the
+// reference output that a later kSseRef launch reads: on the fp16/bf16/int8
+// matrix-core path in the accumulator-fragment layout (frag_index below), on
+// the fp32 path row-major.  kSseRef sums (Y_ref - y)^2, kSseDelta sums y^2.
+enum class Epi { kStore = 0, kSseRef = 1, kSseDelta = 2, kRefOut = 3 };
+// Fragment layout of a matrix-core GEMM's fp32 output: the 256 x 256 tile
+// (tm, tn) is 64 K floats at float offset (tm * tiles_n + tn) * 65536; inside
+// it wave w (8 waves, 2 x 4 over 128 x 64 blocks), 16 x 16 block (i, j)
+// (8 x 4 per wave) and lane l hold the float4 at float4 offset
+// (w * 32 + i * 4 + j) * 64 + l, whose component r is output
+// (tm * 256 + (w / 4) * 128 + i * 16 + (l / 16) * 4 + r,
+//  tn * 256 + (w % 4) * 64 + j * 16 + l % 16).
+// A wave's 16-byte pieces of one block are 1 KB contiguous.  Outputs past T or
+// N are written (as the product of the zero padding) and never read back.
 struct GemmTiles {
   int tile_m, tile_n;
 };

@@ -305,7 +305,15 @@ void gemm_mfma_kernel(const S* __restrict__ Xt, const S* __restrict__ B, int nb,
   const int ecol = lane & 15, erow = (lane >> 4) * 4;
   auto epilogue = [&]() {
     const int m0 = cur.tm * BM, n0 = cur.tn * BN;
-    if (kEpi == Epi::kStore) {
+    // this wave's float4 pieces of the tile in the fragment layout (kRefOut, kSseRef)
+    const int64_t frag0 = (((int64_t)cur.tm * tiles_n + cur.tn) * kWaves + wave) * (MI * NI * 64) + lane;
+    if (kEpi == Epi::kRefOut) {
+      f32x4* const yfrag = reinterpret_cast<f32x4*>(Y) + frag0;
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NI; ++j) yfrag[(i * NI + j) * 64] = acc[i][j];
+    } else if (kEpi == Epi::kStore) {
 #pragma unroll
       for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -322,6 +330,13 @@ void gemm_mfma_kernel(const S* __restrict__ Xt, const S* __restrict__ B, int nb,
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
         float part = 0.0f;
+        // one 16-byte piece of the reference per block: 1 KB a wave, contiguous
+        f32x4 yr[NI];
+        if (kEpi == Epi::kSseRef) {
+          const f32x4* const yfrag = reinterpret_cast<const f32x4*>(Y) + frag0;
+#pragma unroll
+          for (int j = 0; j < NI; ++j) yr[j] = yfrag[(i * NI + j) * 64];
+        }
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
           const int n = n0 + wn * WTN + j * 16 + ecol;
@@ -330,8 +345,7 @@ void gemm_mfma_kernel(const S* __restrict__ Xt, const S* __restrict__ B, int nb,
             const int tt = m0 + wm * WTM + i * 16 + erow + rr;
             float e;
             if (kEpi == Epi::kSseRef)
-              e = (tt < T && n < N) ? Y[(int64_t)tt * N + n] - acc_value<S>(acc[i][j][rr], rs, cs, tt, n)
-                                    : 0.0f;
+              e = (tt < T && n < N) ? yr[j][rr] - acc_value<S>(acc[i][j][rr], rs, cs, tt, n) : 0.0f;
             else e = acc[i][j][rr];
             part += e * e;
           }
@@ -474,14 +488,14 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(Epi epi, const float* __r
     for (int j = 0; j < 4; ++j) {
       const int t = m0 + ty * 4 + i, n = n0 + tx * 4 + j;
       if (t >= T || n >= N) continue;
-      if (epi == Epi::kStore) {
+      if (epi == Epi::kStore || epi == Epi::kRefOut) {   // row-major on this path
         Y[(int64_t)t * N + n] = acc[i][j];
       } else {
         const float e = (epi == Epi::kSseRef) ? Y[(int64_t)t * N + n] - acc[i][j] : acc[i][j];
         sse += (double)(e * e);
       }
     }
-  if (epi == Epi::kStore) return;
+  if (epi == Epi::kStore || epi == Epi::kRefOut) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) sse += __shfl_xor(sse, off);
@@ -590,9 +604,9 @@ template <typename S>
 hipError_t dispatch_epi(Epi epi, const void* X, const void* B, bool b_tiled, int nb, int64_t T,
                         int64_t N, int64_t K, float* Y, double* partials, int a0, hipStream_t st,
                         int tile0, int ntiles) {
-  if (!b_tiled) {
-    if (epi != Epi::kStore) return hipErrorInvalidValue;
-    return launch_mfma<S, Epi::kStore, false>(X, B, nb, T, N, K, Y, partials, a0, st);
+  if (!b_tiled) {   // the reference output, from the row-major weights
+    if (epi != Epi::kRefOut) return hipErrorInvalidValue;
+    return launch_mfma<S, Epi::kRefOut, false>(X, B, nb, T, N, K, Y, partials, a0, st);
   }
   switch (epi) {
     case Epi::kSseRef:
@@ -625,7 +639,8 @@ GemmTiles gemm_tiles(awq_dtype_t dt) {
 hipError_t launch_gemm(Epi epi, awq_dtype_t dt, const void* X, const void* B, bool b_tiled,
                        int nb, int64_t T, int64_t N, int64_t K, float* Y, double* partials,
                        int a0, hipStream_t st, int tile0, int ntiles) {
-  ProfScope p(epi == Epi::kStore ? "awq_gemm_ref_output" : "awq_gemm_sse", st);
+  if (epi == Epi::kStore) return hipErrorInvalidValue;   // the reference output is kRefOut
+  ProfScope p(epi == Epi::kRefOut ? "awq_gemm_ref_output" : "awq_gemm_sse", st);
   if (dt == AWQ_F32) {
     if (tile0 != 0 || ntiles >= 0) return hipErrorInvalidValue;   // whole batch only
     const int tiles_m = (int)((T + FT - 1) / FT);

@@ -134,6 +134,9 @@ def test_search_layout_full_and_batched():
     # ragged sizes: the tiled operands are padded to 256 rows
     rag = awq.awq_search_layout(torch.bfloat16, 300, 256, 77, 3, 0, 0)
     assert rag["w_hat_offset"] - rag["x_tiled_offset"] >= 256 * 256 * 2
+    # the fp16 reference output holds whole 256 x 256 tiles (fragment layout)
+    ragr = awq.awq_search_layout(torch.float16, 300, 256, 77, 3, awq.AWQ_SEARCH_REFERENCE_OUTPUT, 0)
+    assert ragr["x_tiled_offset"] - ragr["y_ref_offset"] >= 256 * 512 * 4
     assert rag["total_bytes"] - rag["w_hat_offset"] == 3 * 512 * 256 * 2
     part = awq.awq_search_layout(torch.float16, N, K, T, n, awq.AWQ_SEARCH_REFERENCE_OUTPUT,
                                  full["w_hat_offset"] + 3 * per_alpha + 5)
@@ -144,6 +147,8 @@ def test_search_layout_full_and_batched():
     with pytest.raises(awq.AwqError):
         awq.awq_search_layout(torch.float16, N, K, T, n, awq.AWQ_SEARCH_REFERENCE_OUTPUT,
                               full["w_hat_offset"] + 10)
+    f32r = awq.awq_search_layout(torch.float32, 100, 256, 70, 2, awq.AWQ_SEARCH_REFERENCE_OUTPUT, 0)
+    assert f32r["w_hat_offset"] - f32r["y_ref_offset"] >= 70 * 100 * 4   # row-major [T][N]
     f32 = awq.awq_search_layout(torch.float32, 100, 256, 70, 2, 0, 0)
     assert (f32["tile_m"], f32["tiles_m"], f32["tiles_n"]) == (64, 2, 2)
     assert f32["x_tiled_offset"] == 2 ** 64 - 1
@@ -389,4 +394,7 @@ def test_w8a8_workspace_size():
     # int8 operands (padded rows), steps, fp16 X tiled, the fp32 reference output
     n = awq.awq_w8a8_workspace_size(4096, 4096, 4096)
     assert n >= 2 * 4096 * 4096 + 4096 * 4096 * 2 + 4096 * 4096 * 4
+    # ragged: padded int8 operands and tiled X, the reference output in whole tiles
+    r = awq.awq_w8a8_workspace_size(300, 128, 77)
+    assert r >= (256 + 512) * 128 + 256 * 128 * 2 + 256 * 512 * 4
     assert awq.awq_w8a8_workspace_size(0, 4096, 16) == 0

@@ -14,6 +14,7 @@ import torch
 import oracle
 import post_weight_quantization_act_amd as awq
 from datagen import random_layer, to_numpy
+from layouts import frag_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -340,8 +341,7 @@ def test_search_matches_oracle(dtype, bits, group, N, K, T, flags):
     parts = ws[p0:p0 + 20 * tiles * 8].view(torch.float64).view(20, tiles).cpu().numpy()
     np.testing.assert_allclose(parts.sum(1) / (T * N), losses, rtol=1e-12)
     if flags == awq.AWQ_SEARCH_REFERENCE_OUTPUT:
-        y0 = lay["y_ref_offset"]
-        Y = ws[y0:y0 + T * N * 4].view(torch.float32).view(T, N).cpu().numpy()
+        Y = reference_output_of(ws, lay, T, N, dtype)
         Yr = oracle.reference_output(Wn, Xn)
         np.testing.assert_allclose(Y, Yr, rtol=0, atol=2e-6 * np.abs(Yr).max() + 1e-30)
 
@@ -396,8 +396,7 @@ def test_search_multi_round(dtype, bits, group, N, K, T, n_alpha, flags):
             sse = float(np.sum(blk * blk))
             assert abs(parts[best, tm, tn] - sse) <= 1e-3 * sse, (tm, tn, parts[best, tm, tn], sse)
     if flags == awq.AWQ_SEARCH_REFERENCE_OUTPUT:
-        y0 = lay["y_ref_offset"]
-        Y = ws[y0:y0 + T * N * 4].view(torch.float32).view(T, N).cpu().numpy()
+        Y = reference_output_of(ws, lay, T, N, dtype)
         Yr = oracle.reference_output(Wn, Xn)
         np.testing.assert_allclose(Y, Yr, rtol=0, atol=2e-6 * np.abs(Yr).max() + 1e-30)
 
@@ -506,6 +505,19 @@ def test_search_custom_grid_and_ties():
     assert int(res["best_idx"].cpu()[0]) == (0 if losses[0] <= losses[2] else 2)
     ref = oracle.search(to_numpy(W), to_numpy(X), 4, 128, alphas)
     np.testing.assert_allclose(losses, ref["losses"], rtol=1e-3)
+
+
+def reference_output_of(ws, lay, T, N, dtype):
+    """The reference output the search left in its workspace: fp16/bf16 in the
+    fragment layout (whole 256 x 256 tiles, the padding entries zero), fp32
+    row-major."""
+    y0 = lay["y_ref_offset"]
+    if dtype == "fp32":
+        return ws[y0:y0 + T * N * 4].view(torch.float32).view(T, N).cpu().numpy()
+    Tp, Np = -(-T // 256) * 256, -(-N // 256) * 256
+    full = frag_rows(ws[y0:y0 + Tp * Np * 4].view(torch.float32).cpu().numpy(), Tp, Np)
+    assert not full[T:].any() and not full[:, N:].any()
+    return full[:T, :N]
 
 
 def tiled_rows(flat, rows, K):
