@@ -116,12 +116,10 @@ __device__ __forceinline__ uint32_t pair_f16(const uint32_t (&w)[BITS], int t, h
 // with sh + BITS <= 23, is AND-ed out in place and OR-ed under the exponent of
 // 2^(23 - sh), whose mantissa step is 2^-sh: the float reads 2^(23 - sh) + c
 // exactly, and subtracting 2^(23 - sh) + z (an integer below 2^24) leaves
-// c - z exactly.  Only AND / OR with constants and an fp32 subtraction are
-// needed: instructions that two waves of a SIMD can issue side by side,
-// unlike bit-field extracts, integer conversions and permutes (one wave64
-// instruction per 4 cycles).  The chunk's bitstream is read
-// through windows: dwords starting at a code boundary b that hold the codes
-// whose bits lie in [b, b + 23), chosen greedily from bit 0.
+// c - z exactly.  One AND-OR (and_or below) and one fp32 subtraction per
+// code, no bit-field extracts or integer conversions.  The chunk's bitstream
+// is read through windows: dwords starting at a code boundary b that hold the
+// codes whose bits lie in [b, b + 23), chosen greedily from bit 0.
 template <int BITS>
 struct MagicWindows {
   static constexpr int kSpan = 23;                          // mantissa bits of fp32
@@ -133,6 +131,34 @@ struct MagicWindows {
     return (w_end < 32 ? w_end : 32) * BITS - 1;
   }
 };
+
+// The AND-OR of the unpacking as one v_and_or_b32, mask in an SGPR and
+// exponent in a VGPR.  Written out because the compiler splits (w & mask) |
+// expo into a v_and_b32 and a v_or_b32 with literal operands, which measured
+// slower (the 70B decode call 36.5 -> 32.0 us with the single instruction).
+// The constants come from magic_ops(), built once per kernel.
+__device__ __forceinline__ uint32_t and_or(uint32_t w, uint32_t smask, uint32_t vexpo) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(w), "s"(smask), "v"(vexpo));
+  return r;
+}
+
+// Masks (SGPRs) and exponents (VGPRs) of the window offsets sh = BITS t.
+template <int BITS, int N>
+struct MagicOps {
+  uint32_t mask[N];
+  uint32_t expo[N];
+};
+template <int BITS, int N>
+__device__ __forceinline__ MagicOps<BITS, N> magic_ops() {
+  MagicOps<BITS, N> o;
+#pragma unroll
+  for (int t = 0; t < N; ++t) {
+    asm("s_mov_b32 %0, %1" : "=s"(o.mask[t]) : "i"(((1u << BITS) - 1u) << (BITS * t)));
+    asm("v_mov_b32 %0, %1" : "=v"(o.expo[t]) : "i"((uint32_t)(150 - BITS * t) << 23));
+  }
+  return o;
+}
 
 template <int BITS>
 __device__ __forceinline__ uint32_t magic_window(const uint32_t (&w)[BITS], int i) {
@@ -160,21 +186,24 @@ __device__ __forceinline__ MagicNeg<BITS> magic_neg(float z) {
 }
 
 template <int BITS>
+using GemvOps = MagicOps<BITS, MagicWindows<BITS>::kPerWin>;
+
+template <int BITS>
 __device__ __forceinline__ float magic_cz(const uint32_t (&w)[BITS], int i,
-                                          const MagicNeg<BITS>& neg) {
+                                          const MagicNeg<BITS>& neg, const GemvOps<BITS>& ops) {
   using MW = MagicWindows<BITS>;
   const int sh = MW::shift(i);
-  const uint32_t mask = ((1u << BITS) - 1u) << sh;
-  const uint32_t expo = (uint32_t)(150 - sh) << 23;          // 2^(23 - sh)
-  const float m = __uint_as_float((magic_window<BITS>(w, i) & mask) | expo);
+  // the float reads 2^(23 - sh) + c
+  const float m = __uint_as_float(and_or(magic_window<BITS>(w, i), ops.mask[sh / BITS], ops.expo[sh / BITS]));
   return m - neg.v[sh / BITS];
 }
 
 // Pair t of (c - z) as two bf16 (exact: |c - z| <= 255 has 8 significant bits).
 template <int BITS>
 __device__ __forceinline__ uint32_t pair_bf16(const uint32_t (&w)[BITS], int t,
-                                              const MagicNeg<BITS>& neg) {
-  const bf162v p = {(__bf16)magic_cz<BITS>(w, 2 * t, neg), (__bf16)magic_cz<BITS>(w, 2 * t + 1, neg)};
+                                              const MagicNeg<BITS>& neg, const GemvOps<BITS>& ops) {
+  const bf162v p = {(__bf16)magic_cz<BITS>(w, 2 * t, neg, ops),
+                    (__bf16)magic_cz<BITS>(w, 2 * t + 1, neg, ops)};
   return __builtin_bit_cast(uint32_t, p);
 }
 
@@ -251,6 +280,7 @@ __global__ __launch_bounds__(kRows) void lowbit_gemv_kernel(
   for (int m = 0; m < MB; ++m) acc[m] = accg[m] = 0.0f;
   float2 gc = {0.0f, 0.0f};                  // the current group's (delta, z)
   MagicNeg<BITS> neg;                         // and its subtrahends
+  const GemvOps<BITS> ops = magic_ops<BITS, MagicWindows<BITS>::kPerWin>();
   auto sum_chunks = [&](int c0, const uint32_t (&w)[kUnroll][BITS], const float2 (&g)[kUnroll]) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
@@ -265,7 +295,7 @@ __global__ __launch_bounds__(kRows) void lowbit_gemv_kernel(
         // fp32 activations: plain fp32 products of x and the exact (c - z)
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
-          const float cz = magic_cz<BITS>(w[u], i, neg);
+          const float cz = magic_cz<BITS>(w[u], i, neg, ops);
 #pragma unroll
           for (int m = 0; m < MB; ++m) accg[m] = fmaf(cz, (float)xs[m][kl + i], accg[m]);
         }
@@ -278,7 +308,7 @@ __global__ __launch_bounds__(kRows) void lowbit_gemv_kernel(
           for (int t = 0; t < 16; ++t) pr[t] = pair_f16<BITS>(w[u], t, negz);
         } else {
 #pragma unroll
-          for (int t = 0; t < 16; ++t) pr[t] = pair_bf16<BITS>(w[u], t, neg);
+          for (int t = 0; t < 16; ++t) pr[t] = pair_bf16<BITS>(w[u], t, neg, ops);
         }
 #pragma unroll
         for (int m = 0; m < MB; ++m) {
@@ -498,6 +528,41 @@ template <>
 __device__ __forceinline__ f32x16 mfma32<__bf16>(i32x4 a, i32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Code T of 8 consecutive ones (bits [T BITS, T BITS + BITS) of hi:lo) as
+// the fp32 value c - z without integer conversions: the code is masked in
+// place inside a window dword that starts at a code boundary and holds it
+// below bit 23 - BITS, OR-ed under the exponent of 2^(23 - sh), so the float
+// reads 2^(23 - sh) + c exactly; sub[sh / BITS] = 2^(23 - sh) + z.
+template <int BITS>
+struct QuarterWindows {
+  static constexpr int kPer = (23 - BITS) / BITS + 1;   // codes per window
+};
+template <int BITS>
+using QuarterOps = MagicOps<BITS, QuarterWindows<BITS>::kPer>;
+
+template <int BITS, int T>
+__device__ __forceinline__ float quarter_cz(uint32_t lo, uint32_t hi, const float* sub,
+                                            const QuarterOps<BITS>& ops) {
+  constexpr int kPer = QuarterWindows<BITS>::kPer;
+  constexpr int w0 = (T / kPer) * kPer * BITS;          // first bit of T's window
+  constexpr int sh = T * BITS - w0;
+  uint32_t win;
+  if constexpr (w0 == 0) win = lo;
+  else if constexpr (w0 >= 32) win = hi >> (w0 - 32);
+  else win = __builtin_amdgcn_alignbit(hi, lo, w0);
+  return __uint_as_float(and_or(win, ops.mask[sh / BITS], ops.expo[sh / BITS])) - sub[sh / BITS];
+}
+
+// Pair P of a quarter as two bf16 (c - z), exact: the upper halves of the
+// exact fp32 values.
+template <int BITS, int P>
+__device__ __forceinline__ uint32_t quarter_pair_bf16(uint32_t lo, uint32_t hi, const float* sub,
+                                                      const QuarterOps<BITS>& ops) {
+  const float f0 = quarter_cz<BITS, 2 * P>(lo, hi, sub, ops);
+  const float f1 = quarter_cz<BITS, 2 * P + 1>(lo, hi, sub, ops);
+  return __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
 }
 
 // Code t of 8 consecutive ones held in bits [t BITS, t BITS + BITS) of hi:lo.
@@ -770,36 +835,6 @@ __global__ __launch_bounds__(kGThreads, 1) void lowbit_gemm_kernel(
     }
 }
 
-// Code T of 8 consecutive ones (bits [T BITS, T BITS + BITS) of hi:lo) as
-// the fp32 value c - z without integer conversions: the code is masked in
-// place inside a window dword that starts at a code boundary and holds it
-// below bit 23 - BITS, OR-ed under the exponent of 2^(23 - sh), so the float
-// reads 2^(23 - sh) + c exactly; sub[sh / BITS] = 2^(23 - sh) + z.
-template <int BITS>
-struct QuarterWindows {
-  static constexpr int kPer = (23 - BITS) / BITS + 1;   // codes per window
-};
-template <int BITS, int T>
-__device__ __forceinline__ float quarter_cz(uint32_t lo, uint32_t hi, const float* sub) {
-  constexpr int kPer = QuarterWindows<BITS>::kPer;
-  constexpr int w0 = (T / kPer) * kPer * BITS;          // first bit of T's window
-  constexpr int sh = T * BITS - w0;
-  uint32_t win;
-  if constexpr (w0 == 0) win = lo;
-  else if constexpr (w0 >= 32) win = hi >> (w0 - 32);
-  else win = __builtin_amdgcn_alignbit(hi, lo, w0);
-  constexpr uint32_t mask = ((1u << BITS) - 1u) << sh;
-  constexpr uint32_t expo = (uint32_t)(150 - sh) << 23;
-  return __uint_as_float((win & mask) | expo) - sub[sh / BITS];
-}
-
-// Pair P of a quarter as two bf16 (c - z), exact: the upper halves of the
-// exact fp32 values.
-template <int BITS, int P>
-__device__ __forceinline__ uint32_t quarter_pair_bf16(uint32_t lo, uint32_t hi, const float* sub) {
-  const float f0 = quarter_cz<BITS, 2 * P>(lo, hi, sub), f1 = quarter_cz<BITS, 2 * P + 1>(lo, hi, sub);
-  return __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
-}
 
 // ---- prefill-sized GEMM, 256 x 256 tiles with running sums in step units ----------
 // The same Y [M, N] = Xs W'^T, now with one accumulator set per wave, which
@@ -982,6 +1017,7 @@ __global__ __launch_bounds__(kTThreads, 1) void lowbit_tile_kernel(
     c.dz = reinterpret_cast<const float2*>(lds + L::kMeta + slot * 2048)[lr];
     return c;
   };
+  const QuarterOps<BITS> qops = magic_ops<BITS, QuarterWindows<BITS>::kPer>();
   auto dq_store = [&](int s, const Codes& c) __attribute__((always_inline)) {
     // a zero step unpacks as zeros: codes and zero-point read as 0, so every
     // c - z is 0
@@ -1014,8 +1050,10 @@ __global__ __launch_bounds__(kTThreads, 1) void lowbit_tile_kernel(
         v = i32x4{(int)pair_of<S, BITS, 0>(lo, hi, negz, z), (int)pair_of<S, BITS, 1>(lo, hi, negz, z),
                   (int)pair_of<S, BITS, 2>(lo, hi, negz, z), (int)pair_of<S, BITS, 3>(lo, hi, negz, z)};
       } else {
-        v = i32x4{(int)quarter_pair_bf16<BITS, 0>(lo, hi, sub), (int)quarter_pair_bf16<BITS, 1>(lo, hi, sub),
-                  (int)quarter_pair_bf16<BITS, 2>(lo, hi, sub), (int)quarter_pair_bf16<BITS, 3>(lo, hi, sub)};
+        v = i32x4{(int)quarter_pair_bf16<BITS, 0>(lo, hi, sub, qops),
+                  (int)quarter_pair_bf16<BITS, 1>(lo, hi, sub, qops),
+                  (int)quarter_pair_bf16<BITS, 2>(lo, hi, sub, qops),
+                  (int)quarter_pair_bf16<BITS, 3>(lo, hi, sub, qops)};
       }
       *reinterpret_cast<i32x4*>(brow + g_off(lr, 2 * grp + h)) = v;
     }
@@ -1193,15 +1231,34 @@ __device__ __forceinline__ uint32_t code_in(const uint32_t (&sw)[NW]) {
   else return __builtin_amdgcn_alignbit(sw[w + 1], sw[w], o) & mask;
 }
 
+// Code T of the run as fp32 (c - z) in the magic-exponent form of the
+// quarter unpacking: windows of QuarterWindows<BITS>::kPer codes start at code
+// boundaries, sub[sh / BITS] = 2^(23 - sh) + z.
+template <int BITS, int NW, int T>
+__device__ __forceinline__ float small_cz(const uint32_t (&sw)[NW], const float* sub,
+                                          const QuarterOps<BITS>& ops) {
+  constexpr int kPer = QuarterWindows<BITS>::kPer;
+  constexpr int w0 = (T / kPer) * kPer * BITS, wi = w0 >> 5, o = w0 & 31;
+  constexpr int sh = T * BITS - w0;
+  uint32_t win;
+  if constexpr (o == 0) win = sw[wi];
+  else if constexpr (wi + 1 >= NW || o + sh + BITS <= 32) win = sw[wi] >> o;
+  else win = __builtin_amdgcn_alignbit(sw[wi + 1], sw[wi], o);
+  return __uint_as_float(and_or(win, ops.mask[sh / BITS], ops.expo[sh / BITS])) - sub[sh / BITS];
+}
+
 // Codes 2P and 2P + 1 of the run as two S values (c - z), exact.
 template <typename S, int BITS, int NW, int P>
-__device__ __forceinline__ int small_pair(const uint32_t (&sw)[NW], half2v negz, int z) {
-  const uint32_t c0 = code_in<BITS, NW, 2 * P>(sw), c1 = code_in<BITS, NW, 2 * P + 1>(sw);
+__device__ __forceinline__ int small_pair(const uint32_t (&sw)[NW], half2v negz, const float* sub,
+                                          const QuarterOps<BITS>& ops) {
   if constexpr (std::is_same<S, _Float16>::value) {
+    const uint32_t c0 = code_in<BITS, NW, 2 * P>(sw), c1 = code_in<BITS, NW, 2 * P + 1>(sw);
     const uint32_t v = c0 | (c1 << 16) | 0x64006400u;
     return (int)__builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, v) + negz);
   } else {
-    const float f0 = (float)((int)c0 - z), f1 = (float)((int)c1 - z);
+    // small integers are exact in fp32 and their upper halves are exact bf16
+    const float f0 = small_cz<BITS, NW, 2 * P>(sw, sub, ops);
+    const float f1 = small_cz<BITS, NW, 2 * P + 1>(sw, sub, ops);
     return (int)__builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
   }
 }
@@ -1265,6 +1322,7 @@ __global__ __launch_bounds__(256, 2) void lowbit_small_kernel(
     acc[i] = zero16;
     tot[i] = zero16;
   }
+  const QuarterOps<BITS> qops = magic_ops<BITS, QuarterWindows<BITS>::kPer>();
   // one stage: unpack this lane's 16 codes, read the activation fragments,
   // multiply; scale the group's sums at a group or split end
   auto stage = [&](int s, int set, const char* xb, int u) {
@@ -1280,10 +1338,13 @@ __global__ __launch_bounds__(256, 2) void lowbit_small_kernel(
     const int z = (int)mt[set].y;
     const _Float16 nzh = (_Float16)(-(1024 + z));
     const half2v negz = {nzh, nzh};
-    const i32x4 fb0 = {small_pair<S, BITS, NW, 0>(sw, negz, z), small_pair<S, BITS, NW, 1>(sw, negz, z),
-                       small_pair<S, BITS, NW, 2>(sw, negz, z), small_pair<S, BITS, NW, 3>(sw, negz, z)};
-    const i32x4 fb1 = {small_pair<S, BITS, NW, 4>(sw, negz, z), small_pair<S, BITS, NW, 5>(sw, negz, z),
-                       small_pair<S, BITS, NW, 6>(sw, negz, z), small_pair<S, BITS, NW, 7>(sw, negz, z)};
+    float sub[QuarterWindows<BITS>::kPer];
+#pragma unroll
+    for (int t = 0; t < QuarterWindows<BITS>::kPer; ++t) sub[t] = (float)(1 << (23 - BITS * t)) + (float)z;
+    const i32x4 fb0 = {small_pair<S, BITS, NW, 0>(sw, negz, sub, qops), small_pair<S, BITS, NW, 1>(sw, negz, sub, qops),
+                       small_pair<S, BITS, NW, 2>(sw, negz, sub, qops), small_pair<S, BITS, NW, 3>(sw, negz, sub, qops)};
+    const i32x4 fb1 = {small_pair<S, BITS, NW, 4>(sw, negz, sub, qops), small_pair<S, BITS, NW, 5>(sw, negz, sub, qops),
+                       small_pair<S, BITS, NW, 6>(sw, negz, sub, qops), small_pair<S, BITS, NW, 7>(sw, negz, sub, qops)};
     i32x4 fa[MB][2];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
