@@ -300,17 +300,17 @@ __global__ __launch_bounds__(kFqThreads) void fake_quant_kernel(
       const GroupQ g = group_params(mn, mx, qmax, rq);
       // c - z = clamp(rint(w' / delta), -z, qmax - z), decided from t = RN(w' y)
       // (the bound of safe_limit holds with z = 0 in the fma, so it holds here);
-      // t is clamped to [-z - 1/4, qmax - z + 1/4] and rounded to an integer by
-      // adding 1.5 * 2^23 (spacing 1 there, even, ties to even), which also
-      // gives the exact difference to t.  A risky lane sends the wave to the
-      // exact quotients.
+      // t is clamped to [-z - 1/4, qmax - z + 1/4] and rounded to the nearest
+      // integer, ties to even (v_rndne); t - rint(t) is exact (the two lie
+      // within a factor 2 of each other unless rint(t) = 0).  A risky lane
+      // sends the wave to the exact quotients.
       const float lim = safe_limit(mn, mx, g.rdelta, g.z);
       float cmz[8];
       bool risky = false;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float t = __builtin_amdgcn_fmed3f(wp[i] * g.rdelta, -g.z - 0.25f, qmax - g.z + 0.25f);
-        cmz[i] = (t + 0x1.8p23f) - 0x1.8p23f;
+        cmz[i] = __builtin_rintf(t);
         risky |= !(fabsf(t - cmz[i]) < lim);
       }
       if (__builtin_amdgcn_ballot_w64(risky) != 0) {       // wave-uniform

@@ -9,8 +9,8 @@ a group with min mn, max mx, step delta, y = RN(1/delta) and zero-point z:
 where rint(t) is read from the low mantissa bits of RN(t + 2^23) (otherwise
 the kernel computes the exact quotient).  The fake quantisation decides
 c - z = clamp(rint(RN(w'/delta)), -z, qmax - z) the same way from
-t = clamp(RN(w' * y), -z - 1/4, qmax - z + 1/4), rounded by adding 1.5 * 2^23,
-against the same lim (a t without z is within the same bound).  The claim: t lies within
+t = clamp(RN(w' * y), -z - 1/4, qmax - z + 1/4), rounded to the nearest integer
+(ties to even), against the same lim (a t without z is within the same bound).  The claim: t lies within
 2^-24 (3 |w'/delta| + z) of RN(w'/delta) + z, so a t that far from every
 half-integer rounds like the oracle's value.  This test checks it for IEEE
 fp32 in exact rational arithmetic (every operation rounded to fp32 from its
@@ -151,8 +151,7 @@ def decide_cmz(wp, delta, y, z, lim, bits):
     qmax = F32((1 << bits) - 1)
     t = rn32(fr(wp) * fr(y))
     t = min(max(t, F32(-z - F32(0.25))), F32(qmax - z + F32(0.25)))
-    r = F32(rn32(fr(t) + 3 * 2 ** 22) - F32(3 * 2.0 ** 22))
-    assert r == np.rint(t)                                           # ties to even
+    r = F32(np.rint(t))                                              # ties to even
     safe = bool(abs(F32(t - r)) < lim)
     exact = np.clip(np.rint(rn32(fr(wp) / fr(delta))), -z, qmax - z)
     return safe, r, exact
