@@ -135,7 +135,8 @@ struct MagicWindows {
 // The AND-OR of the unpacking as one v_and_or_b32, mask in an SGPR and
 // exponent in a VGPR.  Written out because the compiler splits (w & mask) |
 // expo into a v_and_b32 and a v_or_b32 with literal operands, which measured
-// slower (the 70B decode call 36.5 -> 32.0 us with the single instruction).
+// slower (the 70B decode call took 36.5 us that way, 30.3 us with the single
+// instruction).
 // The constants come from magic_ops(), built once per kernel.
 __device__ __forceinline__ uint32_t and_or(uint32_t w, uint32_t smask, uint32_t vexpo) {
   uint32_t r;
