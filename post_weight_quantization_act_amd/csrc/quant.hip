@@ -89,13 +89,6 @@ __device__ __forceinline__ GroupQ group_params(float mn, float mx, float qmax, f
   return g;
 }
 
-// c - z for c = clamp(rint(q) + z, 0, qmax), formed as clamp(rint(q), -z, qmax - z).
-// The two agree exactly: the integers involved are exact in fp32 unless
-// |rint(q)| >= 2^24, and then both clamp to the same bound.
-__device__ __forceinline__ float code_minus_z(float wp, const GroupQ& g, float qmax) {
-  return __builtin_amdgcn_fmed3f(__builtin_rintf(div_rn(wp, g.delta, g.rdelta)), -g.z, qmax - g.z);
-}
-
 // ---------------------------------------------------------------------------
 // Rounding decision of the code without the exact quotient.
 //
@@ -123,6 +116,54 @@ __device__ __forceinline__ float safe_limit(float mn, float mx, float y, float z
 }
 
 constexpr float kRecipSafeLo = 0x1p-60f, kRecipSafeHi = 0x1p60f;
+
+// ---------------------------------------------------------------------------
+// Group parameters of four rows at once, for groups of 16 lanes (one DPP row).
+//
+// Every lane of a group needs the same step, reciprocal, zero-point and safety
+// bound, so forming them in all 16 lanes repeats the same work 16 times.
+// Instead the lanes' partial min / max of four rows are reduced so that each
+// quad of the group ends with one row's group-wide values (a reduce-scatter),
+// each lane forms the parameters of that one row, and they are broadcast back
+// per row with ds_swizzle (LDS crossbar, no vector-ALU issue).
+//   step 1: row_mirror pairs lane j with 15 - j (opposite bit 3); a lane with
+//           bit 3 clear keeps rows 0, 1 and sends rows 2, 3, the other way round
+//           for its partner;
+//   step 2: row_half_mirror pairs j with the lane of opposite bit 2 in its half
+//           row; bit 2 clear keeps the lower of its two rows;
+//   steps 3, 4: the four lanes of a quad hold the same row and all-reduce.
+// Lane j then holds row (j >> 2) & 3 reduced over all 16 lanes (the four
+// lanes of quad q cover {q', 7 - q', 8 + q', 15 - q'} for its four q', whose
+// union is the whole row).  min / max are exact, so the result does not depend
+// on the order.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void minmax_scatter4(const float (&mn)[4], const float (&mx)[4],
+                                                int lane, float& omn, float& omx) {
+  const bool b3 = (lane & 8) != 0, b2 = (lane & 4) != 0;
+  float kn[2], kx[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const float keep_n = b3 ? mn[2 + i] : mn[i], send_n = b3 ? mn[i] : mn[2 + i];
+    const float keep_x = b3 ? mx[2 + i] : mx[i], send_x = b3 ? mx[i] : mx[2 + i];
+    kn[i] = fminf(keep_n, dpp<0x140>(send_n));   // row_mirror
+    kx[i] = fmaxf(keep_x, dpp<0x140>(send_x));
+  }
+  const float keep_n = b2 ? kn[1] : kn[0], send_n = b2 ? kn[0] : kn[1];
+  const float keep_x = b2 ? kx[1] : kx[0], send_x = b2 ? kx[0] : kx[1];
+  omn = fminf(keep_n, dpp<0x141>(send_n));       // row_half_mirror
+  omx = fmaxf(keep_x, dpp<0x141>(send_x));
+  omn = fminf(omn, dpp<0x4E>(omn));              // quad_perm [2,3,0,1]
+  omx = fmaxf(omx, dpp<0x4E>(omx));
+  omn = fminf(omn, dpp<0xB1>(omn));              // quad_perm [1,0,3,2]
+  omx = fmaxf(omx, dpp<0xB1>(omx));
+}
+
+// Value of lane 4 p of the lane's 16-lane group (ds_swizzle bitmask mode within
+// 32 lanes: source lane = (lane & 0x10) | 4 p).
+template <int P>
+__device__ __forceinline__ float from_quad(float v) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), ((4 * P) << 5) | 0x10));
+}
 
 template <typename S>
 __device__ __forceinline__ void load8(const S* p, float (&v)[8]);
@@ -209,7 +250,9 @@ __global__ __launch_bounds__(256) void scale_table_kernel(const float* __restric
 // values per lane) and reused for every scale vector; only the 8 scales of
 // the lane's columns are fetched per vector, with their reciprocals (read from
 // rs when the caller has them, else computed) shared by the 8 rows.  A group of G channels lives in
-// G/8 consecutive lanes and is reduced with DPP.  Output k is written to
+// G/8 consecutive lanes and is reduced with DPP; for G = 128 (16 lanes) the
+// rows are taken four at a time and each row's group parameters are formed
+// once per group (minmax_scatter4) instead of in all 16 lanes.  Output k is written to
 // out + k*out_rows*K, row-major or in the GEMM's tiled layout (16-byte chunks
 // land on their swizzled slot; padding rows up to a multiple of 256 get zeros).
 // ---------------------------------------------------------------------------
@@ -221,12 +264,15 @@ constexpr int kFqRows = kFqRowSteps * (kFqThreads / 64);
 // kLanes = G/8 lanes per group, or 0 to take it from lanes_rt.
 // kKeep: columns with keep[j] != 0 stay at full precision (output W, or 0 in
 // the delta form) and take no part in their group's min / max.
-template <typename S, typename O, bool kDelta, bool kTiled, int kLanes, bool kKeep = false>
+template <typename S, typename O, bool kDelta, bool kTiled, int kLanes, bool kKeep = false,
+          bool kRs = true>
 __global__ __launch_bounds__(kFqThreads) void fake_quant_kernel(
     const S* __restrict__ W, int64_t N, int64_t K, const float* __restrict__ s,
     const float* __restrict__ rs, int n_s, float qmax, int lanes_rt, int64_t out_rows,
     O* __restrict__ out, const uint8_t* __restrict__ keep = nullptr) {
   const int lanes = kLanes ? kLanes : lanes_rt;
+  // groups of 16 lanes (G = 128) form their parameters once per row and group
+  constexpr bool kShare = kLanes == 16 && !kKeep;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t col = (int64_t)blockIdx.x * kFqCols + lane * 8;
@@ -259,7 +305,7 @@ __global__ __launch_bounds__(kFqThreads) void fake_quant_kernel(
     float sv[8], ys[8];
     if (col_ok) {
       load8(s + (int64_t)k * K + col, sv);
-      if (rs) load8(rs + (int64_t)k * K + col, ys);
+      if (kRs) load8(rs + (int64_t)k * K + col, ys);
     } else {
 #pragma unroll
       for (int i = 0; i < 8; ++i) sv[i] = ys[i] = 1.0f;
@@ -267,62 +313,67 @@ __global__ __launch_bounds__(kFqThreads) void fake_quant_kernel(
     bool extreme = false;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      if (!rs) ys[i] = 1.0f / sv[i];
+      if (!kRs) ys[i] = 1.0f / sv[i];
+      // kept in a register: left alone the compiler may recompute the
+      // division in every row rather than hold the eight reciprocals
+      asm("" : "+v"(ys[i]));
       extreme |= !(fabsf(sv[i]) >= kRecipSafeLo && fabsf(sv[i]) <= kRecipSafeHi);
     }
     const bool exact_div = __builtin_amdgcn_ballot_w64(extreme) != 0;   // wave-uniform
     O* outk = out + (int64_t)k * out_rows * K;
+
+    // Codes, dequantisation, division by s and the store of row step p, given
+    // the row's group step, its reciprocal, the clamp bounds lo = -z - 1/4 and
+    // hi = qmax - z + 1/4 and the safety bound lim.
+    // c - z for c = clamp(rint(w' / delta) + z, 0, qmax) is formed as
+    // clamp(rint(w' / delta), -z, qmax - z): the two agree exactly, as the
+    // integers involved are exact in fp32 unless |rint| >= 2^24, and then both
+    // clamp to the same bound.  It is decided from t = RN(w' y)
+    // (the bound of safe_limit holds with z = 0 in the fma, so it holds here);
+    // t is clamped to [lo, hi] and rounded to the nearest integer, ties to
+    // even (v_rndne); t - rint(t) is exact (the two lie within a factor 2 of
+    // each other unless rint(t) = 0).  A risky lane sends the wave to the exact
+    // quotients.  z = -lo - 1/4 exactly (z <= 255).
+    auto finish_row = [&](int p, const float (&wp)[8], float delta, float rdelta, float lo,
+                          float hi, float lim) {
+      // an opaque copy, so that the compiler widens again here instead of
+      // keeping the first widening live
+      WRow<S> raw = wraw[p];
 #pragma unroll
-    for (int p = 0; p < kFqRowSteps; ++p) {
-      float w[8], wp[8];
-      float mn, mx;
-      widen_wrow(wraw[p], w);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) wp[i] = w[i] * sv[i];
-      if (kKeep) {
-        mn = kept[0] ? __builtin_inff() : wp[0];
-        mx = kept[0] ? -__builtin_inff() : wp[0];
-#pragma unroll
-        for (int i = 1; i < 8; ++i) {
-          mn = fminf(mn, kept[i] ? __builtin_inff() : wp[i]);
-          mx = fmaxf(mx, kept[i] ? -__builtin_inff() : wp[i]);
-        }
-      } else {
-        mn = wp[0];
-        mx = wp[0];
-#pragma unroll
-        for (int i = 1; i < 8; ++i) {
-          mn = fminf(mn, wp[i]);
-          mx = fmaxf(mx, wp[i]);
-        }
-      }
-      group_minmax(mn, mx, lanes);
-      const GroupQ g = group_params(mn, mx, qmax, rq);
-      // c - z = clamp(rint(w' / delta), -z, qmax - z), decided from t = RN(w' y)
-      // (the bound of safe_limit holds with z = 0 in the fma, so it holds here);
-      // t is clamped to [-z - 1/4, qmax - z + 1/4] and rounded to the nearest
-      // integer, ties to even (v_rndne); t - rint(t) is exact (the two lie
-      // within a factor 2 of each other unless rint(t) = 0).  A risky lane
-      // sends the wave to the exact quotients.
-      const float lim = safe_limit(mn, mx, g.rdelta, g.z);
+      for (int i = 0; i < (int)(sizeof(S) / 2); ++i) asm("" : "+v"(raw.v[i]));
+      float w[8];
+      widen_wrow(raw, w);
       float cmz[8];
       bool risky = false;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float t = __builtin_amdgcn_fmed3f(wp[i] * g.rdelta, -g.z - 0.25f, qmax - g.z + 0.25f);
+        const float t = __builtin_amdgcn_fmed3f(wp[i] * rdelta, lo, hi);
         cmz[i] = __builtin_rintf(t);
         risky |= !(fabsf(t - cmz[i]) < lim);
       }
       if (__builtin_amdgcn_ballot_w64(risky) != 0) {       // wave-uniform
+        const float z = -lo - 0.25f, nz = -z, qz = qmax - z;   // as group_params gave them
 #pragma unroll
-        for (int i = 0; i < 8; ++i) cmz[i] = code_minus_z(wp[i], g, qmax);
+        for (int i = 0; i < 8; ++i)
+          cmz[i] = __builtin_amdgcn_fmed3f(__builtin_rintf(div_rn(wp[i], delta, rdelta)), nz, qz);
+      }
+      // W_hat = deq / s from the reciprocal; a wave with an extreme scale
+      // redoes the row with true divisions (one wave-uniform branch per row,
+      // not one per element)
+      float deq[8], what[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        deq[i] = cmz[i] * delta;
+        what[i] = div_rn(deq[i], sv[i], ys[i]);
+      }
+      if (exact_div) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) what[i] = deq[i] / sv[i];
       }
       float o[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float deq = cmz[i] * g.delta;
-        const float what = exact_div ? deq / sv[i] : div_rn(deq, sv[i], ys[i]);
-        o[i] = kDelta ? (w[i] - what) : what;
+        o[i] = kDelta ? (w[i] - what[i]) : what[i];
         if (kKeep && kept[i]) o[i] = kDelta ? 0.0f : w[i];
       }
       const int64_t r = row0 + (int64_t)p * (kFqThreads / 64);
@@ -337,6 +388,75 @@ __global__ __launch_bounds__(kFqThreads) void fake_quant_kernel(
         }
       } else if (col_ok && row_ok[p]) {
         store8(outk + r * K + col, o);
+      }
+    };
+
+    if constexpr (kShare) {
+      // Four rows at a time: partial min / max, one reduce-scatter, the group
+      // parameters once per (row, group), broadcast back per row.
+#pragma unroll
+      for (int h = 0; h < kFqRowSteps; h += 4) {
+        // w' of the four rows is kept; w is widened again where the row is
+        // finished (one instruction per element, against 32 registers that
+        // would cost a wave per SIMD).
+        float wp[4][8], mn[4], mx[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float w[8];
+          widen_wrow(wraw[h + q], w);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) wp[q][i] = w[i] * sv[i];
+          mn[q] = wp[q][0];
+          mx[q] = wp[q][0];
+#pragma unroll
+          for (int i = 1; i < 8; ++i) {
+            mn[q] = fminf(mn[q], wp[q][i]);
+            mx[q] = fmaxf(mx[q], wp[q][i]);
+          }
+        }
+        float gmn, gmx;
+        minmax_scatter4(mn, mx, lane, gmn, gmx);
+        const GroupQ g = group_params(gmn, gmx, qmax, rq);
+        const float lim = safe_limit(gmn, gmx, g.rdelta, g.z);
+        const float lo = -g.z - 0.25f, hi = qmax - g.z + 0.25f;
+        finish_row(h + 0, wp[0], from_quad<0>(g.delta), from_quad<0>(g.rdelta),
+                   from_quad<0>(lo), from_quad<0>(hi), from_quad<0>(lim));
+        finish_row(h + 1, wp[1], from_quad<1>(g.delta), from_quad<1>(g.rdelta),
+                   from_quad<1>(lo), from_quad<1>(hi), from_quad<1>(lim));
+        finish_row(h + 2, wp[2], from_quad<2>(g.delta), from_quad<2>(g.rdelta),
+                   from_quad<2>(lo), from_quad<2>(hi), from_quad<2>(lim));
+        finish_row(h + 3, wp[3], from_quad<3>(g.delta), from_quad<3>(g.rdelta),
+                   from_quad<3>(lo), from_quad<3>(hi), from_quad<3>(lim));
+      }
+    } else {
+#pragma unroll
+      for (int p = 0; p < kFqRowSteps; ++p) {
+        float w[8], wp[8];
+        float mn, mx;
+        widen_wrow(wraw[p], w);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) wp[i] = w[i] * sv[i];
+        if (kKeep) {
+          mn = kept[0] ? __builtin_inff() : wp[0];
+          mx = kept[0] ? -__builtin_inff() : wp[0];
+#pragma unroll
+          for (int i = 1; i < 8; ++i) {
+            mn = fminf(mn, kept[i] ? __builtin_inff() : wp[i]);
+            mx = fmaxf(mx, kept[i] ? -__builtin_inff() : wp[i]);
+          }
+        } else {
+          mn = wp[0];
+          mx = wp[0];
+#pragma unroll
+          for (int i = 1; i < 8; ++i) {
+            mn = fminf(mn, wp[i]);
+            mx = fmaxf(mx, wp[i]);
+          }
+        }
+        group_minmax(mn, mx, lanes);
+        const GroupQ g = group_params(mn, mx, qmax, rq);
+        const float lim = safe_limit(mn, mx, g.rdelta, g.z);
+        finish_row(p, wp, g.delta, g.rdelta, -g.z - 0.25f, qmax - g.z + 0.25f, lim);
       }
     }
   }
@@ -525,10 +645,20 @@ hipError_t fq_dispatch(const void* W, int64_t N, int64_t K, const float* s, cons
   ProfScope p("awq_fake_quant", st);
   if (!tiled) {
     if (keep) return hipErrorInvalidValue;
-    fake_quant_kernel<S, O, kDelta, false, 0><<<grid, kFqThreads, 0, st>>>(w, N, K, s, rs, n_s,
-                                                                           qmax, lanes, out_rows, o);
+    // G = 128: group parameters shared across each group's lanes; kRs: the
+    // reciprocals of s are read from rs rather than computed
+#define AWQ_FQ_ROWS(L, R)                                                                        \
+  fake_quant_kernel<S, O, kDelta, false, L, false, R><<<grid, kFqThreads, 0, st>>>(              \
+      w, N, K, s, rs, n_s, qmax, lanes, out_rows, o)
+    if (lanes == 16) {
+      if (rs) AWQ_FQ_ROWS(16, true); else AWQ_FQ_ROWS(16, false);
+    } else {
+      if (rs) AWQ_FQ_ROWS(0, true); else AWQ_FQ_ROWS(0, false);
+    }
+#undef AWQ_FQ_ROWS
     return hipGetLastError();
   }
+  if (!rs) return hipErrorInvalidValue;   // the search's launches pass RN(1 / s)
   // the search's launch: the group width is a compile-time constant
 #define AWQ_FQ_TILED(L)                                                                          \
   if (keep)                                                                                      \
