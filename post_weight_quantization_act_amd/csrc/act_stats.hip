@@ -67,20 +67,17 @@ __global__ __launch_bounds__(kThreads) void act_stats_partial(const S* __restric
     if (col0 < K) {
       const S* p = X + r_begin * K + col0;
       int64_t r = r_begin + ty;
-      // four rows in flight per lane
-      for (; r + 3 * kRowThreads < r_end; r += 4 * kRowThreads) {
-        float v0[E], v1[E], v2[E], v3[E];
+      // eight rows in flight per lane (four measured 13% slower on 32 MB inputs,
+      // the same on large ones); the additions stay in row order
+      for (; r + 7 * kRowThreads < r_end; r += 8 * kRowThreads) {
+        float v[8][E];
         const S* q = p + (r - r_begin) * K;
-        load_vec(q, v0);
-        load_vec(q + kRowThreads * K, v1);
-        load_vec(q + 2 * kRowThreads * K, v2);
-        load_vec(q + 3 * kRowThreads * K, v3);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) load_vec(q + u * kRowThreads * K, v[u]);
 #pragma unroll
         for (int i = 0; i < E; ++i) {
-          acc[i] += (double)fabsf(v0[i]);
-          acc[i] += (double)fabsf(v1[i]);
-          acc[i] += (double)fabsf(v2[i]);
-          acc[i] += (double)fabsf(v3[i]);
+#pragma unroll
+          for (int u = 0; u < 8; ++u) acc[i] += (double)fabsf(v[u][i]);
         }
       }
       for (; r < r_end; r += kRowThreads) {

@@ -349,16 +349,35 @@ __global__ __launch_bounds__(kRows) void lowbit_gemv_kernel(
     if (m < mb) dst[(m0 + m) * N + n] = acc[m];
 }
 
-// Y[m, n] = sum over splits in index order.
+// Y[m, n] = sum over splits in index order.  kBatch splits' loads are issued
+// before any is added: all of them (32) when the grid is smaller than the chip
+// and each thread's round trips are the cost, 8 when many threads share the
+// memory system.
+template <int kBatch>
 __global__ __launch_bounds__(256) void lowbit_reduce_kernel(const float* __restrict__ partials,
                                                             int splits, int64_t MN,
                                                             float* __restrict__ Y) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= MN) return;
   float v = 0.0f;
-#pragma unroll 8
-  for (int s = 0; s < splits; ++s) v += partials[s * MN + t];
+  for (int s0 = 0; s0 < splits; s0 += kBatch) {
+    float p[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) p[i] = s0 + i < splits ? partials[(s0 + i) * MN + t] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i)
+      if (s0 + i < splits) v += p[i];
+  }
   Y[t] = v;
+}
+
+hipError_t launch_reduce(const float* partials, int splits, int64_t MN, float* Y, hipStream_t st) {
+  const unsigned blocks = (unsigned)((MN + 255) / 256);
+  if (MN <= 256 * 256)
+    lowbit_reduce_kernel<32><<<blocks, 256, 0, st>>>(partials, splits, MN, Y);
+  else
+    lowbit_reduce_kernel<8><<<blocks, 256, 0, st>>>(partials, splits, MN, Y);
+  return hipGetLastError();
 }
 
 // Activation rows per pass: as many as M needs, up to kMB.
@@ -389,11 +408,8 @@ hipError_t gemv_launch(const void* X, int64_t M, int64_t K, const uint32_t* code
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || sp.s == 1) return e;
   const int64_t MN = M * N;
-  {
-    ProfScope p("awq_lowbit_reduce", st);
-    lowbit_reduce_kernel<<<(unsigned)((MN + 255) / 256), 256, 0, st>>>(partials, sp.s, MN, Y);
-  }
-  return hipGetLastError();
+  ProfScope p("awq_lowbit_reduce", st);
+  return launch_reduce(partials, sp.s, MN, Y, st);
 }
 
 template <typename S>
@@ -1467,11 +1483,8 @@ hipError_t small_launch(const void* X, int64_t M, int64_t K, const uint32_t* cod
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || sp.s == 1) return e;
   const int64_t MN = M * N;
-  {
-    ProfScope p("awq_lowbit_reduce", st);
-    lowbit_reduce_kernel<<<(unsigned)((MN + 255) / 256), 256, 0, st>>>(partials, sp.s, MN, Y);
-  }
-  return hipGetLastError();
+  ProfScope p("awq_lowbit_reduce", st);
+  return launch_reduce(partials, sp.s, MN, Y, st);
 }
 
 template <typename S>
