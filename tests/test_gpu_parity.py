@@ -136,6 +136,30 @@ def test_fake_quant_alpha_zero_is_rtn():
     np.testing.assert_array_equal(got, exp)
 
 
+
+@pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
+@pytest.mark.parametrize("group", [64, 128])
+@pytest.mark.parametrize("delta", [False, True])
+def test_fake_quant_extreme_scales(dtype, group, delta):
+    """Scales outside [2^-60, 2^60] send their wave to true divisions for
+    W_hat = deq / s (the reciprocal-based quotient needs normal intermediates).
+    Columns 0-511 hold only ordinary scales; 512-1023 one scale of 2^70 and one
+    of 2^-70 among them; 1024-1535 the boundary 2^60 and 2^-60, which stay on
+    the reciprocal path; 1536-2047 2^61.  Both paths must equal the oracle."""
+    log_case(test="fake_quant_extreme", dtype=dtype, group=group, delta=delta)
+    N, K = 37, 2048
+    W, _ = random_layer(900 + group, N, K, 1, dtype=dtype)
+    Wn = to_numpy(W).astype(F32)
+    s = rand_scales(K, 901, outliers=((600, 2.0 ** 70), (900, 2.0 ** -70), (1030, 2.0 ** 60),
+                                      (1300, 2.0 ** -60), (1700, 2.0 ** 61)))
+    out = awq.awq_fake_quant(W.cuda(), torch.from_numpy(s[None, :]).cuda(), 4, group,
+                             awq.AWQ_FQ_WEIGHT_DELTA if delta else awq.AWQ_FQ_WEIGHT_HAT)
+    got = dev_f32(out)[0]
+    what = oracle.fake_quant(Wn, s, 4, group)
+    exp = cast_like((Wn - what).astype(F32) if delta else what, DT[dtype])
+    bad = got != exp
+    assert not bad.any(), (np.argwhere(bad)[:5], got[bad][:5], exp[bad][:5])
+
 # ---------------------------------------------------------------------------
 # step 5b: quantise + pack
 # ---------------------------------------------------------------------------
@@ -528,6 +552,44 @@ def tiled_rows(flat, rows, K):
     t, r, s = rows // 256, rows % 256, k // 32
     c = (k % 32) // 8
     return flat[((t * (K // 32) + s) * 256 + r) * 32 + 8 * (c ^ ((r >> 1) & 3)) + k % 8]
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("group", [64, 128])
+def test_search_candidates_extreme_scales(dtype, group):
+    """The search's fake-quant launch with scales beyond 2^60 and below 2^-60:
+    activation columns 640 on spread over 2^-12 .. 2^12 (those before over
+    2^-2 .. 2^2) and alpha = 6 give s = a^6 from about 2^-75 to 2^73 there,
+    so the waves of columns 0-511 keep the reciprocal path and the others
+    take true divisions.  Every D = W - W_hat equals the oracle's."""
+    log_case(test="search_candidates_extreme", dtype=dtype, group=group)
+    N, K, T = 300, 1280, 40
+    W, X = random_layer(1200 + group, N, K, T, dtype=dtype, outlier_frac=0.0)
+    rng = np.random.default_rng(1201)
+    col = (2.0 ** np.where(np.arange(K) < 640, rng.uniform(-2, 2, K),
+                           rng.uniform(-12, 12, K))).astype(F32)
+    Xn = (to_numpy(X).astype(F32) * col[None, :]).astype(F32)
+    X = torch.from_numpy(Xn).to(DT[dtype])
+    Wn = to_numpy(W).astype(F32)
+    alphas = np.array([0.0, 0.5, 6.0], dtype=F32)
+    Wd, Xd = W.cuda(), X.cuda()
+    a = awq.awq_act_stats(Xd)
+    res = awq.awq_search_scales(Wd, Xd, a, 4, group, alphas)
+    torch.cuda.synchronize()
+    lay, ws = res["layout"], res["workspace"]
+    n_a = len(alphas)
+    s0 = lay["s_table_offset"]
+    s_tab = ws[s0:s0 + n_a * K * 4].view(torch.float32).view(n_a, K).cpu().numpy()
+    assert s_tab[2].max() > 2.0 ** 60 and s_tab[2].min() < 2.0 ** -60
+    Np = (N + 255) // 256 * 256
+    d0 = lay["w_hat_offset"]
+    D = ws[d0:d0 + n_a * Np * K * 2].view(DT[dtype]).view(n_a, Np * K)
+    for k in range(n_a):
+        got = tiled_rows(D[k], np.arange(Np), K).to(torch.float32).cpu().numpy()
+        exp = cast_like(Wn - oracle.fake_quant(Wn, s_tab[k], 4, group), DT[dtype])
+        bad = got[:N] != exp
+        assert not bad.any(), (k, np.argwhere(bad)[:5])
+        assert not got[N:].any()
 
 
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
