@@ -120,14 +120,27 @@ __global__ __launch_bounds__(kThreads) void act_stats_finish(const double* __res
   __shared__ double red[kFinSplit][kFinCols];
   const int c = threadIdx.x % kFinCols, q = threadIdx.x / kFinCols;
   const int64_t j = (int64_t)blockIdx.x * kFinCols + c;
+  // Two running sums: s0 takes chunks q, q + 16, q + 32, ..., s1 chunks
+  // q + 8, q + 24, ...  A batch of the lane's chunks is loaded before any is
+  // added (the partials sit in L2 or the MALL: the round trips, not the
+  // bandwidth, are the cost), then added in that order.
+  constexpr int kFinBatch = 16;
   double s0 = 0.0, s1 = 0.0;
   if (j < K) {
-    int64_t i = q;
-    for (; i + kFinSplit < chunks; i += 2 * kFinSplit) {
-      s0 += part[i * K + j];
-      s1 += part[(i + kFinSplit) * K + j];
+    for (int64_t b = q; b < chunks; b += kFinBatch * kFinSplit) {
+      double v[kFinBatch];
+#pragma unroll
+      for (int u = 0; u < kFinBatch; ++u) {
+        const int64_t i = b + (int64_t)u * kFinSplit;
+        v[u] = i < chunks ? part[i * K + j] : 0.0;
+      }
+#pragma unroll
+      for (int u = 0; u < kFinBatch; ++u) {
+        if (b + (int64_t)u * kFinSplit >= chunks) break;
+        if (u % 2 == 0) s0 += v[u];
+        else s1 += v[u];
+      }
     }
-    if (i < chunks) s0 += part[i * K + j];
   }
   red[q][c] = s0 + s1;
   __syncthreads();
