@@ -158,6 +158,36 @@ __device__ __forceinline__ void minmax_scatter4(const float (&mn)[4], const floa
   omx = fmaxf(omx, dpp<0xB1>(omx));
 }
 
+// The same reduce-scatter for groups of 8 lanes (half a DPP row): the half-row
+// mirror pairs lane j with 7 - j (opposite bit 2), the quad permute [2,3,0,1]
+// pairs lanes of opposite bit 1, and [1,0,3,2] finishes; lane j then holds
+// row (j >> 1) & 3 reduced over its 8 lanes ({j', 7 - j', j' ^ 2, 7 - (j' ^ 2)}
+// for both lanes j' of the pair cover all 8).
+__device__ __forceinline__ void minmax_scatter4_8(const float (&mn)[4], const float (&mx)[4],
+                                                  int lane, float& omn, float& omx) {
+  const bool b2 = (lane & 4) != 0, b1 = (lane & 2) != 0;
+  float kn[2], kx[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const float keep_n = b2 ? mn[2 + i] : mn[i], send_n = b2 ? mn[i] : mn[2 + i];
+    const float keep_x = b2 ? mx[2 + i] : mx[i], send_x = b2 ? mx[i] : mx[2 + i];
+    kn[i] = fminf(keep_n, dpp<0x141>(send_n));   // row_half_mirror
+    kx[i] = fmaxf(keep_x, dpp<0x141>(send_x));
+  }
+  const float keep_n = b1 ? kn[1] : kn[0], send_n = b1 ? kn[0] : kn[1];
+  const float keep_x = b1 ? kx[1] : kx[0], send_x = b1 ? kx[0] : kx[1];
+  omn = fminf(keep_n, dpp<0x4E>(send_n));        // quad_perm [2,3,0,1]
+  omx = fmaxf(keep_x, dpp<0x4E>(send_x));
+  omn = fminf(omn, dpp<0xB1>(omn));              // quad_perm [1,0,3,2]
+  omx = fmaxf(omx, dpp<0xB1>(omx));
+}
+
+// Value of lane 2 p of the lane's 8-lane group (source lane (lane & 0x18) | 2 p).
+template <int P>
+__device__ __forceinline__ float from_pair(float v) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), ((2 * P) << 5) | 0x18));
+}
+
 // Value of lane 4 p of the lane's 16-lane group (ds_swizzle bitmask mode within
 // 32 lanes: source lane = (lane & 0x10) | 4 p).
 template <int P>
@@ -519,7 +549,9 @@ __device__ __forceinline__ uint32_t shifted_word(const uint32_t (&f)[NW], int wi
 // Sizes arrive precomputed (no integer division in the kernel): col_blocks =
 // ceil(K / 1024) waves per row block, group_shift = log2(group), lanes =
 // group / 16 (a power of two, at least 2).
-template <typename S, int BITS>
+// kShare: groups of 128 columns (8 lanes); the four rows' group parameters are
+// formed once per row and group (minmax_scatter4_8) and broadcast.
+template <typename S, int BITS, bool kShare>
 __global__ __launch_bounds__(64 * kPackWaves) void quantize_pack_kernel(
     const S* __restrict__ W, int N, int K, const float* __restrict__ s, int group_shift,
     int lanes, int col_blocks, uint32_t* __restrict__ codes, float* __restrict__ scales,
@@ -567,23 +599,11 @@ __global__ __launch_bounds__(64 * kPackWaves) void quantize_pack_kernel(
   uint32_t* dst = codes + (int64_t)row0 * words_per_row + (col >> 5) * BITS;
   const int64_t g0 = (int64_t)row0 * groups_per_row + (col >> group_shift);
   const bool group_lead = (lane & (lanes - 1)) == 0;
-#pragma unroll
-  for (int p = 0; p < kPackRows; ++p) {
-    if (row0 + p >= N) break;                              // wave-uniform
-    float w[16], wp[16];
-    unpack16(raw[p], w);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) wp[i] = w[i] * sv[i];
-    float mn = wp[0], mx = wp[0];
-#pragma unroll
-    for (int i = 1; i < 16; ++i) {
-      mn = fminf(mn, wp[i]);
-      mx = fmaxf(mx, wp[i]);
-    }
-    group_minmax(mn, mx, lanes);
-    const GroupQ g = group_params(mn, mx, qmax, rq);
-    const float lim = safe_limit(mn, mx, g.rdelta, g.z);
-
+  // Codes, packing and stores of row step p from its w' and its group's step,
+  // reciprocal, zero-point and safety bound.
+  auto finish_row = [&](int p, const float (&wp)[16], float delta, float rdelta, float zf,
+                        float lim) {
+    const GroupQ g{delta, rdelta, zf};
     // Code = clamp(rint(t), 0, qmax).  t is first clamped to [-1/4, qmax + 1/4]
     // (beyond, the clamp decides the code whatever the rounding); adding 2^23
     // then rounds it to the nearest integer, ties to even (2^23 is even, and
@@ -628,6 +648,59 @@ __global__ __launch_bounds__(64 * kPackWaves) void quantize_pack_kernel(
         scales[g0 + (int64_t)p * groups_per_row] = g.delta;
         zeros[g0 + (int64_t)p * groups_per_row] = (uint8_t)g.z;
       }
+    }
+  };
+  if constexpr (kShare) {
+    float wp[kPackRows][16], mn[kPackRows], mx[kPackRows];
+#pragma unroll
+    for (int p = 0; p < kPackRows; ++p) {
+      float w[16];
+      unpack16(raw[p], w);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) wp[p][i] = w[i] * sv[i];
+      mn[p] = wp[p][0];
+      mx[p] = wp[p][0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) {
+        mn[p] = fminf(mn[p], wp[p][i]);
+        mx[p] = fmaxf(mx[p], wp[p][i]);
+      }
+    }
+    float gmn, gmx;
+    minmax_scatter4_8(mn, mx, lane, gmn, gmx);
+    const GroupQ g = group_params(gmn, gmx, qmax, rq);
+    const float lim = safe_limit(gmn, gmx, g.rdelta, g.z);
+    static_assert(kPackRows == 4, "four rows per reduce-scatter");
+    // rows past N (wave-uniform) are skipped; their zero rows took part harmlessly
+    if (row0 + 0 < N)
+      finish_row(0, wp[0], from_pair<0>(g.delta), from_pair<0>(g.rdelta), from_pair<0>(g.z),
+                 from_pair<0>(lim));
+    if (row0 + 1 < N)
+      finish_row(1, wp[1], from_pair<1>(g.delta), from_pair<1>(g.rdelta), from_pair<1>(g.z),
+                 from_pair<1>(lim));
+    if (row0 + 2 < N)
+      finish_row(2, wp[2], from_pair<2>(g.delta), from_pair<2>(g.rdelta), from_pair<2>(g.z),
+                 from_pair<2>(lim));
+    if (row0 + 3 < N)
+      finish_row(3, wp[3], from_pair<3>(g.delta), from_pair<3>(g.rdelta), from_pair<3>(g.z),
+                 from_pair<3>(lim));
+  } else {
+#pragma unroll
+    for (int p = 0; p < kPackRows; ++p) {
+      if (row0 + p >= N) break;                              // wave-uniform
+      float w[16], wp[16];
+      unpack16(raw[p], w);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) wp[i] = w[i] * sv[i];
+      float mn = wp[0], mx = wp[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) {
+        mn = fminf(mn, wp[i]);
+        mx = fmaxf(mx, wp[i]);
+      }
+      group_minmax(mn, mx, lanes);
+      const GroupQ g = group_params(mn, mx, qmax, rq);
+      finish_row(p, wp, g.delta, g.rdelta, g.z, safe_limit(mn, mx, g.rdelta, g.z));
     }
   }
 }
@@ -690,9 +763,12 @@ hipError_t pack_dispatch(const void* W, int64_t N, int64_t K, const float* s, in
   const int lanes = group / kPackLaneCols;
   const int group_shift = __builtin_ctz((unsigned)group);
   ProfScope p("awq_quantize_pack", st);
-#define AWQ_PACK(B)                                                                               \
-  quantize_pack_kernel<S, B><<<blocks, 64 * kPackWaves, 0, st>>>(                                 \
+  // G = 128 (8 lanes a group): group parameters shared across the group's lanes
+#define AWQ_PACK_K(B, SH)                                                                         \
+  quantize_pack_kernel<S, B, SH><<<blocks, 64 * kPackWaves, 0, st>>>(                             \
       w, (int)N, (int)K, s, group_shift, lanes, col_blocks, codes, scales, zeros)
+#define AWQ_PACK(B)                                                                               \
+  if (lanes == 8) AWQ_PACK_K(B, true); else AWQ_PACK_K(B, false)
   switch (bits) {
     case 2: AWQ_PACK(2); break;
     case 3: AWQ_PACK(3); break;
@@ -703,6 +779,7 @@ hipError_t pack_dispatch(const void* W, int64_t N, int64_t K, const float* s, in
     default: AWQ_PACK(8); break;
   }
 #undef AWQ_PACK
+#undef AWQ_PACK_K
   return hipGetLastError();
 }
 
