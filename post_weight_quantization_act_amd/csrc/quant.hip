@@ -311,7 +311,8 @@ __global__ __launch_bounds__(kFqThreads) void fake_quant_kernel(
 
   // The tile stays in registers in its storage type (8 16-bit values in four
   // registers per row), widened to fp32 per scale vector: half the registers
-  // of an fp32 copy, for one shift or conversion per element.
+  // of an fp32 copy, for one shift or conversion per element (two on the
+  // shared-parameter path, which widens again where a row is finished).
   WRow<S> wraw[kFqRowSteps];
   bool row_ok[kFqRowSteps];
 #pragma unroll
