@@ -47,8 +47,8 @@ def parse():
     p.add_argument("--config", default="70b-mlp",
                    help="synthetic layer: tiny-512, llama7b-qproj, llama7b-upgate, llama7b-down, "
                         "70b-mlp (default, the largest)")
-    p.add_argument("--hbm-reps", type=int, default=3,
-                   help="cache-evicted repetitions per HBM-bound pass")
+    p.add_argument("--hbm-reps", type=int, default=10,
+                   help="cache-evicted repetitions per HBM-bound pass (the median is reported)")
     p.add_argument("--flags", type=int, default=0, help="0 weight-delta form, 1 reference-output form")
     p.add_argument("--alpha-batch", type=int, default=0,
                    help="size the search workspace for this many candidates per fake-quant + GEMM "
@@ -538,7 +538,9 @@ def hbm_passes(step, stats_call, spec, dev, reps: int) -> dict:
     awq_act_stats call between two HIP events on its stream; the fake
     quantisation and the packing (one kernel each) are timed inside a whole
     step, with HIP events on the launch stream around that kernel only.
-    Bytes are the algorithmic ones: what the pass must read and write."""
+    Each repetition is timed on its own and the median is reported, with the
+    fastest and slowest.  Bytes are the algorithmic ones: what the pass must
+    read and write."""
     import torch
 
     import post_weight_quantization_act_amd as awq
@@ -556,29 +558,33 @@ def hbm_passes(step, stats_call, spec, dev, reps: int) -> dict:
     out = {}
     for name, (prefix, nbytes) in passes.items():
         launches = 0
-        total_ms = 0.0
-        if prefix is None:
-            for _ in range(reps):
+        times = []
+        for _ in range(reps):
+            if prefix is None:
                 flush.amax()
                 e0.record()
                 stats_call()
                 e1.record()
                 torch.cuda.synchronize()
-                total_ms += e0.elapsed_time(e1)
-        else:
-            awq.awq_profile_reset()
-            awq.awq_profile_select(prefix)
-            for _ in range(reps):
+                times.append(e0.elapsed_time(e1))
+            else:
+                awq.awq_profile_reset()
+                awq.awq_profile_select(prefix)
                 flush.amax()
                 awq.awq_profile_enable(True)
                 step()
                 awq.awq_profile_enable(False)
-            torch.cuda.synchronize()
-            launches, total_ms = awq.awq_profile_read(prefix)
-            awq.awq_profile_reset()
-        ms_pass = total_ms / reps
+                torch.cuda.synchronize()
+                n, t = awq.awq_profile_read(prefix)
+                launches += n
+                times.append(t)
+                awq.awq_profile_reset()
+        times.sort()
+        ms_pass = times[len(times) // 2] if len(times) % 2 else \
+            0.5 * (times[len(times) // 2 - 1] + times[len(times) // 2])
         gbps = nbytes / (ms_pass * 1e-3) / 1e9
-        out[name] = {"ms": ms_pass, "bytes": nbytes, "gbps": gbps, "frac": gbps / PEAK_HBM_GBPS,
+        out[name] = {"ms": ms_pass, "ms_min": times[0], "ms_max": times[-1], "reps": reps,
+                     "bytes": nbytes, "gbps": gbps, "frac": gbps / PEAK_HBM_GBPS,
                      "meets_target": gbps / PEAK_HBM_GBPS >= HBM_TARGET,
                      "timed": "one entry-point call" if prefix is None else
                               f"{launches / reps:g} kernel launch(es) per step"}
